@@ -1,0 +1,203 @@
+"""Benchmark: decode-step weight-read bandwidth of the skinny W4A8/W6A8 linears.
+
+One step is one mbq_layer_sequence call: the whole decode-step walk (per layer:
+RMSNorm+quant -> q/k/v, quant -> o, quant -> gate/up, quant -> down) over a
+synthetic 9B-shaped (default) or 27B-shaped weight set, every weight matrix
+read once.  Weights, buffers and the workspace are resident in HBM before the
+timed region.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--set 9b|27b] [--bits 4|6]
+                  [--m 1] [--extra-m 3] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "weight-read GB/s (% of HBM peak) and equiv. tokens/s per decode step, M=1 and M=3"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def build_set(mbq, set_name, bits, n_layers):
+    """Pack every matrix of the weight set on the GPU; returns (ops, widths, dev_ops)."""
+    import torch
+    shapes_fn, _ = synth.WEIGHT_SETS[set_name]
+    ops, widths = synth.layer_program(shapes_fn, n_layers)
+    dev_ops = []
+    t0 = time.time()
+    for o in ops:
+        canon, S = synth.weights(bits, o["N"], o["K"], seed=1 + o["matrix"])
+        packed = mbq.pack_weights(bits, to_dev(canon), to_dev(S), o["N"], o["K"])
+        dev_ops.append(dict(bits=bits, prologue=o["prologue"], N=o["N"], K=o["K"], packed=packed,
+                            in_buf=o["in_buf"], out_buf=o["out_buf"]))
+        if o["matrix"] % 28 == 27:
+            log(f"packed {o['matrix'] + 1}/{len(ops)} matrices ({time.time() - t0:.0f} s)")
+    torch.cuda.synchronize()
+    return ops, widths, dev_ops
+
+
+def time_sequence(mbq, dev_ops, widths, M, steps, warmup, fused=True):
+    import torch
+    bufs = [torch.zeros((M, w), dtype=torch.bfloat16, device="cuda") for w in widths]
+    bufs[0].copy_(to_dev(synth.activations(M, widths[0])))
+    seq = mbq.LayerSequence(dev_ops, bufs, M, fused=fused)
+    for _ in range(warmup):
+        seq.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        seq.run()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if fused:
+        seq.check()      # raises if a bounded wait inside the walk gave up
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])  # ms
+    for b in bufs:
+        assert torch.isfinite(b.float()).all(), "non-finite output in the timed walk"
+    return dict(ms_per_step=wall * 1e3 / steps, event_ms_median=float(np.median(per)),
+                event_ms_best=float(per.min()), event_ms_mean=float(per.mean()))
+
+
+def cpu_baseline(set_name, bits, n_layers, budget_s=12.0):
+    """The oracle on the host cores, layer by layer until about budget_s of work."""
+    import oracle
+    shapes_fn, _ = synth.WEIGHT_SETS[set_name]
+    ops, widths = synth.layer_program(shapes_fn, n_layers)
+    M = 1
+    bufs = {i: np.zeros((M, w), np.uint16) for i, w in enumerate(widths)}
+    bufs[0] = synth.activations(M, widths[0])
+    per_layer = len(shapes_fn())
+    spent, done_bytes, layers = 0.0, 0, 0
+    for layer in range(n_layers):
+        lops = ops[layer * per_layer:(layer + 1) * per_layer]
+        mats = {o["matrix"]: synth.weights(bits, o["N"], o["K"], seed=1 + o["matrix"]) for o in lops}
+        t0 = time.perf_counter()
+        oracle.layer_sequence(bits, lops, bufs, lambda i: mats[i])
+        spent += time.perf_counter() - t0
+        done_bytes += synth.weight_bytes(bits, [(o["name"], o["K"], o["N"]) for o in lops])
+        layers += 1
+        if spent >= budget_s:
+            break
+    gbs = done_bytes / spent / 1e9
+    return dict(value=round(gbs, 4), unit="GB/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"first {layers} of {n_layers} layers of the same walk at M=1 "
+                       f"({done_bytes / 1e9:.3f} GB of weights, {spent:.1f} s), scaled to GB/s; "
+                       f"equivalent {gbs * 1e9 / synth.weight_bytes(bits, [(o['name'], o['K'], o['N']) for o in ops]):.4f} steps/s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--set", default="9b", choices=sorted(synth.WEIGHT_SETS))
+    ap.add_argument("--bits", type=int, default=4, choices=[4, 6])
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--m", type=int, default=1)
+    ap.add_argument("--extra-m", type=int, nargs="*", default=[3])
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--unfused", action="store_true", help="also time the one-launch-per-op walk")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the skinny linear would shard by output rows with no exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import memory_bound_quantised_amd as mbq
+    mbq.lib()   # fails loudly if the HIP library is not built
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    n_layers = args.layers or synth.WEIGHT_SETS[args.set][1]
+    shapes = synth.weight_set(args.set, n_layers)
+    wbytes = synth.weight_bytes(args.bits, shapes)
+    log(f"set {args.set} W{args.bits}A8, {n_layers} layers, {len(shapes)} matrices, "
+        f"{wbytes / 1e9:.3f} GB of weights + scales")
+    ops, widths, dev_ops = build_set(mbq, args.set, args.bits, n_layers)
+
+    results = {}
+    for M in [args.m] + [m for m in args.extra_m if m != args.m]:
+        log(f"timing M={M}: {args.warmup} warmup + {args.steps} steps")
+        results[M] = time_sequence(mbq, dev_ops, widths, M, args.steps, args.warmup)
+        log(f"M={M}: {results[M]}")
+
+    unfused = None
+    if args.unfused:
+        log(f"timing the unfused walk at M={args.m}")
+        unfused = time_sequence(mbq, dev_ops, widths, args.m, max(3, args.steps // 4), 1, fused=False)
+    main_r = results[args.m]
+    t_s = main_r["event_ms_median"] / 1e3
+    gbs = wbytes / t_s / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{args.set}-shaped decode step, {n_layers} layers x 7 W{args.bits}A8 "
+                               f"linears, M={args.m}",
+                   "weight_bytes": wbytes, "layers": n_layers, "bits": args.bits, "M": args.m},
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(1.0 / t_s, 2),
+        "event_ms": {k: round(v, 4) for k, v in main_r.items()},
+    }
+    for M, r in results.items():
+        if M == args.m:
+            continue
+        tm = r["event_ms_median"] / 1e3
+        out[f"m{M}"] = {"GB/s": round(wbytes / tm / 1e9, 2), "ms_per_step": round(r["ms_per_step"], 4),
+                        "event_ms_median": round(r["event_ms_median"], 4),
+                        "steps_per_s": round(1 / tm, 2), "rows_per_s_upper_bound": round(M / tm, 2),
+                        "marginal_cost_vs_m%d" % args.m: round(tm / t_s - 1, 4)}
+    if unfused is not None:
+        out["unfused_walk"] = {"event_ms_median": round(unfused["event_ms_median"], 4),
+                               "GB/s": round(wbytes / (unfused["event_ms_median"] / 1e3) / 1e9, 2)}
+    # One step is one launch of the persistent walk kernel, timed with HIP events
+    # recorded on the stream it is launched on.
+    out["roofline"] = {"bound": "hbm", "kernel": "seq_kernel (fused decode-step walk, 1 launch per step)",
+                       "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                       "bytes_per_launch": wbytes, "launch_ms": round(main_r["event_ms_median"], 4)}
+    if not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(args.set, args.bits, n_layers)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,217 @@
+/*
+ * mbq.h -- C ABI of libmbq: memory-bound quantised skinny linears for MI355X (gfx950).
+ *
+ * The hot path of batch-of-one LLM token generation as described on the page
+ * "Doubling LLM token rates in ComfyUI" (blog.comfy.org):
+ *   - section "What is the bottleneck?": a dense, often square weight matrix
+ *     times one activation row (M = 1) or a thin block (M = 2..4) for a
+ *     multi-token-prediction verify step; every weight is read once per step
+ *     for about one operation, so HBM read speed bounds the step;
+ *   - section "Optimizing the Linear Kernel": W4A8 / W6A8 weights (4- or 6-bit
+ *     integer codes with per-group scales), the activation quantised to 8 bits,
+ *     an integer matrix-vector kernel, weights and their group scales
+ *     re-laid out once per model load in the order the kernel consumes them,
+ *     and the activation quantisation fused with the RMSNorm before it.
+ *
+ * Definitions used by every entry point (the pages state the operations but
+ * not their formulas; these are the readings the library implements):
+ *   canonical W4   u8[N][K/2]: two's-complement int4 codes in [-8, 7], even k in
+ *                  the low nibble of byte k/2.
+ *   canonical W6   u8[N][3K/4]: int6 codes in [-32, 31]; codes 4j..4j+3 form the
+ *                  little-endian 24-bit word of bytes 3j..3j+2, code 4j+i at bits 6i.
+ *   scales         IEEE fp16 S[N][K/128]: one scale per 128 consecutive k of a row.
+ *   quantisation   per row m: amax = max_k |x[m][k]|, s[m] = amax / 127 (fp32, IEEE
+ *                  divide); q[m][k] = clamp(round_half_even(x[m][k] / s[m]), -127, 127);
+ *                  an all-zero row gives s = 0 and q = 0.
+ *   linear         acc[m][n][g] = sum_{k in group g} q[m][k] * w[n][k]  (exact int32);
+ *                  y[m][n] = bf16_round_nearest_even(s[m] * sum_g S[n][g] * acc[m][n][g])
+ *                  with the group sum taken in fp32 (so y matches the exact value
+ *                  to within fp32 summation error before the bf16 rounding).
+ *   RMSNorm        (weightless, optional before a quantisation): ss = sum_k x^2 in
+ *                  fp64, r = 1 / sqrtf((float)(ss / K) + 1e-6f) in fp32,
+ *                  t = bf16_round(x * r); then the quantisation runs on t.
+ *
+ * Conventions for every call:
+ *   - Pointers marked "device" are caller-owned device memory of the current
+ *     HIP device; "host" pointers are ordinary host memory read during the
+ *     call only.  The library never allocates or frees memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls validate
+ *     their arguments, enqueue work on `stream` and return without waiting;
+ *     device faults surface at the caller's next synchronisation.
+ *   - Return value: MBQ_OK (0) or a negative mbq_status.  On any non-zero
+ *     status nothing has been enqueued, except MBQ_ERR_HIP, which reports a
+ *     launch failure (the HIP error code is then in mbq_last_hip_error()).
+ *   - Shapes: M in [1, 4]; K a positive multiple of 128 (at most 2^24);
+ *     1 <= N <= 2^20; bits 4 or 6.
+ *   - Alignment: packed weights 256-byte aligned; activation, q and y
+ *     pointers 16-byte aligned; workspaces 256-byte aligned.
+ *   - Workspaces: caller-owned device memory of at least the queried size,
+ *     zero-filled before its first use (e.g. allocated with zeros).  A call
+ *     that runs to completion leaves the workspace's counters zero again, so
+ *     the same workspace serves any later call.  Calls that share a workspace
+ *     must not overlap in time (same stream, or synchronised).
+ */
+#ifndef MBQ_H
+#define MBQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MBQ_OK = 0,
+    MBQ_ERR_NULL = -1,      /* a required pointer is NULL */
+    MBQ_ERR_SHAPE = -2,     /* M, N or K outside the supported set */
+    MBQ_ERR_BITS = -3,      /* bits is not 4 or 6 */
+    MBQ_ERR_ALIGN = -4,     /* a pointer violates the alignment rules */
+    MBQ_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required */
+    MBQ_ERR_PROGRAM = -6,   /* malformed layer-sequence op list */
+    MBQ_ERR_HIP = -7,       /* a HIP runtime call failed */
+    MBQ_ERR_DEVICE = -8,    /* the current device is not a gfx950 */
+    MBQ_ERR_TIMEOUT = -9    /* a bounded wait inside the fused walk gave up */
+} mbq_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *mbq_status_string(int status);
+
+/* hipError_t behind the last MBQ_ERR_HIP returned on this thread (0 if none). */
+int mbq_last_hip_error(void);
+
+/* Library version string (static). */
+const char *mbq_version(void);
+
+/* ---------------------------------------------------------------- weight layout
+ * Kernel-order layout ("Optimizing the Linear Kernel": weights and their
+ * per-group scales interleaved in the order the kernel consumes them, laid out
+ * once per model load).  Rows are cut into blocks of 64; each (row block,
+ * 128-wide k group) tile holds the 64 rows' codes followed by their 64 fp16
+ * scales, and tiles follow each other row block by row block, k group by k
+ * group.  Rows past N are zero-filled.  The layout is opaque to callers: its
+ * size comes from mbq_packed_bytes and it is produced by mbq_pack_weights.
+ */
+
+/* Bytes of the packed layout for an N x K matrix of `bits`-bit codes, or a
+ * negative mbq_status for invalid arguments. */
+int64_t mbq_packed_bytes(int bits, int64_t N, int64_t K);
+
+/* Re-lay a canonical matrix (w_canon: device u8, scales_f16: device fp16
+ * [N][K/128]) into `packed` (device, mbq_packed_bytes bytes).  Lossless. */
+int mbq_pack_weights(int bits, int64_t N, int64_t K, const void *w_canon,
+                     const void *scales_f16, void *packed, void *stream);
+
+/* Inverse of mbq_pack_weights (device pointers); for tests and tooling. */
+int mbq_unpack_weights(int bits, int64_t N, int64_t K, const void *packed,
+                       void *w_canon, void *scales_f16, void *stream);
+
+/* ---------------------------------------------------------------- activation quantisation
+ * "Optimizing the Linear Kernel": quantise the activation to 8 bits before
+ * the integer linear.  x_bf16: device bf16 [M][K] (row stride K);
+ * q: device int8 [M][K]; s: device fp32 [M]. */
+int mbq_quantize_act(int64_t M, int64_t K, const void *x_bf16, int8_t *q, float *s,
+                     void *stream);
+
+/* Same, preceded by the weightless RMSNorm of each row (the prologue fusion
+ * of "Optimizing the Linear Kernel").  Arguments as mbq_quantize_act. */
+int mbq_rmsnorm_quantize_act(int64_t M, int64_t K, const void *x_bf16, int8_t *q, float *s,
+                             void *stream);
+
+/* ---------------------------------------------------------------- the skinny linear
+ * "What is the bottleneck?" / "Optimizing the Linear Kernel": y = rescale(q x W^T).
+ * q: device int8 [M][K]; s: device fp32 [M]; packed: device, from
+ * mbq_pack_weights with the matching bits; y_bf16: device bf16 [M][N];
+ * ws: device workspace of mbq_linear_workspace_bytes bytes (see conventions). */
+int64_t mbq_linear_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K);
+
+int mbq_w4a8_linear(int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,
+                    const void *packed, void *y_bf16, void *ws, int64_t ws_bytes,
+                    void *stream);
+
+int mbq_w6a8_linear(int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,
+                    const void *packed, void *y_bf16, void *ws, int64_t ws_bytes,
+                    void *stream);
+
+/* The exact int32 group sums acc[m][n][g] (device int32 [M][N][K/128]) that the
+ * linear rescales, computed by the same unpack and dot-product code.  For tests. */
+int mbq_linear_group_acc(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q,
+                         const void *packed, int32_t *acc, void *stream);
+
+/* ---------------------------------------------------------------- decode-step walk
+ * "What is the bottleneck?": one decode step reads every weight matrix of the
+ * model once.  An op list describes the walk: op i quantises columns [0, K) of
+ * buffer in_buf (optionally after the weightless RMSNorm), multiplies by its
+ * packed matrix and writes all N columns of buffer out_buf.  Consecutive ops
+ * with the same in_buf, prologue and K share one quantisation (a phase, e.g.
+ * q/k/v or gate/up).  Semantics are those of running the ops one after the
+ * other.  Buffers are device bf16 [M][width] with row stride width. */
+enum { MBQ_PRO_QUANT = 0, MBQ_PRO_RMSNORM_QUANT = 1 };
+
+typedef struct mbq_op {
+    int32_t bits;        /* 4 or 6 */
+    int32_t prologue;    /* MBQ_PRO_QUANT or MBQ_PRO_RMSNORM_QUANT */
+    int64_t N;           /* output columns; must equal the width of out_buf */
+    int64_t K;           /* input columns read; multiple of 128, <= width of in_buf */
+    const void *packed;  /* device, from mbq_pack_weights(bits, N, K) */
+    int32_t in_buf;      /* index into bufs */
+    int32_t out_buf;     /* index into bufs; differs from in_buf and from the
+                            out_buf of every other op of the same phase */
+} mbq_op;
+
+/* Workspace bytes for the walk (fused and unfused forms), or a negative
+ * mbq_status (MBQ_ERR_PROGRAM for a malformed op list).  ops, buf_widths: host. */
+int64_t mbq_sequence_workspace_bytes(const mbq_op *ops, int32_t n_ops,
+                                     const int64_t *buf_widths, int32_t n_bufs, int64_t M);
+
+/* Launch parameters of a prepared walk (filled by mbq_sequence_prepare; host memory). */
+typedef struct mbq_sequence_info {
+    uint64_t magic;
+    int32_t bits, M;
+    int32_t grid, lds_bytes;
+    int64_t ws_bytes;
+    int64_t plan_offset;
+} mbq_sequence_info;
+
+/* Validate the walk and write its execution plan into ws (device), then wait
+ * for `stream` to drain (a set-up call, not for the per-step loop).  ops,
+ * bufs (device pointers) and buf_widths (elements per row, multiples of 8)
+ * are host arrays.  All ops must share one bit width.  Returns
+ * MBQ_ERR_PROGRAM if an op reads a buffer index out of range, N != width of
+ * out_buf, K > width of in_buf, a phase writes its own input or the same
+ * buffer twice, the bit widths differ, or one op's output is read with two
+ * different K.  The plan stays valid while ws, bufs and the packed weights
+ * stay where they are. */
+int mbq_sequence_prepare(const mbq_op *ops, int32_t n_ops, void *const *bufs,
+                         const int64_t *buf_widths, int32_t n_bufs, int64_t M, void *ws,
+                         int64_t ws_bytes, void *stream, mbq_sequence_info *info);
+
+/* One decode step: a single persistent-kernel launch that runs every op of
+ * the prepared walk with all its quantisations fused in, keeping the weight
+ * stream going across op boundaries.  Enqueued on `stream`; does not wait.
+ * Needs every workgroup of its grid resident at once (cooperative launch);
+ * nothing else may run on the device in parallel with it. */
+int mbq_sequence_run(const mbq_sequence_info *info, void *ws, void *stream);
+
+/* Wait for `stream`, then report whether the last walks run on ws completed
+ * normally: MBQ_OK, MBQ_ERR_TIMEOUT (a bounded wait gave up: outputs are not
+ * valid) or MBQ_ERR_PROGRAM (ws held no prepared plan).  Clears the report. */
+int mbq_sequence_check(void *ws, void *stream);
+
+/* mbq_sequence_prepare + mbq_sequence_run. */
+int mbq_layer_sequence(const mbq_op *ops, int32_t n_ops, void *const *bufs,
+                       const int64_t *buf_widths, int32_t n_bufs, int64_t M, void *ws,
+                       int64_t ws_bytes, void *stream);
+
+/* The same walk as one quantisation launch plus one linear launch per op
+ * (mixed bit widths allowed).  Same results within the linear's tolerance;
+ * kept as the unfused baseline.  Does not wait. */
+int mbq_layer_sequence_unfused(const mbq_op *ops, int32_t n_ops, void *const *bufs,
+                               const int64_t *buf_widths, int32_t n_bufs, int64_t M, void *ws,
+                               int64_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MBQ_H */

@@ -1,0 +1,246 @@
+"""Thin Python binding of libmbq (include/mbq.h) for PyTorch tensors.
+
+Every function marshals tensor pointers, sizes and the current HIP stream into
+the C ABI of the same name; all arithmetic runs in the library's HIP kernels.
+If libmbq.so has not been built, importing works but every call raises
+RuntimeError: there is no fallback implementation.
+
+Build the library with ``python -m memory_bound_quantised_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmbq.so")
+
+PRO_QUANT = 0
+PRO_RMSNORM_QUANT = 1
+STATUS = {0: "MBQ_OK", -1: "MBQ_ERR_NULL", -2: "MBQ_ERR_SHAPE", -3: "MBQ_ERR_BITS",
+          -4: "MBQ_ERR_ALIGN", -5: "MBQ_ERR_WORKSPACE", -6: "MBQ_ERR_PROGRAM",
+          -7: "MBQ_ERR_HIP", -8: "MBQ_ERR_DEVICE", -9: "MBQ_ERR_TIMEOUT"}
+
+EXPORTS = ["mbq_status_string", "mbq_last_hip_error", "mbq_version", "mbq_packed_bytes",
+           "mbq_pack_weights", "mbq_unpack_weights", "mbq_quantize_act",
+           "mbq_rmsnorm_quantize_act", "mbq_linear_workspace_bytes", "mbq_w4a8_linear",
+           "mbq_w6a8_linear", "mbq_linear_group_acc", "mbq_sequence_workspace_bytes",
+           "mbq_sequence_prepare", "mbq_sequence_run", "mbq_sequence_check", "mbq_layer_sequence",
+           "mbq_layer_sequence_unfused"]
+
+
+class MbqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = f"{fn} failed: {STATUS.get(status, status)}"
+        if status == -7 and _lib_handle is not None:
+            msg += f" (hipError {_lib_handle.mbq_last_hip_error()})"
+        super().__init__(msg)
+
+
+class MbqOp(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("prologue", ctypes.c_int32), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("packed", ctypes.c_void_p), ("in_buf", ctypes.c_int32),
+                ("out_buf", ctypes.c_int32)]
+
+
+class MbqSequenceInfo(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint64), ("bits", ctypes.c_int32), ("M", ctypes.c_int32),
+                ("grid", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("ws_bytes", ctypes.c_int64),
+                ("plan_offset", ctypes.c_int64)]
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmbq; raises RuntimeError if it has not been built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m memory_bound_quantised_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.mbq_status_string.argtypes = [ctypes.c_int]
+        L.mbq_status_string.restype = ctypes.c_char_p
+        L.mbq_last_hip_error.restype = ctypes.c_int
+        L.mbq_version.restype = ctypes.c_char_p
+        L.mbq_packed_bytes.argtypes = [ctypes.c_int, I64, I64]
+        L.mbq_packed_bytes.restype = I64
+        L.mbq_pack_weights.argtypes = [ctypes.c_int, I64, I64, P, P, P, P]
+        L.mbq_unpack_weights.argtypes = [ctypes.c_int, I64, I64, P, P, P, P]
+        L.mbq_quantize_act.argtypes = [I64, I64, P, P, P, P]
+        L.mbq_rmsnorm_quantize_act.argtypes = [I64, I64, P, P, P, P]
+        L.mbq_linear_workspace_bytes.argtypes = [ctypes.c_int, I64, I64, I64]
+        L.mbq_linear_workspace_bytes.restype = I64
+        for fn in (L.mbq_w4a8_linear, L.mbq_w6a8_linear):
+            fn.argtypes = [I64, I64, I64, P, P, P, P, P, I64, P]
+        L.mbq_linear_group_acc.argtypes = [ctypes.c_int, I64, I64, I64, P, P, P, P]
+        L.mbq_sequence_workspace_bytes.argtypes = [P, I32, P, I32, I64]
+        L.mbq_sequence_workspace_bytes.restype = I64
+        L.mbq_layer_sequence.argtypes = [P, I32, P, P, I32, I64, P, I64, P]
+        L.mbq_layer_sequence_unfused.argtypes = [P, I32, P, P, I32, I64, P, I64, P]
+        L.mbq_sequence_prepare.argtypes = [P, I32, P, P, I32, I64, P, I64, P, P]
+        L.mbq_sequence_run.argtypes = [P, P, P]
+        L.mbq_sequence_check.argtypes = [P, P]
+        for name in EXPORTS:
+            if name not in ("mbq_status_string", "mbq_last_hip_error", "mbq_version",
+                            "mbq_packed_bytes", "mbq_linear_workspace_bytes",
+                            "mbq_sequence_workspace_bytes"):
+                getattr(L, name).restype = ctypes.c_int
+        _lib_handle = L
+    return _lib_handle
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise MbqError(fn, rc)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+# ---------------------------------------------------------------- sizes
+
+def packed_bytes(bits: int, N: int, K: int) -> int:
+    v = lib().mbq_packed_bytes(bits, N, K)
+    if v < 0:
+        raise MbqError("mbq_packed_bytes", v)
+    return v
+
+
+def linear_workspace_bytes(bits: int, M: int, N: int, K: int) -> int:
+    v = lib().mbq_linear_workspace_bytes(bits, M, N, K)
+    if v < 0:
+        raise MbqError("mbq_linear_workspace_bytes", v)
+    return v
+
+
+# ---------------------------------------------------------------- calls on torch tensors
+
+def _empty(nbytes: int, device):
+    import torch
+    # 256-byte aligned by the caching allocator; at least one element
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def _zeros(nbytes: int, device):
+    import torch
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def pack_weights(bits: int, w_canon, scales_f16, N: int, K: int, out=None):
+    """Canonical codes (uint8 [N][K*bits/8]) + fp16 scales [N][K/128] -> packed uint8 tensor."""
+    if out is None:
+        out = _empty(packed_bytes(bits, N, K), w_canon.device)
+    _check("mbq_pack_weights", lib().mbq_pack_weights(bits, N, K, _ptr(w_canon), _ptr(scales_f16),
+                                                      _ptr(out), _stream()))
+    return out
+
+
+def unpack_weights(bits: int, packed, N: int, K: int):
+    import torch
+    canon = torch.empty((N, K * bits // 8), dtype=torch.uint8, device=packed.device)
+    scales = torch.empty((N, K // 128), dtype=torch.float16, device=packed.device)
+    _check("mbq_unpack_weights", lib().mbq_unpack_weights(bits, N, K, _ptr(packed), _ptr(canon),
+                                                          _ptr(scales), _stream()))
+    return canon, scales
+
+
+def quantize_act(x_bf16, rmsnorm: bool = False):
+    """bf16 [M][K] -> (q int8 [M][K], s fp32 [M])."""
+    import torch
+    M, K = x_bf16.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=x_bf16.device)
+    s = torch.empty((M,), dtype=torch.float32, device=x_bf16.device)
+    fn = lib().mbq_rmsnorm_quantize_act if rmsnorm else lib().mbq_quantize_act
+    _check("mbq_quantize_act", fn(M, K, _ptr(x_bf16), _ptr(q), _ptr(s), _stream()))
+    return q, s
+
+
+def linear(bits: int, q, s, packed, N: int, ws=None, out=None):
+    """y bf16 [M][N] = rescale(q x W^T); ws is a zero-initialised uint8 workspace (made if None)."""
+    import torch
+    M, K = q.shape
+    need = linear_workspace_bytes(bits, M, N, K)
+    if ws is None:
+        ws = _zeros(need, q.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=q.device)
+    fn = lib().mbq_w4a8_linear if bits == 4 else lib().mbq_w6a8_linear
+    _check("mbq_w%da8_linear" % bits, fn(M, N, K, _ptr(q), _ptr(s), _ptr(packed), _ptr(out),
+                                         _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def w4a8_linear(q, s, packed, N, ws=None, out=None):
+    return linear(4, q, s, packed, N, ws, out)
+
+
+def w6a8_linear(q, s, packed, N, ws=None, out=None):
+    return linear(6, q, s, packed, N, ws, out)
+
+
+def linear_group_acc(bits: int, q, packed, N: int):
+    import torch
+    M, K = q.shape
+    acc = torch.empty((M, N, K // 128), dtype=torch.int32, device=q.device)
+    _check("mbq_linear_group_acc", lib().mbq_linear_group_acc(bits, M, N, K, _ptr(q), _ptr(packed),
+                                                              _ptr(acc), _stream()))
+    return acc
+
+
+class LayerSequence:
+    """A decode-step walk: an op list over bf16 buffers.
+
+    ops: iterable of dicts with bits, prologue, N, K, packed (uint8 tensor),
+    in_buf, out_buf.  bufs: list of bf16 tensors [M][width].  The workspace is
+    allocated (zero-filled) once here.  fused=True prepares the persistent
+    kernel's plan once (mbq_sequence_prepare) and run() is one launch
+    (mbq_sequence_run); fused=False runs mbq_layer_sequence_unfused.
+    """
+
+    def __init__(self, ops, bufs, M: int, fused: bool = True):
+        self.M = M
+        self.fused = fused
+        self.bufs = list(bufs)
+        self._keep = [o["packed"] for o in ops]
+        arr = (MbqOp * len(ops))()
+        for i, o in enumerate(ops):
+            arr[i] = MbqOp(o["bits"], o["prologue"], o["N"], o["K"], o["packed"].data_ptr(),
+                           o["in_buf"], o["out_buf"])
+        self._ops = arr
+        self._n_ops = len(ops)
+        self._widths = (ctypes.c_int64 * len(bufs))(*[b.shape[1] for b in bufs])
+        self._ptrs = (ctypes.c_void_p * len(bufs))(*[b.data_ptr() for b in bufs])
+        need = lib().mbq_sequence_workspace_bytes(arr, self._n_ops, self._widths, len(bufs), M)
+        if need < 0:
+            raise MbqError("mbq_sequence_workspace_bytes", need)
+        self.ws = _zeros(need, bufs[0].device)
+        self.info = MbqSequenceInfo()
+        if fused:
+            _check("mbq_sequence_prepare",
+                   lib().mbq_sequence_prepare(self._ops, self._n_ops, self._ptrs, self._widths,
+                                              len(self.bufs), M, _ptr(self.ws), self.ws.numel(),
+                                              _stream(), ctypes.byref(self.info)))
+
+    def run(self):
+        if self.fused:
+            _check("mbq_sequence_run", lib().mbq_sequence_run(ctypes.byref(self.info), _ptr(self.ws),
+                                                              _stream()))
+        else:
+            _check("mbq_layer_sequence_unfused",
+                   lib().mbq_layer_sequence_unfused(self._ops, self._n_ops, self._ptrs, self._widths,
+                                                    len(self.bufs), self.M, _ptr(self.ws),
+                                                    self.ws.numel(), _stream()))
+
+    def check(self):
+        """Synchronise and raise if a bounded wait inside the fused walk gave up."""
+        _check("mbq_sequence_check", lib().mbq_sequence_check(_ptr(self.ws), _stream()))

@@ -1,0 +1,347 @@
+// C ABI of libmbq (declared in include/mbq.h): argument validation, workspace
+// sizing and dispatch.  Every check runs before the first HIP call, so a call
+// that returns an error has enqueued nothing.
+#include <string.h>
+
+#include <atomic>
+#include <vector>
+
+#include "../../include/mbq.h"
+#include "mbq_internal.h"
+#include "mbq_kernels.h"
+
+using namespace mbq;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return MBQ_ERR_HIP;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool bits_ok(int bits) { return bits == 4 || bits == 6; }
+bool k_ok(int64_t K) { return K >= kGroup && K % kGroup == 0 && K <= (int64_t)1 << 24; }
+bool n_ok(int64_t N) { return N >= 1 && N <= kMaxN; }
+bool m_ok(int64_t M) { return M >= 1 && M <= 4; }
+
+// 0 = unknown, 1 = gfx950, -1 = other; cached per device ordinal.
+std::atomic<int> g_dev_ok[64];
+
+int check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= 64) return MBQ_ERR_DEVICE;
+    int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e);
+        st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        g_dev_ok[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? MBQ_OK : MBQ_ERR_DEVICE;
+}
+
+int linear_common(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,
+                  const void *packed, void *y, void *ws, int64_t ws_bytes, void *stream) {
+    if (!q || !s || !packed || !y) return MBQ_ERR_NULL;
+    if (!m_ok(M) || !n_ok(N) || !k_ok(K)) return MBQ_ERR_SHAPE;
+    if (!aligned(packed, 256) || !aligned(q, 16) || !aligned(s, 4) || !aligned(y, 16))
+        return MBQ_ERR_ALIGN;
+    const LinearPlan plan = plan_linear(bits, M, N, K);
+    if (!ws || ws_bytes < plan.ws_bytes) return MBQ_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return MBQ_ERR_ALIGN;
+    int st = check_device();
+    if (st) return st;
+    hipError_t e = launch_linear(bits, M, N, K, q, s, packed, y, N, ws, plan, (hipStream_t)stream);
+    return e == hipSuccess ? MBQ_OK : hip_fail(e);
+}
+
+// ------------------------------------------------------------------ layer sequence
+
+struct Phase {
+    int32_t first, count;   // ops [first, first + count)
+};
+
+int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
+
+// Validates the op list and splits it into phases; returns the workspace size
+// or a negative status.
+int64_t analyse_program(const mbq_op *ops, int32_t n_ops, const int64_t *widths, int32_t n_bufs,
+                        int64_t M, std::vector<Phase> *phases) {
+    if (!ops || !widths) return MBQ_ERR_NULL;
+    if (n_ops < 1 || n_bufs < 1) return MBQ_ERR_PROGRAM;
+    if (!m_ok(M)) return MBQ_ERR_SHAPE;
+    for (int32_t b = 0; b < n_bufs; ++b)
+        if (widths[b] < 8 || widths[b] % 8 || widths[b] > kMaxN) return MBQ_ERR_PROGRAM;
+    int64_t k_max = 0, lin_ws = 0;
+    std::vector<Phase> ph;
+    for (int32_t i = 0; i < n_ops; ++i) {
+        const mbq_op &o = ops[i];
+        if (!bits_ok(o.bits)) return MBQ_ERR_BITS;
+        if (!o.packed) return MBQ_ERR_NULL;
+        if (!aligned(o.packed, 256)) return MBQ_ERR_ALIGN;
+        if (o.prologue != MBQ_PRO_QUANT && o.prologue != MBQ_PRO_RMSNORM_QUANT) return MBQ_ERR_PROGRAM;
+        if (!k_ok(o.K) || !n_ok(o.N)) return MBQ_ERR_SHAPE;
+        if (o.in_buf < 0 || o.in_buf >= n_bufs || o.out_buf < 0 || o.out_buf >= n_bufs)
+            return MBQ_ERR_PROGRAM;
+        if (o.out_buf == o.in_buf) return MBQ_ERR_PROGRAM;
+        if (o.K > widths[o.in_buf] || o.N != widths[o.out_buf]) return MBQ_ERR_PROGRAM;
+        const bool joins = !ph.empty() && ops[ph.back().first].in_buf == o.in_buf &&
+                           ops[ph.back().first].prologue == o.prologue && ops[ph.back().first].K == o.K;
+        if (joins) {
+            for (int32_t j = ph.back().first; j < i; ++j)
+                if (ops[j].out_buf == o.out_buf) return MBQ_ERR_PROGRAM;
+            ph.back().count++;
+        } else {
+            ph.push_back(Phase{i, 1});
+        }
+        if (o.K > k_max) k_max = o.K;
+        const LinearPlan p = plan_linear(o.bits, M, o.N, o.K);
+        if (p.ws_bytes > lin_ws) lin_ws = p.ws_bytes;
+    }
+    if (phases) *phases = ph;
+    // [q int8 M x k_max][s fp32 x 4][linear workspace]
+    return align256(M * k_max) + 256 + align256(lin_ws);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mbq_status_string(int status) {
+    switch (status) {
+        case MBQ_OK: return "ok";
+        case MBQ_ERR_NULL: return "null pointer";
+        case MBQ_ERR_SHAPE: return "unsupported shape (M in 1..4, K multiple of 128, 1 <= N <= 2^20)";
+        case MBQ_ERR_BITS: return "bits must be 4 or 6";
+        case MBQ_ERR_ALIGN: return "misaligned pointer";
+        case MBQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case MBQ_ERR_PROGRAM: return "malformed op list";
+        case MBQ_ERR_HIP: return "HIP runtime error";
+        case MBQ_ERR_DEVICE: return "current device is not gfx950";
+        case MBQ_ERR_TIMEOUT: return "a wait inside the fused walk gave up";
+        default: return "unknown status";
+    }
+}
+
+int mbq_last_hip_error(void) { return g_last_hip_error; }
+
+const char *mbq_version(void) { return "mbq 0.1 (gfx950)"; }
+
+int64_t mbq_packed_bytes(int bits, int64_t N, int64_t K) {
+    if (!bits_ok(bits)) return MBQ_ERR_BITS;
+    if (!n_ok(N) || !k_ok(K)) return MBQ_ERR_SHAPE;
+    return row_blocks(N) * (K / kGroup) * tile_bytes(bits);
+}
+
+int mbq_pack_weights(int bits, int64_t N, int64_t K, const void *w_canon, const void *scales_f16,
+                     void *packed, void *stream) {
+    if (!bits_ok(bits)) return MBQ_ERR_BITS;
+    if (!w_canon || !scales_f16 || !packed) return MBQ_ERR_NULL;
+    if (!n_ok(N) || !k_ok(K)) return MBQ_ERR_SHAPE;
+    if (!aligned(w_canon, 16) || !aligned(scales_f16, 2) || !aligned(packed, 256)) return MBQ_ERR_ALIGN;
+    int st = check_device();
+    if (st) return st;
+    hipError_t e = launch_pack(bits, N, K, w_canon, scales_f16, packed, (hipStream_t)stream);
+    return e == hipSuccess ? MBQ_OK : hip_fail(e);
+}
+
+int mbq_unpack_weights(int bits, int64_t N, int64_t K, const void *packed, void *w_canon,
+                       void *scales_f16, void *stream) {
+    if (!bits_ok(bits)) return MBQ_ERR_BITS;
+    if (!w_canon || !scales_f16 || !packed) return MBQ_ERR_NULL;
+    if (!n_ok(N) || !k_ok(K)) return MBQ_ERR_SHAPE;
+    if (!aligned(w_canon, 16) || !aligned(scales_f16, 2) || !aligned(packed, 256)) return MBQ_ERR_ALIGN;
+    int st = check_device();
+    if (st) return st;
+    hipError_t e = launch_unpack(bits, N, K, packed, w_canon, scales_f16, (hipStream_t)stream);
+    return e == hipSuccess ? MBQ_OK : hip_fail(e);
+}
+
+static int quant_common(bool norm, int64_t M, int64_t K, const void *x, int8_t *q, float *s,
+                        void *stream) {
+    if (!x || !q || !s) return MBQ_ERR_NULL;
+    if (!m_ok(M) || !k_ok(K)) return MBQ_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return MBQ_ERR_ALIGN;
+    int st = check_device();
+    if (st) return st;
+    hipError_t e = launch_prologue_quant(norm, M, K, x, K, q, s, (hipStream_t)stream);
+    return e == hipSuccess ? MBQ_OK : hip_fail(e);
+}
+
+int mbq_quantize_act(int64_t M, int64_t K, const void *x_bf16, int8_t *q, float *s, void *stream) {
+    return quant_common(false, M, K, x_bf16, q, s, stream);
+}
+
+int mbq_rmsnorm_quantize_act(int64_t M, int64_t K, const void *x_bf16, int8_t *q, float *s,
+                             void *stream) {
+    return quant_common(true, M, K, x_bf16, q, s, stream);
+}
+
+int64_t mbq_linear_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K) {
+    if (!bits_ok(bits)) return MBQ_ERR_BITS;
+    if (!m_ok(M) || !n_ok(N) || !k_ok(K)) return MBQ_ERR_SHAPE;
+    return plan_linear(bits, M, N, K).ws_bytes;
+}
+
+int mbq_w4a8_linear(int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,
+                    const void *packed, void *y_bf16, void *ws, int64_t ws_bytes, void *stream) {
+    return linear_common(4, M, N, K, q, s, packed, y_bf16, ws, ws_bytes, stream);
+}
+
+int mbq_w6a8_linear(int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,
+                    const void *packed, void *y_bf16, void *ws, int64_t ws_bytes, void *stream) {
+    return linear_common(6, M, N, K, q, s, packed, y_bf16, ws, ws_bytes, stream);
+}
+
+int mbq_linear_group_acc(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q,
+                         const void *packed, int32_t *acc, void *stream) {
+    if (!bits_ok(bits)) return MBQ_ERR_BITS;
+    if (!q || !packed || !acc) return MBQ_ERR_NULL;
+    if (!m_ok(M) || !n_ok(N) || !k_ok(K)) return MBQ_ERR_SHAPE;
+    if (!aligned(packed, 256) || !aligned(q, 16) || !aligned(acc, 4)) return MBQ_ERR_ALIGN;
+    int st = check_device();
+    if (st) return st;
+    hipError_t e = launch_group_acc(bits, M, N, K, q, packed, acc, (hipStream_t)stream);
+    return e == hipSuccess ? MBQ_OK : hip_fail(e);
+}
+
+static int device_cus(int *n_cu) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    return e == hipSuccess ? MBQ_OK : hip_fail(e);
+}
+
+int64_t mbq_sequence_workspace_bytes(const mbq_op *ops, int32_t n_ops, const int64_t *buf_widths,
+                                     int32_t n_bufs, int64_t M) {
+    const int64_t unfused = analyse_program(ops, n_ops, buf_widths, n_bufs, M, nullptr);
+    if (unfused < 0) return unfused;
+    int n_cu = 256;                                  // without a device: the MI355X's CU count
+    if (hipGetDeviceCount(&n_cu) == hipSuccess && n_cu > 0) {
+        if (device_cus(&n_cu) != MBQ_OK) n_cu = 256;
+    } else {
+        n_cu = 256;
+    }
+    const int64_t fused = build_sequence_plan(ops, n_ops, nullptr, buf_widths, n_bufs, M, n_cu, nullptr, nullptr);
+    if (fused < 0) return fused;
+    return fused > unfused ? fused : unfused;
+}
+
+static std::atomic<uint32_t> g_generation{0};
+
+int mbq_sequence_prepare(const mbq_op *ops, int32_t n_ops, void *const *bufs, const int64_t *buf_widths,
+                         int32_t n_bufs, int64_t M, void *ws, int64_t ws_bytes, void *stream,
+                         mbq_sequence_info *info) {
+    if (!bufs || !info) return MBQ_ERR_NULL;
+    const int64_t unfused = analyse_program(ops, n_ops, buf_widths, n_bufs, M, nullptr);
+    if (unfused < 0) return (int)unfused;
+    for (int32_t b = 0; b < n_bufs; ++b) {
+        if (!bufs[b]) return MBQ_ERR_NULL;
+        if (!aligned(bufs[b], 16)) return MBQ_ERR_ALIGN;
+    }
+    if (!ws) return MBQ_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return MBQ_ERR_ALIGN;
+    int st = check_device();
+    if (st) return st;
+    int n_cu = 0;
+    st = device_cus(&n_cu);
+    if (st) return st;
+    SeqBuild b;
+    const int64_t need = build_sequence_plan(ops, n_ops, bufs, buf_widths, n_bufs, M, n_cu, (uint8_t *)ws, &b);
+    if (need < 0) return (int)need;
+    if (ws_bytes < need) return MBQ_ERR_WORKSPACE;
+    hipStream_t hs = (hipStream_t)stream;
+    hipError_t e = hipMemsetAsync(ws, 0, 256, hs);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync((char *)ws + b.plan_offset, b.blob.data(), b.blob.size(), hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);
+    if (e != hipSuccess) return hip_fail(e);
+    memset(info, 0, sizeof(*info));
+    info->magic = 0x6d62712d73657131ull;
+    info->bits = b.bits;
+    info->M = (int32_t)M;
+    info->grid = b.grid;
+    info->lds_bytes = b.lds_bytes;
+    info->ws_bytes = need;
+    info->plan_offset = b.plan_offset;
+    return MBQ_OK;
+}
+
+int mbq_sequence_run(const mbq_sequence_info *info, void *ws, void *stream) {
+    if (!info || !ws) return MBQ_ERR_NULL;
+    if (info->magic != 0x6d62712d73657131ull || (info->bits != 4 && info->bits != 6) || info->M < 1 ||
+        info->M > 4 || info->grid < 1)
+        return MBQ_ERR_PROGRAM;
+    if (!aligned(ws, 256)) return MBQ_ERR_ALIGN;
+    uint32_t gen = (g_generation.fetch_add(1, std::memory_order_relaxed) % ((1u << 22) - 1)) + 1;
+    hipError_t e = launch_sequence(info->bits, info->M, info->grid, info->lds_bytes,
+                                   (const char *)ws + info->plan_offset, (uint32_t *)ws, gen,
+                                   (hipStream_t)stream);
+    return e == hipSuccess ? MBQ_OK : hip_fail(e);
+}
+
+int mbq_sequence_check(void *ws, void *stream) {
+    if (!ws) return MBQ_ERR_NULL;
+    uint32_t word = 0;
+    hipStream_t hs = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(&word, ws, 4, hipMemcpyDeviceToHost, hs);
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);
+    if (e != hipSuccess) return hip_fail(e);
+    if (word == 0) return MBQ_OK;
+    e = hipMemsetAsync(ws, 0, 4, hs);
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);
+    if (e != hipSuccess) return hip_fail(e);
+    return word == 2 ? MBQ_ERR_PROGRAM : MBQ_ERR_TIMEOUT;
+}
+
+int mbq_layer_sequence(const mbq_op *ops, int32_t n_ops, void *const *bufs, const int64_t *buf_widths,
+                       int32_t n_bufs, int64_t M, void *ws, int64_t ws_bytes, void *stream) {
+    mbq_sequence_info info;
+    int st = mbq_sequence_prepare(ops, n_ops, bufs, buf_widths, n_bufs, M, ws, ws_bytes, stream, &info);
+    if (st) return st;
+    return mbq_sequence_run(&info, ws, stream);
+}
+
+int mbq_layer_sequence_unfused(const mbq_op *ops, int32_t n_ops, void *const *bufs,
+                               const int64_t *buf_widths, int32_t n_bufs, int64_t M, void *ws,
+                               int64_t ws_bytes, void *stream) {
+    if (!bufs) return MBQ_ERR_NULL;
+    std::vector<Phase> phases;
+    const int64_t need = analyse_program(ops, n_ops, buf_widths, n_bufs, M, &phases);
+    if (need < 0) return (int)need;
+    for (int32_t b = 0; b < n_bufs; ++b) {
+        if (!bufs[b]) return MBQ_ERR_NULL;
+        if (!aligned(bufs[b], 16)) return MBQ_ERR_ALIGN;
+    }
+    if (!ws || ws_bytes < need) return MBQ_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return MBQ_ERR_ALIGN;
+    int st = check_device();
+    if (st) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    int64_t k_max = 0;
+    for (int32_t i = 0; i < n_ops; ++i) k_max = ops[i].K > k_max ? ops[i].K : k_max;
+    int8_t *q = (int8_t *)ws;
+    float *s = (float *)((char *)ws + align256(M * k_max));
+    void *lin_ws = (char *)ws + align256(M * k_max) + 256;
+    for (const Phase &p : phases) {
+        const mbq_op &o0 = ops[p.first];
+        hipError_t e = launch_prologue_quant(o0.prologue == MBQ_PRO_RMSNORM_QUANT, M, o0.K,
+                                             bufs[o0.in_buf], buf_widths[o0.in_buf], q, s, hs);
+        if (e != hipSuccess) return hip_fail(e);
+        for (int32_t i = p.first; i < p.first + p.count; ++i) {
+            const mbq_op &o = ops[i];
+            const LinearPlan plan = plan_linear(o.bits, M, o.N, o.K);
+            e = launch_linear(o.bits, M, o.N, o.K, q, s, o.packed, bufs[o.out_buf], o.N, lin_ws, plan, hs);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+    }
+    return MBQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,232 @@
+// The skinny W4A8 / W6A8 linear, one launch per matrix.
+//
+// "What is the bottleneck?" (page "Doubling LLM token rates in ComfyUI"):
+// one activation row (M = 1) or a thin block (M = 2..4) times a dense weight
+// matrix; every weight is read once for about one operation, so the kernel is
+// a stream over the packed weights.
+//
+// Work split: each wave owns one row block (64 rows, one per lane) and a
+// contiguous range of its k groups (a "split").  For every 64x128 tile the
+// lane unpacks its 128 codes to int8, takes int8 dot products against the
+// activation (wave-uniform, so it is read through the scalar unit and shared
+// by all 64 rows), sums them exactly in int32, and adds the group's
+// scale * sum into an fp32 accumulator.  When a row block has several splits,
+// each writes its fp32 partial to the workspace and the last split to arrive
+// (device-scope counter) sums the partials in split order -- a fixed order, so
+// results are bitwise reproducible -- and writes the bf16 output.  The same
+// last-arriver combine inside one launch is what the page uses for its
+// split-prefix decode attention ("Paying attention to the attention!").
+#include "mbq_internal.h"
+#include "mbq_kernels.h"
+
+namespace mbq {
+
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kTargetWaves = 2048;   // about 8 waves per CU on 256 CUs
+
+template <int BITS, int M>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void linear_kernel(
+    const uint8_t *__restrict__ packed, const int8_t *__restrict__ q, const float *__restrict__ s,
+    uint16_t *__restrict__ y, int64_t y_stride, float *__restrict__ partials,
+    unsigned *__restrict__ counters, int N, int K, int splits) {
+    using L = Layout<BITS>;
+    const int lane = threadIdx.x & 63;
+    const int item = blockIdx.x * kWavesPerBlock + uniform(threadIdx.x >> 6);
+    const int G = K >> 7;
+    const int n_rb = (N + 63) >> 6;
+    const int rb = item / splits;
+    const int sp = item - rb * splits;
+    if (rb >= n_rb) return;
+    const int g0 = (int)(((int64_t)sp * G) / splits);
+    const int g1 = (int)(((int64_t)(sp + 1) * G) / splits);
+
+    const uint8_t *tiles = packed + (int64_t)rb * G * L::kTileBytes;
+    const int *qa = reinterpret_cast<const int *>(q);
+    const int kdw = K >> 2;  // dwords per activation row
+
+    float facc[4][M];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < M; ++m) facc[i][m] = 0.0f;
+    const int slice = lane >> 4;   // this lane's k slice
+
+    v4i wc[L::kSlabs];
+    v2u sc = {0u, 0u};
+    if (g0 < g1) load_tile<BITS>(tiles + (int64_t)g0 * L::kTileBytes, lane, wc, sc);
+    for (int g = g0; g < g1; ++g) {
+        v4i wn[L::kSlabs];
+        v2u sn = {0u, 0u};
+        if (g + 1 < g1) load_tile<BITS>(tiles + (int64_t)(g + 1) * L::kTileBytes, lane, wn, sn);
+        int acc[4][M];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[i][m] = 0;
+        const int *qg = qa + g * 32 + slice * 8;
+        dot_tile<BITS, M>(wc, [&](int m, int d) { return qg[m * kdw + d]; }, acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float S = row_scale(sc, i);
+#pragma unroll
+            for (int m = 0; m < M; ++m) facc[i][m] = fmaf((float)acc[i][m], S, facc[i][m]);
+        }
+#pragma unroll
+        for (int j = 0; j < L::kSlabs; ++j) wc[j] = wn[j];
+        sc = sn;
+    }
+    // lane l takes row l: sum the four k slices, then redistribute
+    float frow[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        float f[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = slice_sum(facc[i][m]);
+        frow[m] = to_row_layout(f, lane);
+    }
+
+    const float unscale = 1.0f / (float)(1 << L::kAccShift);   // exact power of two
+    const int n = rb * 64 + lane;
+    if (splits == 1) {
+        if (n < N) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                y[m * y_stride + n] = (uint16_t)f32_to_bf16_bits(s[m] * (frow[m] * unscale));
+        }
+        return;
+    }
+    float *part = partials + ((int64_t)item * M) * 64;
+#pragma unroll
+    for (int m = 0; m < M; ++m) store_shared(part + m * 64 + lane, frow[m]);
+    wait_memory();
+    unsigned prev = 0;
+    if (lane == 0) prev = counter_add(&counters[rb], 1u);
+    prev = (unsigned)__builtin_amdgcn_readfirstlane((int)prev);
+    if (prev != (unsigned)(splits - 1)) return;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    float tot[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) tot[m] = 0.0f;
+    const float *rbp = partials + ((int64_t)rb * splits * M) * 64;
+    // issue eight partial loads at a time, then add them in split order
+    for (int p0 = 0; p0 < splits; p0 += 8) {
+        float v[8][M];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                v[u][m] = p0 + u < splits ? load_shared(rbp + ((p0 + u) * M + m) * 64 + lane) : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int m = 0; m < M; ++m) tot[m] += v[u][m];
+    }
+    if (n < N) {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            y[m * y_stride + n] = (uint16_t)f32_to_bf16_bits(s[m] * (tot[m] * unscale));
+    }
+    if (lane == 0) store_shared(&counters[rb], 0u);
+}
+
+// Exact int32 group sums for the tests: one wave per tile.
+template <int BITS, int M>
+__global__ __launch_bounds__(64) void group_acc_kernel(const uint8_t *__restrict__ packed,
+                                                       const int8_t *__restrict__ q,
+                                                       int32_t *__restrict__ acc_out, int N, int K) {
+    using L = Layout<BITS>;
+    const int G = K >> 7;
+    const int tile = blockIdx.x;
+    const int rb = tile / G, g = tile % G;
+    const int lane = threadIdx.x;
+    v4i w[L::kSlabs];
+    v2u sb;
+    load_tile<BITS>(packed + (int64_t)tile * L::kTileBytes, lane, w, sb);
+    int acc[4][M];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[i][m] = 0;
+    const int *qg = reinterpret_cast<const int *>(q) + g * 32 + (lane >> 4) * 8;
+    const int kdw = K >> 2;
+    dot_tile<BITS, M>(w, [&](int m, int d) { return qg[m * kdw + d]; }, acc);
+    const int n = rb * 64 + lane;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        int f[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = slice_sum(acc[i][m]);
+        const int v = to_row_layout(f, lane);
+        if (n < N) acc_out[((int64_t)m * N + n) * G + g] = v >> L::kAccShift;
+    }
+}
+
+template <int BITS>
+hipError_t launch_linear_bits(int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,
+                              const void *packed, void *y, int64_t y_stride, void *ws,
+                              const LinearPlan &plan, hipStream_t st) {
+    const int64_t items = plan.n_rb * plan.splits;
+    const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
+    const dim3 block(64 * kWavesPerBlock);
+    unsigned *counters = (unsigned *)ws;
+    float *partials = (float *)((char *)ws + kCounterBytes);
+    const uint8_t *p = (const uint8_t *)packed;
+    uint16_t *yo = (uint16_t *)y;
+#define MBQ_LAUNCH(MM)                                                                          \
+    linear_kernel<BITS, MM><<<grid, block, 0, st>>>(p, q, s, yo, y_stride, partials, counters, \
+                                                    (int)N, (int)K, (int)plan.splits)
+    switch (M) {
+        case 1: MBQ_LAUNCH(1); break;
+        case 2: MBQ_LAUNCH(2); break;
+        case 3: MBQ_LAUNCH(3); break;
+        default: MBQ_LAUNCH(4); break;
+    }
+#undef MBQ_LAUNCH
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_group_acc_bits(int64_t M, int64_t N, int64_t K, const int8_t *q, const void *packed,
+                                 int32_t *acc, hipStream_t st) {
+    const dim3 grid((unsigned)(row_blocks(N) * (K / kGroup)));
+    const uint8_t *p = (const uint8_t *)packed;
+    switch (M) {
+        case 1: group_acc_kernel<BITS, 1><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
+        case 2: group_acc_kernel<BITS, 2><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
+        case 3: group_acc_kernel<BITS, 3><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
+        default: group_acc_kernel<BITS, 4><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+LinearPlan plan_linear(int bits, int64_t M, int64_t N, int64_t K) {
+    (void)bits;
+    LinearPlan p;
+    p.n_rb = row_blocks(N);
+    p.groups = K / kGroup;
+    int64_t sp = (kTargetWaves + p.n_rb - 1) / p.n_rb;
+    if (sp > p.groups) sp = p.groups;
+    if (sp < 1) sp = 1;
+    p.splits = sp;
+    p.ws_bytes = kCounterBytes + (sp > 1 ? p.n_rb * sp * M * 64 * 4 : 0);
+    return p;
+}
+
+hipError_t launch_linear(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,
+                         const void *packed, void *y, int64_t y_stride, void *ws, const LinearPlan &plan,
+                         hipStream_t st) {
+    return bits == 4 ? launch_linear_bits<4>(M, N, K, q, s, packed, y, y_stride, ws, plan, st)
+                     : launch_linear_bits<6>(M, N, K, q, s, packed, y, y_stride, ws, plan, st);
+}
+
+hipError_t launch_group_acc(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q,
+                            const void *packed, int32_t *acc, hipStream_t st) {
+    return bits == 4 ? launch_group_acc_bits<4>(M, N, K, q, packed, acc, st)
+                     : launch_group_acc_bits<6>(M, N, K, q, packed, acc, st);
+}
+
+}  // namespace mbq

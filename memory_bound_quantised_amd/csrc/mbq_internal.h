@@ -1,0 +1,243 @@
+// Internal definitions shared by the HIP kernels of libmbq (gfx950 only).
+//
+// Kernel-order weight layout ("Optimizing the Linear Kernel" on the page
+// "Doubling LLM token rates in ComfyUI": weights and their per-group scales
+// interleaved in the order the kernel consumes them, so that a block streams
+// one contiguous run):
+//
+//   A matrix is cut into row blocks of 64 rows and 128-wide k groups.  Tile
+//   (rb, g) lives at byte offset (rb * G + g) * TILE_BYTES and holds SLABS
+//   slabs of 1024 B followed by the 64 rows' fp16 scales (S[rb*64 + r][g] at
+//   WEIGHT_BYTES + 2*r).  One slab is exactly one wave-wide dwordx4 load
+//   (1 KiB, 8 full 128-B lines).
+//
+//   Lane l of a wave owns rows 4*(l & 15) + i (i = 0..3) of the tile and the
+//   k slice s = l >> 4, i.e. k = g*128 + 32*s + (0..31): each activation
+//   dword it reads is reused for four rows.  The lane's four scales are the 8
+//   bytes at WEIGHT_BYTES + 8*(l & 15).
+//
+//   W4 (4 slabs): slab i holds the lane's row i; lane dword d (0..3) covers
+//   k0 = 32*s + 8*d:
+//     byte b low nibble  = code(k0 + b)      (two's complement)
+//     byte b high nibble = code(k0 + 4 + b)  (two's complement)
+//   so (x << 4) & 0xF0F0F0F0 and x & 0xF0F0F0F0 are four int8 lanes holding
+//   16*w, matching activation dwords k0/4 and k0/4 + 1.
+//
+//   W6 (6 slabs): the lane's 24 dwords D = 4*slab + (dword in slab) form
+//   triples D = 6*i + 3*t + (0, 1, 2) for row i and half t (t = 0, 1), which
+//   cover k0 = 32*s + 16*t + (0..15):
+//     dword c of the triple, byte b, bits 7..2 = code(k0 + 4c + b)      (c = 0, 1, 2)
+//     dword c of the triple, byte b, bits 1..0 = bits (5-2c)..(4-2c) of code(k0 + 12 + b)
+//   so x & 0xFCFCFCFC gives int8 lanes holding 4*w for k0+4c..k0+4c+3, and
+//   ((x0&3)<<6)|((x1&3)<<4)|((x2&3)<<2) gives 4*w for k0+12..k0+15.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mbq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+constexpr int kRows = 64;     // rows per row block = lanes per wave
+constexpr int kGroup = 128;   // k per scale group
+constexpr int kSlab = 1024;   // bytes of one wave-wide dwordx4 load
+
+// Every workspace starts with one fixed region of 32-bit counters, one per
+// row block of the largest supported matrix.  Because its size never depends
+// on the call's shape, counters that one call leaves at zero are still zero
+// for any later call, whatever its shape.
+constexpr int64_t kMaxN = (int64_t)1 << 20;
+constexpr int64_t kCounterBytes = (kMaxN / kRows) * 4;   // 64 KiB
+
+template <int BITS> struct Layout;
+template <> struct Layout<4> {
+    static constexpr int kSlabs = 4;
+    static constexpr int kWeightBytes = 4096;
+    static constexpr int kTileBytes = 4096 + 128;
+    static constexpr int kAccShift = 4;     // unpacked lanes hold 16*w
+};
+template <> struct Layout<6> {
+    static constexpr int kSlabs = 6;
+    static constexpr int kWeightBytes = 6144;
+    static constexpr int kTileBytes = 6144 + 128;
+    static constexpr int kAccShift = 2;     // unpacked lanes hold 4*w
+};
+
+inline int64_t tile_bytes(int bits) { return bits == 4 ? Layout<4>::kTileBytes : Layout<6>::kTileBytes; }
+inline int64_t row_blocks(int64_t N) { return (N + kRows - 1) / kRows; }
+
+// ------------------------------------------------------------------ number formats
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+// Round to nearest even bf16; finite inputs only (inf stays inf, overflow -> inf).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+}
+
+// ------------------------------------------------------------------ integer dot product
+
+__device__ __forceinline__ int dot4(int a, int b, int c) {
+    return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+// Wave-uniform value (the compiler keeps it in an SGPR).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Streaming 16-byte load of packed weights: read once, keep it out of the caches.
+__device__ __forceinline__ v4i load_stream(const v4i *p) {
+    return __builtin_nontemporal_load(p);
+}
+
+// ------------------------------------------------------------------ cross-wave communication
+//
+// Waves on different XCDs see each other's data only at the memory-side
+// coherence point: each XCD has its own L2.  Rather than the compiler's
+// agent-scope fences (which write back and invalidate the whole L2), every
+// value that crosses waves is stored and loaded with agent-scope relaxed
+// atomics (write-through / coherent-read instructions), and the only ordering
+// needed -- "my data is at the coherence point before my counter increment"
+// -- is a wait for this wave's outstanding memory operations.
+
+template <typename T>
+__device__ __forceinline__ void store_shared(T *p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T load_shared(const T *p) {
+    return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_memory() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) expcnt(0) lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ unsigned counter_add(unsigned *p, unsigned v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------ one tile, one lane
+//
+// acc[i][m] += sum over the lane's 32 k of (2^kAccShift * w[row i]) * q[m][k]
+// for the lane's four rows; `act(m, d)` returns activation dword d (k = 32*s +
+// 4d .. +3 of the group, d = 0..7) of row m as four packed int8.
+
+template <int M, typename Act>
+__device__ __forceinline__ void dot_tile_w4(const v4i (&w)[4], Act act, int (&acc)[4][M]) {
+    int a[M][8];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) a[m][d] = act(m, d);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t wd[4] = {(uint32_t)w[i].x, (uint32_t)w[i].y, (uint32_t)w[i].z, (uint32_t)w[i].w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const int lo = (int)((wd[d] << 4) & 0xF0F0F0F0u);
+            const int hi = (int)(wd[d] & 0xF0F0F0F0u);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                acc[i][m] = dot4(lo, a[m][2 * d], acc[i][m]);
+                acc[i][m] = dot4(hi, a[m][2 * d + 1], acc[i][m]);
+            }
+        }
+    }
+}
+
+template <int M, typename Act>
+__device__ __forceinline__ void dot_tile_w6(const v4i (&w)[6], Act act, int (&acc)[4][M]) {
+    int a[M][8];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) a[m][d] = act(m, d);
+    uint32_t wd[24];
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+        wd[4 * j + 0] = (uint32_t)w[j].x;
+        wd[4 * j + 1] = (uint32_t)w[j].y;
+        wd[4 * j + 2] = (uint32_t)w[j].z;
+        wd[4 * j + 3] = (uint32_t)w[j].w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t x0 = wd[6 * i + 3 * t], x1 = wd[6 * i + 3 * t + 1], x2 = wd[6 * i + 3 * t + 2];
+            const uint32_t m6 = 0xFCFCFCFCu;
+            const int a0 = (int)(x0 & m6), a1 = (int)(x1 & m6), a2 = (int)(x2 & m6);
+            const int a3 = (int)(((x0 << 6) & 0xC0C0C0C0u) | ((x1 << 4) & 0x30303030u) |
+                                 ((x2 << 2) & 0x0C0C0C0Cu));
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                acc[i][m] = dot4(a0, a[m][4 * t], acc[i][m]);
+                acc[i][m] = dot4(a1, a[m][4 * t + 1], acc[i][m]);
+                acc[i][m] = dot4(a2, a[m][4 * t + 2], acc[i][m]);
+                acc[i][m] = dot4(a3, a[m][4 * t + 3], acc[i][m]);
+            }
+        }
+}
+
+template <int BITS, int M, typename Act>
+__device__ __forceinline__ void dot_tile(const v4i (&w)[Layout<BITS>::kSlabs], Act act, int (&acc)[4][M]) {
+    if constexpr (BITS == 4)
+        dot_tile_w4<M>(w, act, acc);
+    else
+        dot_tile_w6<M>(w, act, acc);
+}
+
+// The lane's slabs and its four rows' fp16 scales (packed in two dwords).
+template <int BITS>
+__device__ __forceinline__ void load_tile(const uint8_t *tile, int lane, v4i (&w)[Layout<BITS>::kSlabs],
+                                          v2u &scales) {
+#pragma unroll
+    for (int j = 0; j < Layout<BITS>::kSlabs; ++j)
+        w[j] = load_stream(reinterpret_cast<const v4i *>(tile + j * kSlab) + lane);
+    scales = __builtin_nontemporal_load(
+        reinterpret_cast<const v2u *>(tile + Layout<BITS>::kWeightBytes) + (lane & 15));
+}
+
+// fp32 scale of row i (0..3) of the lane from its packed scales.
+__device__ __forceinline__ float row_scale(v2u s, int i) {
+    const uint32_t word = i < 2 ? s.x : s.y;
+    return f16_bits_to_f32((word >> (16 * (i & 1))) & 0xFFFFu);
+}
+
+// Sum a per-lane value over the four k slices (lanes l, l^16, l^32, l^48) in a
+// fixed order; every lane of the group gets the same total.
+__device__ __forceinline__ float slice_sum(float v) {
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+__device__ __forceinline__ int slice_sum(int v) {
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// After slice_sum, row 4r + i of the tile sits in register i of lane r.  Move
+// it so that lane l holds row l.
+template <typename T>
+__device__ __forceinline__ T to_row_layout(const T (&f)[4], int lane) {
+    T r = f[0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const T t = __shfl(f[i], lane >> 2, 64);
+        if ((lane & 3) == i) r = t;
+    }
+    return r;
+}
+
+}  // namespace mbq

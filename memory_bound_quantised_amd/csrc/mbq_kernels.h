@@ -1,0 +1,54 @@
+// Host-side launchers of the libmbq kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+struct mbq_op;
+
+namespace mbq {
+
+hipError_t launch_pack(int bits, int64_t N, int64_t K, const void *canon, const void *scales,
+                       void *packed, hipStream_t s);
+hipError_t launch_unpack(int bits, int64_t N, int64_t K, const void *packed, void *canon,
+                         void *scales, hipStream_t s);
+
+// Per-row quantisation (optionally after the weightless RMSNorm) of columns
+// [0, K) of x (bf16, row stride x_stride elements).
+hipError_t launch_prologue_quant(bool rmsnorm, int64_t M, int64_t K, const void *x, int64_t x_stride,
+                                 int8_t *q, float *s, hipStream_t st);
+
+// Per-op skinny linear: work split, workspace size and launch.
+struct LinearPlan {
+    int64_t n_rb;      // row blocks of 64
+    int64_t groups;    // K / 128
+    int64_t splits;    // waves per row block (k ranges)
+    int64_t ws_bytes;  // counters + fp32 partials
+};
+LinearPlan plan_linear(int bits, int64_t M, int64_t N, int64_t K);
+hipError_t launch_linear(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,
+                         const void *packed, void *y, int64_t y_stride, void *ws, const LinearPlan &plan,
+                         hipStream_t st);
+hipError_t launch_group_acc(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q,
+                            const void *packed, int32_t *acc, hipStream_t st);
+
+// Fused decode-step walk (persistent kernel).
+struct SeqBuild {
+    int64_t ws_bytes = 0;
+    int64_t plan_offset = 0;
+    int grid = 0;
+    int lds_bytes = 0;
+    int bits = 0;
+    std::vector<uint8_t> blob;   // plan bytes to copy to ws + plan_offset
+};
+// Validates the op list and lays out the workspace; with ws and bufs also fills
+// out->blob with the device plan.  Returns the workspace bytes or a negative status.
+int64_t build_sequence_plan(const struct mbq_op *ops, int32_t n_ops, void *const *bufs,
+                            const int64_t *widths, int32_t n_bufs, int64_t M, int n_cu, uint8_t *ws,
+                            SeqBuild *out);
+hipError_t launch_sequence(int bits, int64_t M, int grid, int lds_bytes, const void *plan, uint32_t *err,
+                           uint32_t gen, hipStream_t st);
+
+}  // namespace mbq

@@ -53,6 +53,7 @@ def _load():
         lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
         lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_to_f64.restype = ctypes.c_double
+        lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_w4_code.argtypes = [P, I64]
         lib.oracle_w6_code.argtypes = [P, I64]
         _lib = lib
@@ -124,6 +125,11 @@ def linear(bits: int, q: np.ndarray, s: np.ndarray, canon: np.ndarray, scales: n
     if rc:
         raise ValueError("bad bits or K")
     return (y, pre) if want_pre else y
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's loops run on."""
+    return int(_load().oracle_num_threads())
 
 
 def f64_to_bf16(v: float) -> int:

@@ -31,6 +31,7 @@
  * Every loop below is the plain definition: no blocking, no reordering.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -200,6 +201,9 @@ int oracle_linear(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q, co
     }
     return 0;
 }
+
+/* Threads the OpenMP loops above use (reported with CPU timings). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* Exposed for the tests of the number formats. */
 uint16_t oracle_f64_to_bf16(double v) { return f64_to_bf16(v); }

@@ -1,0 +1,145 @@
+"""The C-ABI library loads, exports what include/mbq.h declares, and rejects bad
+arguments before touching the GPU.  No compute call runs here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import memory_bound_quantised_amd as mbq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mbq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mbq.LIB_PATH),
+                                reason="libmbq.so not built (python -m memory_bound_quantised_amd.build)")
+
+A = 1 << 20          # a 256-byte-aligned fake device address; never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mbq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("mbq_quantize_act", "mbq_w4a8_linear", "mbq_w6a8_linear", "mbq_layer_sequence",
+                     "mbq_pack_weights"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported():
+    L = ctypes.CDLL(mbq.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing
+    assert sorted(mbq.EXPORTS) == declared_functions()
+
+
+def test_status_strings_and_version():
+    L = mbq.lib()
+    assert L.mbq_status_string(0) == b"ok"
+    assert b"bits" in L.mbq_status_string(-3)
+    assert L.mbq_status_string(12345) == b"unknown status"
+    assert L.mbq_version().startswith(b"mbq")
+    assert L.mbq_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("bits,N,K,tile", [(4, 1, 128, 4224), (4, 64, 4096, 4224), (4, 65, 256, 4224),
+                                           (6, 4096, 4096, 6272), (6, 200, 1152, 6272)])
+def test_packed_bytes_formula(bits, N, K, tile):
+    assert mbq.packed_bytes(bits, N, K) == ((N + 63) // 64) * (K // 128) * tile
+    # never smaller than the algorithmic bytes: codes plus fp16 group scales
+    assert mbq.packed_bytes(bits, N, K) >= N * K * bits // 8 + N * (K // 128) * 2
+
+
+def test_packed_bytes_rejects():
+    L = mbq.lib()
+    assert L.mbq_packed_bytes(5, 64, 128) == -3
+    assert L.mbq_packed_bytes(4, 0, 128) == -2
+    assert L.mbq_packed_bytes(4, 64, 100) == -2
+    assert L.mbq_packed_bytes(4, 64, 0) == -2
+
+
+def test_linear_argument_validation():
+    L = mbq.lib()
+    ws_need = L.mbq_linear_workspace_bytes(4, 1, 4096, 4096)
+    assert ws_need > 0
+    f = L.mbq_w4a8_linear
+    assert f(1, 4096, 4096, None, A, A, A, A, ws_need, None) == -1          # null q
+    assert f(0, 4096, 4096, A, A, A, A, A, ws_need, None) == -2             # M = 0
+    assert f(5, 4096, 4096, A, A, A, A, A, ws_need, None) == -2             # M = 5
+    assert f(1, 4096, 4000, A, A, A, A, A, ws_need, None) == -2             # K % 128
+    assert f(1, 0, 4096, A, A, A, A, A, ws_need, None) == -2                # N = 0
+    assert f(1, 4096, 4096, A, A, A + 16, A, A, ws_need, None) == -4        # packed not 256-aligned
+    assert f(1, 4096, 4096, A + 4, A, A, A, A, ws_need, None) == -4         # q not 16-aligned
+    assert f(1, 4096, 4096, A, A, A, A, A, ws_need - 1, None) == -5         # workspace too small
+    assert f(1, 4096, 4096, A, A, A, A, None, ws_need, None) == -5          # no workspace
+    assert L.mbq_w6a8_linear(1, 64, 128, A, A, A, A, A + 8, 1 << 30, None) == -4   # ws alignment
+    assert L.mbq_linear_workspace_bytes(7, 1, 64, 128) == -3
+    assert L.mbq_linear_group_acc(5, 1, 64, 128, A, A, A, None) == -3
+    assert L.mbq_linear_group_acc(4, 1, 64, 128, None, A, A, None) == -1
+
+
+def test_quant_and_pack_validation():
+    L = mbq.lib()
+    assert L.mbq_quantize_act(1, 4096, None, A, A, None) == -1
+    assert L.mbq_quantize_act(5, 4096, A, A, A, None) == -2
+    assert L.mbq_rmsnorm_quantize_act(1, 64, A, A, A, None) == -2
+    assert L.mbq_quantize_act(1, 4096, A + 2, A, A, None) == -4
+    assert L.mbq_pack_weights(3, 64, 128, A, A, A, None) == -3
+    assert L.mbq_pack_weights(4, 64, 128, None, A, A, None) == -1
+    assert L.mbq_pack_weights(4, 64, 130, A, A, A, None) == -2
+    assert L.mbq_pack_weights(6, 64, 128, A, A, A + 128, None) == -4
+    assert L.mbq_unpack_weights(6, 64, 128, A, A, None, None) == -1
+
+
+def _program(ops):
+    arr = (mbq.MbqOp * len(ops))()
+    for i, o in enumerate(ops):
+        arr[i] = mbq.MbqOp(*o)
+    return arr
+
+
+def test_sequence_program_validation():
+    L = mbq.lib()
+    W = (ctypes.c_int64 * 3)(256, 512, 256)
+    good = _program([(4, 1, 512, 256, A, 0, 1), (4, 0, 256, 512, A, 1, 2)])
+    assert L.mbq_sequence_workspace_bytes(good, 2, W, 3, 1) > 0
+    bad_cases = {
+        "out of range buffer": ([(4, 1, 512, 256, A, 0, 3)], -6),
+        "in place": ([(4, 1, 256, 256, A, 0, 0)], -6),
+        "N != width": ([(4, 1, 256, 256, A, 0, 1)], -6),
+        "K > width": ([(4, 1, 512, 384, A, 0, 1)], -6),
+        "bad prologue": ([(4, 7, 512, 256, A, 0, 1)], -6),
+        "bad bits": ([(5, 1, 512, 256, A, 0, 1)], -3),
+        "null weights": ([(4, 1, 512, 256, None, 0, 1)], -1),
+        "misaligned weights": ([(4, 1, 512, 256, A + 64, 0, 1)], -4),
+        "same output twice in a phase": ([(4, 1, 512, 256, A, 0, 1), (4, 1, 512, 256, A, 0, 1)], -6),
+    }
+    for name, (ops, want) in bad_cases.items():
+        assert L.mbq_sequence_workspace_bytes(_program(ops), len(ops), W, 3, 1) == want, name
+    assert L.mbq_sequence_workspace_bytes(good, 2, W, 3, 5) == -2
+    assert L.mbq_sequence_workspace_bytes(good, 0, W, 3, 1) == -6
+    W_bad = (ctypes.c_int64 * 3)(256, 500, 256)
+    assert L.mbq_sequence_workspace_bytes(good, 2, W_bad, 3, 1) == -6
+    bufs = (ctypes.c_void_p * 3)(A, A, A)
+    need = L.mbq_sequence_workspace_bytes(good, 2, W, 3, 1)
+    f = L.mbq_layer_sequence_unfused
+    assert f(good, 2, bufs, W, 3, 1, A, 1, None) == -5
+    assert f(good, 2, None, W, 3, 1, A, need, None) == -1
+    bufs_bad = (ctypes.c_void_p * 3)(A, A + 2, A)
+    assert f(good, 2, bufs_bad, W, 3, 1, A, need, None) == -4
+    info = mbq.MbqSequenceInfo()
+    assert L.mbq_layer_sequence(good, 2, None, W, 3, 1, A, need, None) == -1
+    assert L.mbq_sequence_prepare(good, 2, bufs_bad, W, 3, 1, A, need, None, ctypes.byref(info)) == -4
+    assert L.mbq_sequence_prepare(good, 2, bufs, W, 3, 1, A, need, None, None) == -1
+    assert L.mbq_sequence_prepare(good, 2, bufs, W, 3, 1, A + 64, need, None, ctypes.byref(info)) == -4
+    # mixed bit widths are accepted by the unfused walk only
+    mixed = _program([(4, 1, 512, 256, A, 0, 1), (6, 0, 256, 512, A, 1, 2)])
+    assert L.mbq_sequence_workspace_bytes(mixed, 2, W, 3, 1) == -6
+    # run refuses an info block that prepare did not fill
+    assert L.mbq_sequence_run(ctypes.byref(info), A, None) == -6
+    assert L.mbq_sequence_run(None, A, None) == -1
+    assert L.mbq_sequence_check(None, None) == -1

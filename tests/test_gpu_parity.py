@@ -1,0 +1,299 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars: quantised activations, their scales, packed/unpacked bytes and int32
+group sums are bit-exact; bf16 outputs agree within 1e-3 absolute + 1e-2
+relative.  Inputs are seeded and synthetic (see synth/).
+"""
+import numpy as np
+import pytest
+
+import memory_bound_quantised_amd as mbq
+import oracle
+import synth
+from tests.gpu_util import (assert_close_bf16, dev, host, oracle_rows, packed_on_device,
+                            sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mbq.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def special_rows(K):
+    """Rows that exercise quantisation corner cases."""
+    rows = []
+    z = np.zeros(K, np.float32)
+    rows.append(z)                                            # all zero
+    t = np.zeros(K, np.float32)
+    t[:8] = [127.0, 2.5, -2.5, 0.5, 1.5, -0.5, 126.5, -127.0]  # exact ties at s = 1
+    rows.append(t)
+    one = np.zeros(K, np.float32)
+    one[K - 1] = -3.0                                         # single nonzero at the tail
+    rows.append(one)
+    big = np.random.default_rng(K).standard_normal(K).astype(np.float32) * 1e4
+    rows.append(big)
+    return synth.f32_to_bf16_bits(np.stack(rows))
+
+
+# ---------------------------------------------------------------- activation quantisation
+
+@pytest.mark.parametrize("rmsnorm", [False, True])
+@pytest.mark.parametrize("K", [128, 4096, 5120, 17408])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_quantize_bit_exact(M, K, rmsnorm):
+    x = synth.activations(M, K, seed=K + M)
+    q, s = mbq.quantize_act(dev(x), rmsnorm=rmsnorm)
+    qo, so = oracle.prologue_quant(x, oracle.PRO_RMSNORM_QUANT if rmsnorm else oracle.PRO_QUANT)
+    assert np.array_equal(host(q), qo)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+
+
+@pytest.mark.parametrize("rmsnorm", [False, True])
+@pytest.mark.parametrize("K", [128, 4096])
+def test_quantize_special_rows(K, rmsnorm):
+    x = special_rows(K)
+    for start in range(0, 4, 4):
+        xb = x[start:start + 4]
+        q, s = mbq.quantize_act(dev(xb), rmsnorm=rmsnorm)
+        qo, so = oracle.prologue_quant(xb, oracle.PRO_RMSNORM_QUANT if rmsnorm else oracle.PRO_QUANT)
+        assert np.array_equal(host(q), qo)
+        assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+
+
+# ---------------------------------------------------------------- layout
+
+@pytest.mark.parametrize("bits", [4, 6])
+@pytest.mark.parametrize("N,K", [(1, 128), (63, 256), (65, 1152), (200, 4096)])
+def test_pack_unpack_roundtrip(bits, N, K):
+    canon, S = synth.weights(bits, N, K, seed=N * 7 + K)
+    packed = packed_on_device(bits, canon, S, N, K)
+    assert packed.numel() == mbq.packed_bytes(bits, N, K)
+    c2, s2 = mbq.unpack_weights(bits, packed, N, K)
+    assert np.array_equal(host(c2), canon)
+    assert np.array_equal(host(s2).view(np.uint16), S.view(np.uint16))
+
+
+@pytest.mark.parametrize("bits", [4, 6])
+def test_pack_pads_rows_with_zeros(bits):
+    N, K = 70, 256
+    canon, S = synth.weights(bits, N, K, seed=3)
+    packed = host(packed_on_device(bits, canon, S, N, K))
+    tile = 4224 if bits == 4 else 6272
+    G = K // 128
+    # row block 1 holds rows 64..127; lanes 6..63 are padding
+    for g in range(G):
+        t = packed[(1 * G + g) * tile:(1 * G + g + 1) * tile]
+        slabs = t[:tile - 128].reshape(-1, 64, 16)
+        assert not slabs[:, 6:, :].any()
+        assert not t[tile - 128:].reshape(64, 2)[6:].any()
+
+
+# ---------------------------------------------------------------- exact integer sums
+
+@pytest.mark.parametrize("bits", [4, 6])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("N,K", [(64, 128), (200, 1152)])
+def test_group_acc_bit_exact(bits, M, N, K):
+    canon, S = synth.weights(bits, N, K, seed=11 + N)
+    x = synth.activations(M, K, seed=5)
+    q, _ = oracle.quantize_act(x)
+    acc = mbq.linear_group_acc(bits, dev(q), packed_on_device(bits, canon, S, N, K), N)
+    assert np.array_equal(host(acc), oracle.group_acc(bits, q, canon))
+
+
+@pytest.mark.parametrize("bits", [4, 6])
+def test_group_acc_extreme_codes(bits):
+    # every weight at the most negative code and every activation at -127:
+    # the largest group sums the format allows (130048 for W4, 520192 for W6)
+    N, K, M = 64, 256, 4
+    lo = -8 if bits == 4 else -32
+    from tests.codes import pack
+    canon = pack(bits, np.full((N, K), lo))
+    S = np.ones((N, K // 128), np.float16)
+    q = np.full((M, K), -127, np.int8)
+    acc = mbq.linear_group_acc(bits, dev(q), packed_on_device(bits, canon, S, N, K), N)
+    assert np.all(host(acc) == 128 * 127 * -lo)
+
+
+# ---------------------------------------------------------------- the linear
+
+@pytest.mark.parametrize("bits", [4, 6])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("N,K", [(1, 128), (200, 1152), (1000, 4096), (4096, 4096)])
+def test_linear_vs_oracle(bits, M, N, K):
+    canon, S = synth.weights(bits, N, K, seed=1)
+    x = synth.activations(M, K)
+    q, s = oracle.quantize_act(x)
+    y = mbq.linear(bits, dev(q), dev(s), packed_on_device(bits, canon, S, N, K), N)
+    assert_close_bf16(host(y), oracle.linear(bits, q, s, canon, S), f"W{bits} M={M} {N}x{K}")
+
+
+# Full-size shapes of the 9B- and 27B-shaped decode steps; outputs checked on sampled rows.
+FULL_SHAPES = [(4096, 4096), (1024, 4096), (12288, 4096), (4096, 12288), (16384, 5120),
+               (1024, 5120), (5120, 8192), (17408, 5120), (5120, 17408)]
+
+
+@pytest.mark.parametrize("bits", [4, 6])
+@pytest.mark.parametrize("M", [1, 3])
+@pytest.mark.parametrize("N,K", FULL_SHAPES)
+def test_linear_full_size_sampled(bits, M, N, K):
+    canon, S = synth.weights(bits, N, K, seed=N + K)
+    x = synth.activations(M, K)
+    q, s = oracle.quantize_act(x)
+    y = host(mbq.linear(bits, dev(q), dev(s), packed_on_device(bits, canon, S, N, K), N))
+    rows = sample_rows(np.random.default_rng(N), N)
+    ref = oracle.linear(bits, q, s, canon[rows], S[rows])
+    assert_close_bf16(y[:, rows], ref, f"W{bits} M={M} {N}x{K}")
+
+
+@pytest.mark.parametrize("bits", [4, 6])
+def test_linear_rows_independent_and_deterministic(bits):
+    N, K = 3000, 5120
+    canon, S = synth.weights(bits, N, K, seed=9)
+    packed = packed_on_device(bits, canon, S, N, K)
+    x = synth.activations(3, K)
+    q, s = oracle.quantize_act(x)
+    y3 = host(mbq.linear(bits, dev(q), dev(s), packed, N))
+    y3b = host(mbq.linear(bits, dev(q), dev(s), packed, N))
+    assert np.array_equal(y3, y3b)
+    for m in range(3):
+        ym = host(mbq.linear(bits, dev(q[m:m + 1]), dev(s[m:m + 1]), packed, N))
+        assert np.array_equal(ym, y3[m:m + 1])
+
+
+def test_linear_zero_row():
+    N, K = 256, 1024
+    canon, S = synth.weights(4, N, K, seed=2)
+    x = synth.activations(2, K)
+    x[0] = 0
+    q, s = oracle.quantize_act(x)
+    y = host(mbq.linear(4, dev(q), dev(s), packed_on_device(4, canon, S, N, K), N))
+    assert not y[0].any()
+
+
+def test_linear_workspace_reused_across_shapes():
+    """The split counters reset themselves, so one workspace serves any later call."""
+    import torch
+    ws = torch.zeros(1 << 24, dtype=torch.uint8, device="cuda")
+    for (bits, M, N, K) in [(4, 1, 4096, 4096), (6, 4, 200, 1152), (4, 3, 17408, 5120), (4, 1, 64, 128),
+                            (6, 2, 5120, 17408)]:
+        canon, S = synth.weights(bits, N, K, seed=M * N)
+        x = synth.activations(M, K)
+        q, s = oracle.quantize_act(x)
+        y = host(mbq.linear(bits, dev(q), dev(s), packed_on_device(bits, canon, S, N, K), N, ws=ws))
+        rows = sample_rows(np.random.default_rng(1), N)
+        assert_close_bf16(y[:, rows], oracle.linear(bits, q, s, canon[rows], S[rows]), f"{bits} {N}x{K}")
+    torch.cuda.synchronize()
+    assert not ws[:65536].any()   # counters region left at zero
+
+
+# ---------------------------------------------------------------- decode-step walk
+
+def _run_sequence(bits, shapes_fn, n_layers, M, distinct, seed_base=0, fused=True, runs=1):
+    import torch
+    ops, widths = synth.layer_program(shapes_fn, n_layers, distinct_buffers=distinct)
+    mats = {}
+    dev_ops = []
+    for o in ops:
+        canon, S = synth.weights(bits, o["N"], o["K"], seed=1 + o["matrix"] + seed_base)
+        mats[o["matrix"]] = (canon, S)
+        dev_ops.append(dict(bits=bits, prologue=o["prologue"], N=o["N"], K=o["K"],
+                            packed=packed_on_device(bits, canon, S, o["N"], o["K"]),
+                            in_buf=o["in_buf"], out_buf=o["out_buf"]))
+    bufs = [torch.zeros((M, w), dtype=torch.bfloat16, device="cuda") for w in widths]
+    x0 = synth.activations(M, widths[0])
+    bufs[0].copy_(dev(x0))
+    seq = mbq.LayerSequence(dev_ops, bufs, M, fused=fused)
+    outs = []
+    for _ in range(runs):
+        bufs[0].copy_(dev(x0))
+        seq.run()
+        if fused:
+            seq.check()
+        torch.cuda.synchronize()
+        outs.append([host(b) for b in bufs])
+    if runs > 1:
+        return ops, mats, outs, x0
+    return ops, mats, outs[0], x0
+
+
+def _small_shapes():
+    H, I, KV = 256, 384, 128
+    return [("q", H, H), ("k", H, KV), ("v", H, KV), ("o", H, H),
+            ("gate", H, I), ("up", H, I), ("down", I, H)]
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("bits", [4, 6])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_layer_sequence_teacher_forced_small(bits, M, fused):
+    ops, mats, bufs, _ = _run_sequence(bits, _small_shapes, 3, M, distinct=True, fused=fused)
+    for o in ops:
+        x = np.ascontiguousarray(bufs[o["in_buf"]][:, :o["K"]])
+        ref = oracle.op(bits, x, o["prologue"], *mats[o["matrix"]])
+        assert_close_bf16(bufs[o["out_buf"]], ref, o["name"])
+
+
+@pytest.mark.parametrize("bits", [4, 6])
+@pytest.mark.parametrize("M", [1, 3])
+def test_layer_sequence_9b_layers_teacher_forced(bits, M):
+    ops, mats, bufs, _ = _run_sequence(bits, synth.layer_shapes_9b, 2, M, distinct=True)
+    rng = np.random.default_rng(4)
+    for o in ops:
+        x = np.ascontiguousarray(bufs[o["in_buf"]][:, :o["K"]])
+        canon, S = mats[o["matrix"]]
+        rows = sample_rows(rng, o["N"], 128)
+        ref = oracle_rows(bits, x, o["prologue"], canon, S, rows)
+        assert_close_bf16(bufs[o["out_buf"]][:, rows], ref, o["name"])
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_layer_sequence_27b_layer_teacher_forced(M):
+    """One 27B-shaped layer: q is 16384 wide and o reads its first 8192 columns."""
+    ops, mats, bufs, _ = _run_sequence(4, synth.layer_shapes_27b, 1, M, distinct=True)
+    rng = np.random.default_rng(5)
+    for o in ops:
+        x = np.ascontiguousarray(bufs[o["in_buf"]][:, :o["K"]])
+        canon, S = mats[o["matrix"]]
+        rows = sample_rows(rng, o["N"], 128)
+        ref = oracle_rows(4, x, o["prologue"], canon, S, rows)
+        assert_close_bf16(bufs[o["out_buf"]][:, rows], ref, o["name"])
+
+
+@pytest.mark.parametrize("bits", [4, 6])
+def test_layer_sequence_fused_deterministic_and_rerunnable(bits):
+    """Two runs of one prepared walk give bitwise equal buffers, and the fused
+    walk agrees with the unfused one within the output tolerance."""
+    ops, mats, outs, _ = _run_sequence(bits, _small_shapes, 4, 3, distinct=True, runs=2)
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+    _, _, unf, _ = _run_sequence(bits, _small_shapes, 4, 3, distinct=True, fused=False)
+    # first layer: same inputs, so outputs agree within the linear's tolerance
+    for o in ops[:7]:
+        assert_close_bf16(outs[0][o["out_buf"]], unf[o["out_buf"]], o["name"])
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_layer_sequence_bench_configuration(M):
+    """The 36-layer 9B-shaped walk with reused buffers, as the benchmark runs it.
+    The last layer's o, gate, up and down inputs survive in their buffers and are
+    checked teacher-forced on sampled rows."""
+    ops, mats, bufs, _ = _run_sequence(4, synth.layer_shapes_9b, 36, M, distinct=False)
+    last = [o for o in ops if o["name"].startswith("L35.") and o["name"].split(".")[1]
+            in ("o", "gate", "up", "down")]
+    rng = np.random.default_rng(6)
+    for o in last:
+        x = np.ascontiguousarray(bufs[o["in_buf"]][:, :o["K"]])
+        canon, S = mats[o["matrix"]]
+        rows = sample_rows(rng, o["N"], 128)
+        ref = oracle_rows(4, x, o["prologue"], canon, S, rows)
+        assert_close_bf16(bufs[o["out_buf"]][:, rows], ref, o["name"])
+    for b in bufs:
+        assert np.all(np.isfinite(synth.bf16_bits_to_f32(b)))
