@@ -93,9 +93,18 @@ __device__ __forceinline__ int dot4(int a, int b, int c) {
 // Wave-uniform value (the compiler keeps it in an SGPR).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Every pointer these kernels dereference in global memory goes through the
+// global address space: generic (flat) accesses also count on the LDS/scalar
+// counter, so an LDS read would then wait for every weight load in flight.
+#define MBQ_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ MBQ_GLOBAL T *gptr(T *p) { return (MBQ_GLOBAL T *)p; }
+template <typename T>
+__device__ __forceinline__ const MBQ_GLOBAL T *gptr(const T *p) { return (const MBQ_GLOBAL T *)p; }
+
 // Streaming 16-byte load of packed weights: read once, keep it out of the caches.
 __device__ __forceinline__ v4i load_stream(const v4i *p) {
-    return __builtin_nontemporal_load(p);
+    return __builtin_nontemporal_load(gptr(p));
 }
 
 // ------------------------------------------------------------------ cross-wave communication
@@ -110,11 +119,11 @@ __device__ __forceinline__ v4i load_stream(const v4i *p) {
 
 template <typename T>
 __device__ __forceinline__ void store_shared(T *p, T v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gptr(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 template <typename T>
 __device__ __forceinline__ T load_shared(const T *p) {
-    return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(gptr(const_cast<T *>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_memory() {
@@ -123,7 +132,7 @@ __device__ __forceinline__ void wait_memory() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 __device__ __forceinline__ unsigned counter_add(unsigned *p, unsigned v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_fetch_add(gptr(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ one tile, one lane
@@ -205,7 +214,7 @@ __device__ __forceinline__ void load_tile(const uint8_t *tile, int lane, v4i (&w
     for (int j = 0; j < Layout<BITS>::kSlabs; ++j)
         w[j] = load_stream(reinterpret_cast<const v4i *>(tile + j * kSlab) + lane);
     scales = __builtin_nontemporal_load(
-        reinterpret_cast<const v2u *>(tile + Layout<BITS>::kWeightBytes) + (lane & 15));
+        gptr(reinterpret_cast<const v2u *>(tile + Layout<BITS>::kWeightBytes) + (lane & 15)));
 }
 
 // fp32 scale of row i (0..3) of the lane from its packed scales.

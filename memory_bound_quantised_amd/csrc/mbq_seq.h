@@ -11,7 +11,7 @@ constexpr int kSeqWaves = 4;                   // waves per workgroup
 constexpr int kSeqThreads = 64 * kSeqWaves;
 constexpr int kChunkGroups = 8;                // k groups per k chunk (1024 k)
 constexpr int kStatRecBytes = 128;             // one per (producer op, row block)
-constexpr int kMaxPhases = 1000;
+constexpr int kMaxPhases = 1000;             // < 2^kRunPhaseBits
 constexpr uint64_t kPlanMagic = 0x6d62712d73657131ull;  // "mbq-seq1"
 
 // Every value that one wave hands to another travels in a 64-bit word whose
@@ -56,6 +56,23 @@ struct SeqPhase {
                                  // last tile the workgroup owns (it finalises them)
 };
 
+// One run of a wave's walk: consecutive tiles of one segment (k chunk x row
+// block), contiguous in memory.  hdr packs what the compute side needs when
+// the run starts: bits 0-9 phase, 10-17 the wave's LDS partial slot, 18-29
+// the run's first group relative to the workgroup's first quantised column
+// (in groups), bit 31 set.
+struct SeqRun {
+    const uint8_t *src;      // first tile
+    uint32_t hdr;
+    uint32_t n;              // tiles (1 .. kChunkGroups)
+};
+constexpr uint32_t kRunStart = 1u << 31;
+constexpr int kRunPhaseBits = 10, kRunSlotBits = 8, kRunGroupBits = 12;
+
+struct SeqWave {             // one wave's slice of the run table
+    int32_t run_begin, run_count, tiles, pad;
+};
+
 struct SeqExt {              // an input no op of the walk writes: stats at kernel start
     const uint32_t *in;
     int32_t in_stride2, K;
@@ -77,6 +94,8 @@ struct SeqPlan {
     uint8_t *stats;          // stats records
     uint64_t *partials;      // [segment][part][m][lane]: value bits | tag << 32
     const uint8_t *dummy;    // readable tile-sized area for loads past a stream's end
+    const SeqRun *runs;      // every wave's runs, wave after wave, each in walk order
+    const SeqWave *wtab;     // [waves]
 };
 
 }  // namespace mbq

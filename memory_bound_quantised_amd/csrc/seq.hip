@@ -32,7 +32,6 @@ namespace mbq {
 
 namespace {
 
-constexpr int kRing = 4;                     // tiles in flight per wave
 constexpr int64_t kSpinLimit = 1ll << 23;    // polls before a wait gives up
 
 __device__ __forceinline__ uint32_t make_tag(uint32_t gen, int phase) {
@@ -191,7 +190,7 @@ constexpr int kXBatch = 4;      // input words (2 columns each) per thread per r
 // the producer's stats records, reduced in a fixed order so that every
 // workgroup derives bit-identical scales.  Returns k_lo.
 template <int M>
-__device__ __noinline__ int enter_phase(const SeqPlan *P, int p, uint32_t gen, int wg, int8_t *q_lds,
+__device__ __noinline__ void enter_phase(const SeqPlan *P, int p, uint32_t gen, int wg, int8_t *q_lds,
                                         float (*s_sh)[4], float (*r_sh)[4]) {
     const SeqPhase ph = cload(P->phases, p);
     const WgRange kr = wg_range(ph, wg);
@@ -343,7 +342,6 @@ __device__ __noinline__ int enter_phase(const SeqPlan *P, int p, uint32_t gen, i
         }
     }
     __syncthreads();
-    return kr.k_lo;
 }
 
 // ---------------------------------------------------------------- row-block finalisation (cold path)
@@ -440,146 +438,63 @@ template <int BITS>
 struct Slot {
     v4i w[Layout<BITS>::kSlabs];
     v2u sc;
-    int phase;   // -1: past the end of the stream
-    int kc, rb, g;
+    uint32_t hdr;   // the run header if this tile opens a run, else 0
 };
 
-// Per-wave walk state (all wave-uniform: it lives in scalar registers).
-struct Walk {
-    // issue cursor
-    int ip, it, iend;        // phase, next tile, end of this wave's range
-    int kc, rb, gi, len;     // position of tile `it`: chunk, row block, group in chunk, chunk length
-    int R, G, nkc, op_first; // geometry of phase ip
-    int op, op_end;          // op owning rb, and its last row block + 1
-    int op_rb0;              // first row block of that op
-    const uint8_t *op_w;     // its packed weights
-    // compute side
-    int active;              // phase whose prologue ran last
-    int k_lo;                // first column of the workgroup's LDS activations
-    int seg_kc, seg_rb;      // open segment; seg_kc < 0: none
+// Tiles in flight per wave.  A wave can have at most 63 vector loads
+// outstanding and a tile takes kSlabs + 1 of them (W4: 12 tiles, W6: 9);
+// larger M trims the ring to stay within 512 registers.
+template <int BITS, int M>
+constexpr int ring_depth() {
+    return BITS == 4 ? (M < 4 ? 12 : 10) : (M < 3 ? 9 : (M < 4 ? 8 : 7));
+}
+static_assert(ring_depth<4, 1>() * (Layout<4>::kSlabs + 1) <= 63, "vmcnt limit");
+static_assert(ring_depth<6, 1>() * (Layout<6>::kSlabs + 1) <= 63, "vmcnt limit");
+
+// Issue side: a cursor over the wave's run list.  Everything here is
+// wave-uniform and read with scalar loads, so waiting on a tile never waits
+// on a plan read.
+struct Issue {
+    const SeqRun *runs;
+    int next, count;       // next run to open; runs of this wave
+    int left;              // tiles left in the open run
+    const uint8_t *src;    // next tile
 };
-
-// Re-assert that the walk state is wave-uniform: after control flow the
-// compiler's divergence analysis can lose track of it, and then the cursor
-// arithmetic and plan reads would move to vector registers and vector loads.
-template <typename T>
-__device__ __forceinline__ const T *uniform_ptr(const T *p) {
-    const uint64_t v = (uint64_t)p;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
-    return (const T *)(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ void uniformize(Walk &st) {
-    st.ip = uniform(st.ip);
-    st.it = uniform(st.it);
-    st.iend = uniform(st.iend);
-    st.kc = uniform(st.kc);
-    st.rb = uniform(st.rb);
-    st.gi = uniform(st.gi);
-    st.len = uniform(st.len);
-    st.R = uniform(st.R);
-    st.G = uniform(st.G);
-    st.nkc = uniform(st.nkc);
-    st.op_first = uniform(st.op_first);
-    st.op = uniform(st.op);
-    st.op_end = uniform(st.op_end);
-    st.op_rb0 = uniform(st.op_rb0);
-    st.op_w = uniform_ptr(st.op_w);
-    st.active = uniform(st.active);
-    st.k_lo = uniform(st.k_lo);
-    st.seg_kc = uniform(st.seg_kc);
-    st.seg_rb = uniform(st.seg_rb);
-}
-
-__device__ __forceinline__ void set_op(const SeqPlan *P, Walk &st, int op) {
-    const SeqOp o = cload(P->ops, op);
-    st.op = op;
-    st.op_rb0 = o.rb_base;
-    st.op_end = o.rb_base + o.n_rb;
-    st.op_w = o.packed;
-}
-
-// Position the issue cursor on tile st.it of phase st.ip (one division per
-// range; afterwards the cursor advances by increments only).
-__device__ __forceinline__ void seek(const SeqPlan *P, Walk &st) {
-    const SeqPhase ph = cload(P->phases, st.ip);
-    st.R = ph.R;
-    st.G = ph.G;
-    st.nkc = ph.nkc;
-    st.op_first = ph.op_first;
-    const Pos p = decode(ph, st.it);
-    st.kc = p.kc;
-    st.rb = p.rb;
-    st.gi = p.gi;
-    st.len = chunk_len(ph, p.kc);
-    set_op(P, st, op_of_rb(P, ph, p.rb));
-}
 
 template <int BITS>
-__device__ __forceinline__ void issue(const SeqPlan *P, int n_phases, int w, int lane, Walk &st, Slot<BITS> &r) {
-    using L = Layout<BITS>;
-    if (st.it >= st.iend && st.ip < n_phases) {
-        do {
-            ++st.ip;
-            if (st.ip < n_phases) {
-                const SeqPhase ph = cload(P->phases, st.ip);
-                if (w < ph.W) {
-                    st.it = cload(ph.wave_start, w);
-                    st.iend = cload(ph.wave_start, w + 1);
-                }
-            }
-        } while (st.it >= st.iend && st.ip < n_phases);
-        if (st.ip < n_phases) seek(P, st);
-    }
-    const uint8_t *src = P->dummy;
-    if (st.ip < n_phases) {
-        r.phase = st.ip;
-        r.kc = st.kc;
-        r.rb = st.rb;
-        r.g = st.kc * kChunkGroups + st.gi;
-        src = st.op_w + ((int64_t)(st.rb - st.op_rb0) * st.G + r.g) * L::kTileBytes;
-        // advance: group within chunk, then row block, then chunk
-        ++st.it;
-        if (++st.gi == st.len) {
-            st.gi = 0;
-            if (++st.rb == st.R) {
-                st.rb = 0;
-                ++st.kc;
-                st.len = st.kc < st.nkc - 1 ? kChunkGroups : st.G - kChunkGroups * (st.nkc - 1);
-                if (st.it < st.iend) set_op(P, st, st.op_first);
-            } else if (st.rb == st.op_end) {
-                set_op(P, st, st.op + 1);
-            }
+__device__ __forceinline__ void issue(Issue &is, const uint8_t *dummy, int lane, Slot<BITS> &s) {
+    uint32_t hdr = 0;
+    if (is.left == 0) {
+        if (is.next < is.count) {
+            const SeqRun r = cload(is.runs, is.next);
+            ++is.next;
+            is.src = r.src;
+            is.left = (int)r.n;
+            hdr = r.hdr;
+        } else {                       // past the end: keep the ring's load count fixed
+            is.src = dummy;
+            is.left = 1;
         }
-    } else {
-        r.phase = -1;
-        r.kc = r.rb = r.g = 0;
     }
-    r.phase = uniform(r.phase);
-    r.kc = uniform(r.kc);
-    r.rb = uniform(r.rb);
-    r.g = uniform(r.g);
-    uniformize(st);
-    load_tile<BITS>(uniform_ptr(src), lane, r.w, r.sc);
+    s.hdr = hdr;
+    load_tile<BITS>(is.src, lane, s.w, s.sc);
+    is.src += Layout<BITS>::kTileBytes;
+    --is.left;
 }
 
-// Close the open segment: park its partial in this wave's LDS slot; the
-// workgroup merges the slots when it leaves the phase.
+// Park the open run's partial (segment sums of 4 rows x M per lane, reduced
+// over the wave's k slices) in its LDS slot; lane l holds row l.
 template <int M>
-__device__ __forceinline__ void close_segment(const SeqPlan *P, int w, int lane, Walk &st, float (&facc)[4][M],
-                                              float *lp) {
-    if (st.seg_kc < 0) return;
-    const SeqPhase ph = cload(P->phases, st.active);
-    const int slot = segment(ph, st.seg_kc, st.seg_rb) - first_segment(ph, w);
-    float *dst = lp + (((w % kSeqWaves) * P->slots + slot) * M) * 64 + lane;
+__device__ __forceinline__ void close_segment(int slot, float (&facc)[4][M], float *lp_w, int lane) {
+    if (slot < 0) return;
+    float *dst = lp_w + slot * M * 64;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         float f[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) f[i] = slice_sum(facc[i][m]);
-        dst[m * 64] = to_row_layout(f, lane);   // lane l holds row l
+        dst[m * 64] = to_row_layout(f, lane);
     }
-    st.seg_kc = -1;
 }
 
 // Workgroup-wide exit from phase p: merge the waves' LDS partials of every
@@ -617,22 +532,26 @@ __device__ __noinline__ void leave_phase(const SeqPlan *P, int p, uint32_t gen, 
     for (int i = j; i < fn; i += kSeqWaves) finalize_rb<BITS, M>(P, gen, p, f0 + i, s_act);
 }
 
+struct Compute {
+    int active;   // phase whose prologue ran last
+    int slot;     // LDS slot of the open run's segment; -1: none
+    int q;        // LDS byte offset of the next tile's activation group
+};
+
 template <int BITS, int M>
-__device__ __forceinline__ void compute(const SeqPlan *P, uint32_t gen, int w, int wg, int lane, Walk &st,
-                                        float (&facc)[4][M], const Slot<BITS> &r, int8_t *q_lds,
-                                        float (*s_sh)[4], float (*r_sh)[4]) {
-    if (r.phase < 0) return;
-    float *lp = reinterpret_cast<float *>(q_lds + M * P->q_stride);
-    while (st.active < r.phase) {
-        close_segment<M>(P, w, lane, st, facc, lp);
-        if (st.active >= 0) leave_phase<BITS, M>(P, st.active, gen, wg, lp, s_sh[st.active & 1]);
-        ++st.active;
-        st.k_lo = enter_phase<M>(P, st.active, gen, wg, q_lds, s_sh, r_sh);
-    }
-    if (r.kc != st.seg_kc || r.rb != st.seg_rb) {
-        close_segment<M>(P, w, lane, st, facc, lp);
-        st.seg_kc = r.kc;
-        st.seg_rb = r.rb;
+__device__ __forceinline__ void compute(const SeqPlan *P, uint32_t gen, int wg, int lane, Compute &c,
+                                        float (&facc)[4][M], const Slot<BITS> &s, int8_t *q_lds, int qs,
+                                        float *lp, float *lp_w, float (*s_sh)[4], float (*r_sh)[4]) {
+    if (s.hdr != 0) {   // the tile opens a run: close the previous segment, meet the run's phase
+        close_segment<M>(c.slot, facc, lp_w, lane);
+        const int phase = (int)(s.hdr & ((1u << kRunPhaseBits) - 1));
+        while (c.active < phase) {
+            if (c.active >= 0) leave_phase<BITS, M>(P, c.active, gen, wg, lp, s_sh[c.active & 1]);
+            ++c.active;
+            enter_phase<M>(P, c.active, gen, wg, q_lds, s_sh, r_sh);
+        }
+        c.slot = (int)((s.hdr >> kRunPhaseBits) & ((1u << kRunSlotBits) - 1));
+        c.q = (int)((s.hdr >> (kRunPhaseBits + kRunSlotBits)) & ((1u << kRunGroupBits) - 1)) * kGroup;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -643,16 +562,15 @@ __device__ __forceinline__ void compute(const SeqPlan *P, uint32_t gen, int w, i
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[i][m] = 0;
-    const int8_t *qg = q_lds + (r.g * kGroup - st.k_lo) + (lane >> 4) * 32;
-    const int qs = P->q_stride;
-    dot_tile<BITS, M>(r.w, [&](int m, int d) { return reinterpret_cast<const int *>(qg + m * qs)[d]; }, acc);
+    const int8_t *qg = q_lds + c.q + (lane >> 4) * 32;
+    dot_tile<BITS, M>(s.w, [&](int m, int d) { return reinterpret_cast<const int *>(qg + m * qs)[d]; }, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float S = row_scale(r.sc, i);
+        const float S = row_scale(s.sc, i);
 #pragma unroll
         for (int m = 0; m < M; ++m) facc[i][m] = fmaf((float)acc[i][m], S, facc[i][m]);
     }
-    uniformize(st);
+    c.q += kGroup;
 }
 
 template <int BITS, int M>
@@ -661,51 +579,63 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const SeqPlan *__restr
     extern __shared__ __align__(16) int8_t q_lds[];
     __shared__ float s_sh[2][4];
     __shared__ float r_sh[2][4];
-    if (P->magic != kPlanMagic) {          // workspace does not hold a prepared plan
+    if (cload(&P->magic) != kPlanMagic) {   // workspace does not hold a prepared plan
         if (threadIdx.x == 0 && blockIdx.x == 0) store_shared(err, 2u);
         return;
     }
     const int lane = threadIdx.x & 63;
+    const int wi = uniform(threadIdx.x >> 6);
     const int wg = blockIdx.x;
-    const int w = wg * kSeqWaves + uniform(threadIdx.x >> 6);
+    const int w = wg * kSeqWaves + wi;
+    const int n_phases = cload(&P->n_phases);
+    const int qs = cload(&P->q_stride);
+    const int slots = cload(&P->slots);
+    const uint8_t *dummy = cload(&P->dummy);
 
     external_stats<M>(P, w, lane, gen);
 
-    const int n_phases = P->n_phases;
-    Walk st;
-    st.ip = -1;
-    st.it = st.iend = 0;
-    st.kc = st.rb = st.gi = st.len = st.op = st.op_end = st.op_rb0 = 0;
-    st.R = st.G = st.nkc = st.op_first = 0;
-    st.op_w = P->dummy;
-    st.active = -1;
-    st.k_lo = 0;
-    st.seg_kc = -1;
-    st.seg_rb = 0;
+    const SeqWave wv = cload(cload(&P->wtab), w);
+    Issue is;
+    is.runs = cload(&P->runs) + wv.run_begin;
+    is.next = 0;
+    is.count = wv.run_count;
+    is.left = 0;
+    is.src = dummy;
+    float *lp = reinterpret_cast<float *>(q_lds + M * qs);
+    float *lp_w = lp + (wi * slots * M) * 64 + lane;
+    Compute c;
+    c.active = -1;
+    c.slot = -1;
+    c.q = 0;
     float facc[4][M];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int m = 0; m < M; ++m) facc[i][m] = 0.0f;
-    Slot<BITS> ring[kRing];
+
+    constexpr int D = ring_depth<BITS, M>();
+    Slot<BITS> ring[D];
 #pragma unroll
-    for (int i = 0; i < kRing; ++i) issue<BITS>(P, n_phases, w, lane, st, ring[i]);
-    while (ring[0].phase >= 0) {
+    for (int i = 0; i < D; ++i) issue<BITS>(is, dummy, lane, ring[i]);
+    int left = wv.tiles;
+    while (left > 0) {
 #pragma unroll
-        for (int i = 0; i < kRing; ++i) {
-            compute<BITS, M>(P, gen, w, wg, lane, st, facc, ring[i], q_lds, s_sh, r_sh);
-            issue<BITS>(P, n_phases, w, lane, st, ring[i]);
+        for (int i = 0; i < D; ++i) {
+            if (left > 0) {
+                compute<BITS, M>(P, gen, wg, lane, c, facc, ring[i], q_lds, qs, lp, lp_w, s_sh, r_sh);
+                --left;
+            }
+            issue<BITS>(is, dummy, lane, ring[i]);
         }
     }
     // close the last segment and meet every remaining workgroup-wide prologue
-    float *lp = reinterpret_cast<float *>(q_lds + M * P->q_stride);
-    close_segment<M>(P, w, lane, st, facc, lp);
-    while (st.active < P->n_phases - 1) {
-        if (st.active >= 0) leave_phase<BITS, M>(P, st.active, gen, wg, lp, s_sh[st.active & 1]);
-        ++st.active;
-        st.k_lo = enter_phase<M>(P, st.active, gen, wg, q_lds, s_sh, r_sh);
+    close_segment<M>(c.slot, facc, lp_w, lane);
+    while (c.active < n_phases - 1) {
+        if (c.active >= 0) leave_phase<BITS, M>(P, c.active, gen, wg, lp, s_sh[c.active & 1]);
+        ++c.active;
+        enter_phase<M>(P, c.active, gen, wg, q_lds, s_sh, r_sh);
     }
-    leave_phase<BITS, M>(P, st.active, gen, wg, lp, s_sh[st.active & 1]);
+    leave_phase<BITS, M>(P, c.active, gen, wg, lp, s_sh[c.active & 1]);
 }
 
 }  // namespace

@@ -169,6 +169,48 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
                 parts = std::max(parts, g.owner(t1) / kSeqWaves - g.owner(t0) / kSeqWaves + 1);
             }
     }
+    // ---- per-wave run lists: each wave's tile range of each phase, cut at
+    // segment boundaries (a run's tiles are consecutive groups of one row
+    // block, so they are contiguous in the packed matrix)
+    const int64_t tile_bytes = bits == 4 ? Layout<4>::kTileBytes : Layout<6>::kTileBytes;
+    std::vector<std::vector<SeqRun>> wruns(waves);
+    std::vector<int> wtiles(waves, 0);
+    for (int p = 0; p < n_ph; ++p) {
+        const PhaseGeom &g = geo[p];
+        for (int w = 0; w < g.W; ++w) {
+            const int t0 = g.start(w), t1 = g.start(w + 1);
+            if (t1 <= t0) continue;
+            int kcw, rbw;
+            g.decode(g.start(w / kSeqWaves * kSeqWaves), kcw, rbw);
+            const int wg_g0 = kcw * kChunkGroups;          // first group the workgroup quantises
+            const int seg0 = g.segment(t0);
+            for (int t = t0; t < t1;) {
+                int kc, rb;
+                g.decode(t, kc, rb);
+                const int len = g.chunk_len(kc);
+                const int gi = t - kc * g.R * kChunkGroups - rb * len;
+                const int n = std::min(len - gi, t1 - t);
+                const int g0 = kc * kChunkGroups + gi;
+                const int slot = kc * g.R + rb - seg0;
+                const int gl = g0 - wg_g0;
+                if (slot >= (1 << kRunSlotBits) || gl >= (1 << kRunGroupBits)) return MBQ_ERR_SHAPE;
+                int op = ph[p].first;
+                while (op + 1 < ph[p].first + ph[p].count && rb >= rb_base[p][op + 1 - ph[p].first]) ++op;
+                SeqRun r;
+                r.src = reinterpret_cast<const uint8_t *>(ops[op].packed) +
+                        ((int64_t)(rb - rb_base[p][op - ph[p].first]) * g.G + g0) * tile_bytes;
+                r.hdr = kRunStart | (uint32_t)p | ((uint32_t)slot << kRunPhaseBits) |
+                        ((uint32_t)gl << (kRunPhaseBits + kRunSlotBits));
+                r.n = (uint32_t)n;
+                wruns[w].push_back(r);
+                wtiles[w] += n;
+                t += n;
+            }
+        }
+    }
+    int64_t n_runs = 0;
+    for (int w = 0; w < waves; ++w) n_runs += (int64_t)wruns[w].size();
+
     const int q_stride = (int)up(q_span, 16);
     const int64_t lds = M * q_stride + (int64_t)kSeqWaves * slots * M * 64 * 4;
     if (lds > 150 * 1024) return MBQ_ERR_SHAPE;
@@ -183,9 +225,11 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     const int64_t off_ext = up(off_plan + (int64_t)sizeof(SeqPlan), 64);
     const int64_t off_phases = up(off_ext + (int64_t)ext.size() * sizeof(SeqExt), 64);
     const int64_t off_ops = up(off_phases + (int64_t)n_ph * sizeof(SeqPhase), 64);
+    const int64_t off_wtab = up(off_ops + (int64_t)n_ops * sizeof(SeqOp), 64);
+    const int64_t off_runs = up(off_wtab + (int64_t)waves * sizeof(SeqWave), 64);
     // per-phase tables: wave_start, wave_seg0, seg_owner, wg_k (int32)
     std::vector<int64_t> off_tab(n_ph);
-    int64_t tab = up(off_ops + (int64_t)n_ops * sizeof(SeqOp), 64);
+    int64_t tab = up(off_runs + n_runs * (int64_t)sizeof(SeqRun), 64);
     for (int p = 0; p < n_ph; ++p) {
         off_tab[p] = tab;
         const int64_t ints = (geo[p].W + 1) + geo[p].W + 4LL * geo[p].nkc * geo[p].R + 6LL * grid;
@@ -222,7 +266,24 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     plan.stats = dev(off_stats);
     plan.partials = reinterpret_cast<uint64_t *>(dev(off_part));
     plan.dummy = dev(off_dummy);
+    plan.runs = reinterpret_cast<const SeqRun *>(dev(off_runs));
+    plan.wtab = reinterpret_cast<const SeqWave *>(dev(off_wtab));
     memcpy(blob, &plan, sizeof(plan));
+    {
+        int64_t r0 = 0;
+        for (int w = 0; w < waves; ++w) {
+            SeqWave sw;
+            sw.run_begin = (int32_t)r0;
+            sw.run_count = (int32_t)wruns[w].size();
+            sw.tiles = wtiles[w];
+            sw.pad = 0;
+            memcpy(blob + (off_wtab - off_plan) + w * sizeof(SeqWave), &sw, sizeof(sw));
+            if (!wruns[w].empty())
+                memcpy(blob + (off_runs - off_plan) + r0 * sizeof(SeqRun), wruns[w].data(),
+                       wruns[w].size() * sizeof(SeqRun));
+            r0 += (int64_t)wruns[w].size();
+        }
+    }
     for (size_t j = 0; j < ext.size(); ++j) {
         SeqExt e;
         memset(&e, 0, sizeof(e));

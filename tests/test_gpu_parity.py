@@ -87,11 +87,19 @@ def test_pack_pads_rows_with_zeros(bits):
     packed = host(packed_on_device(bits, canon, S, N, K))
     tile = 4224 if bits == 4 else 6272
     G = K // 128
-    # row block 1 holds rows 64..127; lanes 6..63 are padding
+    # row block 1 holds rows 64..127; its local rows 6..63 are padding.  Lane l
+    # of slab j holds local row 4*(l % 16) + j (W4), or in dword c of the
+    # lane's 16 bytes, triple q = (4j + c) // 3, row 4*(l % 16) + q // 2 (W6).
+    lanes = np.arange(64)
     for g in range(G):
         t = packed[(1 * G + g) * tile:(1 * G + g + 1) * tile]
-        slabs = t[:tile - 128].reshape(-1, 64, 16)
-        assert not slabs[:, 6:, :].any()
+        slabs = t[:tile - 128].reshape(-1, 64, 4, 4)      # [slab][lane][dword][byte]
+        for j in range(slabs.shape[0]):
+            for c in range(4):
+                row = 4 * (lanes % 16) + (j if bits == 4 else ((4 * j + c) // 3) // 2)
+                pad = row >= 6
+                assert not slabs[j, pad, c, :].any()
+                assert slabs[j, ~pad, c, :].any()
         assert not t[tile - 128:].reshape(64, 2)[6:].any()
 
 
