@@ -77,18 +77,19 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void linear_kernel(
         for (int j = 0; j < L::kSlabs; ++j) wc[j] = wn[j];
         sc = sn;
     }
-    // lane l takes row l: sum the four k slices, then redistribute
+    // sum the four k slices: lane l ends with row r = slice_row(l)
     float frow[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         float f[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = slice_sum(facc[i][m]);
-        frow[m] = to_row_layout(f, lane);
+        for (int i = 0; i < 4; ++i) f[i] = facc[i][m];
+        frow[m] = slice_reduce(f);
     }
 
     const float unscale = 1.0f / (float)(1 << L::kAccShift);   // exact power of two
-    const int n = rb * 64 + lane;
+    const int r = slice_row(lane);
+    const int n = rb * 64 + r;
     if (splits == 1) {
         if (n < N) {
 #pragma unroll
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void linear_kernel(
     }
     float *part = partials + ((int64_t)item * M) * 64;
 #pragma unroll
-    for (int m = 0; m < M; ++m) store_shared(part + m * 64 + lane, frow[m]);
+    for (int m = 0; m < M; ++m) store_shared(part + m * 64 + r, frow[m]);
     wait_memory();
     unsigned prev = 0;
     if (lane == 0) prev = counter_add(&counters[rb], 1u);
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void linear_kernel(
         for (int u = 0; u < 8; ++u)
 #pragma unroll
             for (int m = 0; m < M; ++m)
-                v[u][m] = p0 + u < splits ? load_shared(rbp + ((p0 + u) * M + m) * 64 + lane) : 0.0f;
+                v[u][m] = p0 + u < splits ? load_shared(rbp + ((p0 + u) * M + m) * 64 + r) : 0.0f;
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
@@ -152,13 +153,13 @@ __global__ __launch_bounds__(64) void group_acc_kernel(const uint8_t *__restrict
     const int *qg = reinterpret_cast<const int *>(q) + g * 32 + (lane >> 4) * 8;
     const int kdw = K >> 2;
     dot_tile<BITS, M>(w, [&](int m, int d) { return qg[m * kdw + d]; }, acc);
-    const int n = rb * 64 + lane;
+    const int n = rb * 64 + slice_row(lane);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         int f[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = slice_sum(acc[i][m]);
-        const int v = to_row_layout(f, lane);
+        for (int i = 0; i < 4; ++i) f[i] = acc[i][m];
+        const int v = slice_reduce(f);
         if (n < N) acc_out[((int64_t)m * N + n) * G + g] = v >> L::kAccShift;
     }
 }

@@ -217,6 +217,23 @@ __device__ __forceinline__ void load_tile(const uint8_t *tile, int lane, v4i (&w
         gptr(reinterpret_cast<const v2u *>(tile + Layout<BITS>::kWeightBytes) + (lane & 15)));
 }
 
+// The same through a buffer resource: with real == false the resource has no
+// bytes, so every load returns zeros without touching memory (a placeholder
+// that keeps a fixed count of outstanding loads).  Slabs 4 and 5 (W6) reach
+// past the 12-bit instruction offset through the scalar offset.
+template <int BITS>
+__device__ __forceinline__ void load_tile_buf(const uint8_t *tile, bool real, int lane,
+                                              v4i (&w)[Layout<BITS>::kSlabs], v2u &scales) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(tile), 0, real ? Layout<BITS>::kTileBytes : 0, 0x00020000);
+    constexpr int kNt = 2;   // non-temporal: the weights are read once
+#pragma unroll
+    for (int j = 0; j < Layout<BITS>::kSlabs; ++j)
+        w[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16 + (j & 3) * kSlab,
+                                                                              (j >> 2) * 4 * kSlab, kNt));
+    scales = __builtin_amdgcn_raw_buffer_load_b64(r, Layout<BITS>::kWeightBytes + (lane & 15) * 8, 0, kNt);
+}
+
 // fp32 scale of row i (0..3) of the lane from its packed scales.
 __device__ __forceinline__ float row_scale(v2u s, int i) {
     const uint32_t word = i < 2 ? s.x : s.y;
@@ -225,28 +242,88 @@ __device__ __forceinline__ float row_scale(v2u s, int i) {
 
 // Sum a per-lane value over the four k slices (lanes l, l^16, l^32, l^48) in a
 // fixed order; every lane of the group gets the same total.
-__device__ __forceinline__ float slice_sum(float v) {
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
+// ------------------------------------------------------------------ cross-lane reductions
+//
+// DPP moves and gfx950's lane-swap instructions run on the vector ALU; the
+// generic shuffles go through the LDS crossbar and cost a round trip each.
+
+// dst = src of the lane picked by the DPP control; lanes of rows outside
+// ROW_MASK (and lanes with no source) read 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __uint_as_float(dpp_u32<CTRL, ROW_MASK>(__float_as_uint(v)));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint64_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)b), hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(b >> 32));
+    return __longlong_as_double((long long)(lo | (hi << 32)));
+}
+constexpr int kDppQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;    // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppHalfMirror = 0x141;  // lane 7 - i within 8
+constexpr int kDppMirror = 0x140;      // lane 15 - i within 16
+constexpr int kDppBcast15 = 0x142;     // lane 15 of a row into the next row
+constexpr int kDppBcast31 = 0x143;     // lane 31 into rows 2 and 3
+
+// Sum (or max of non-negative values) over the wave, in a fixed tree order;
+// the result is valid in lane 63.
+template <int CTRL, int ROW_MASK = 0xF, typename T>
+__device__ __forceinline__ T dpp_any(T v) {
+    if constexpr (sizeof(T) == 8) return dpp_f64<CTRL, ROW_MASK>(v);
+    else return dpp_f32<CTRL, ROW_MASK>(v);
+}
+template <typename T>
+__device__ __forceinline__ T wave_sum63(T v) {
+    v += dpp_any<kDppQuadSwap1>(v);
+    v += dpp_any<kDppQuadSwap2>(v);
+    v += dpp_any<kDppHalfMirror>(v);
+    v += dpp_any<kDppMirror>(v);
+    v += dpp_any<kDppBcast15, 0xA>(v);
+    v += dpp_any<kDppBcast31, 0xC>(v);
     return v;
 }
-__device__ __forceinline__ int slice_sum(int v) {
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
+__device__ __forceinline__ float wave_max63(float v) {   // v >= 0
+    v = fmaxf(v, dpp_f32<kDppQuadSwap1>(v));
+    v = fmaxf(v, dpp_f32<kDppQuadSwap2>(v));
+    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppBcast15, 0xA>(v));
+    v = fmaxf(v, dpp_f32<kDppBcast31, 0xC>(v));
     return v;
 }
 
-// After slice_sum, row 4r + i of the tile sits in register i of lane r.  Move
-// it so that lane l holds row l.
+// Pairwise reduce-scatter across the two halves (lanes l, l ^ 32) or across
+// row pairs (l, l ^ 16): the lower (even) lanes return a + its partner's a,
+// the upper (odd) lanes b + its partner's b.
+__device__ __forceinline__ uint32_t bits_of(float v) { return __float_as_uint(v); }
+__device__ __forceinline__ uint32_t bits_of(int v) { return (uint32_t)v; }
+__device__ __forceinline__ float from_bits(uint32_t b, float) { return __uint_as_float(b); }
+__device__ __forceinline__ int from_bits(uint32_t b, int) { return (int)b; }
 template <typename T>
-__device__ __forceinline__ T to_row_layout(const T (&f)[4], int lane) {
-    T r = f[0];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const T t = __shfl(f[i], lane >> 2, 64);
-        if ((lane & 3) == i) r = t;
-    }
-    return r;
+__device__ __forceinline__ T swap32_sum(T a, T b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(bits_of(a), bits_of(b), false, false);
+    return from_bits(r[0], T()) + from_bits(r[1], T());
 }
+template <typename T>
+__device__ __forceinline__ T swap16_sum(T a, T b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(bits_of(a), bits_of(b), false, false);
+    return from_bits(r[0], T()) + from_bits(r[1], T());
+}
+
+// Sum a tile's per-lane row partials f[i] (row 4*(l % 16) + i of lane l, one
+// k slice s = l / 16 per lane) over the four k slices.  Lane l returns the
+// total of row slice_row(l) = 4*(l % 16) + l / 16.
+template <typename T>
+__device__ __forceinline__ T slice_reduce(const T (&f)[4]) {
+    const T g0 = swap32_sum(f[0], f[2]);   // lanes 0-31: row 0, lanes 32-63: row 2
+    const T g1 = swap32_sum(f[1], f[3]);   // rows 1 / 3
+    return swap16_sum(g0, g1);             // even 16-lane rows keep g0, odd keep g1
+}
+__device__ __forceinline__ int slice_row(int lane) { return 4 * (lane & 15) + (lane >> 4); }
 
 }  // namespace mbq

@@ -9,10 +9,17 @@ namespace mbq {
 
 constexpr int kSeqWaves = 4;                   // waves per workgroup
 constexpr int kSeqThreads = 64 * kSeqWaves;
+
+// Workgroup roles.  Finalising workgroups gather the partials of row blocks
+// and publish their outputs; the others, once their partials are out, start
+// loading the next phase's weights at once, which keeps the memory busy while
+// the finalisers (whose memory queues are then empty) run the phase hand-over.
+__host__ __device__ inline bool is_final_wg(int wg, int grid) { return grid == 1 || (wg & 1) != 0; }
 constexpr int kChunkGroups = 8;                // k groups per k chunk (1024 k)
 constexpr int kStatRecBytes = 128;             // one per (producer op, row block)
-constexpr int kMaxPhases = 1000;             // < 2^kRunPhaseBits
-constexpr uint64_t kPlanMagic = 0x6d62712d73657131ull;  // "mbq-seq1"
+constexpr int kMaxPhases = 1000;               // < 2^kRunPhaseBits
+constexpr int kMetaMaxBytes = 4096;           // phase record + workgroup block, per LDS slot
+constexpr uint64_t kPlanMagic = 0x6d62712d73657132ull;  // "mbq-seq2"
 
 // Every value that one wave hands to another travels in a 64-bit word whose
 // high half is the epoch tag of the phase that wrote it, so a single load
@@ -21,39 +28,21 @@ constexpr uint64_t kPlanMagic = 0x6d62712d73657131ull;  // "mbq-seq1"
 // Stats record of one row block of an op's output (rows n < stats_cols), for
 // activation row m: word 3m = max|y| bits, 3m+1 / 3m+2 = low / high half of
 // the fp64 sum of y^2; each word's high half is the tag.
-struct SeqOp {
-    const uint8_t *packed;
-    uint32_t *out;           // bf16 pairs; row m starts at word m * N / 2
-    uint64_t *xt;            // tagged copy of out for the consumer: bf16 pair | tag << 32
-    int32_t N;
-    int32_t n_rb;            // row blocks of this op
-    int32_t rb_base;         // first phase-level row block of this op
-    int32_t stats_cols;      // rows n < stats_cols feed the stats records (0: none)
-    int64_t stats_rec;       // index of this op's first stats record
-};
 
-struct SeqPhase {
+struct SeqPhase {            // 64 bytes
     const uint32_t *in;      // bf16 pairs of the input rows (inputs written before the launch)
     const uint64_t *in_xt;   // tagged copy written by the producer op, or null
     int32_t in_stride2;      // input row stride in 32-bit words (and in tagged words)
-    int32_t K, G, nkc, prologue;
-    int32_t op_first, op_count;
-    int32_t R;               // row blocks over all ops of the phase
-    int32_t W;               // waves with work (min(total waves, T))
-    int32_t T;               // tiles, ordered (k chunk, row block, group)
+    int32_t K, prologue;
     int32_t in_nrec;         // stats records describing the input: ceil(K / 64)
-    int32_t in_phase;        // phase that writes them (-1: computed at kernel start)
     int64_t in_rec;          // first of them
-    // Host-computed tables (integer division is slow on the GPU):
-    const int32_t *wave_start;   // [W + 1]: first tile of each wave's range
-    const int32_t *wave_seg0;    // [W]: segment (k chunk * R + row block) of that first tile
-    const int32_t *seg_owner;    // [nkc * R][2]: waves owning the segment's first and last tile
-    const int32_t *wg_k;         // [workgroups][2]: columns [k_lo, k_hi) a workgroup quantises
-    const int32_t *wg_seg;       // [workgroups][2]: first and last segment the workgroup's tiles touch
-                                 // (last < first: none)
-    const int32_t *seg_wg;       // [nkc * R][2]: workgroups owning the segment's first and last tile
-    const int32_t *wg_fin;       // [workgroups][2]: first row block and count of row blocks whose
-                                 // last tile the workgroup owns (it finalises them)
+    int32_t in_phase;        // phase that writes them (-1: computed at kernel start)
+    // The partial area is shared by phases of equal parity: before storing
+    // partials, wait until the phase two back has finalised all wait_n of its
+    // row blocks (*wait_count counts them).
+    int32_t wait_n;
+    const uint32_t *wait_count;
+    uint32_t *fin_count;     // this phase's count of finalised row blocks
 };
 
 // One run of a wave's walk: consecutive tiles of one segment (k chunk x row
@@ -73,6 +62,28 @@ struct SeqWave {             // one wave's slice of the run table
     int32_t run_begin, run_count, tiles, pad;
 };
 
+// Per (phase, workgroup) block: everything the workgroup needs to enter and
+// leave the phase, prefetched into LDS one phase ahead.
+struct SeqWgHead {
+    int32_t k_lo, k_hi;      // input columns the workgroup quantises ([k_lo, k_hi), may be empty)
+    int32_t n_seg, n_fin;    // entries below
+    int32_t tiles[kSeqWaves];   // tiles of each of its waves in this phase
+};
+struct SeqWgSeg {            // a segment the workgroup's tiles touch
+    int32_t cidx;            // its contribution (partial slot) in the phase's partial area
+    uint8_t slot[kSeqWaves]; // each wave's LDS slot holding a part of it (0xFF: none)
+};
+struct SeqFin {              // a row block the workgroup finalises (48 bytes)
+    uint32_t *out;           // its first bf16 pair in output row 0
+    uint64_t *xt;            // same in the tagged copy, or null
+    uint64_t *stats;         // its stats record, or null
+    int32_t row_words;       // output row stride in pairs (N / 2)
+    int32_t rows;            // valid rows (<= 64, even)
+    int32_t stat_rows;       // rows feeding the stats (0 .. rows)
+    int32_t c0, nc;          // its contributions, summed in this order
+    int32_t pad;
+};
+
 struct SeqExt {              // an input no op of the walk writes: stats at kernel start
     const uint32_t *in;
     int32_t in_stride2, K;
@@ -82,20 +93,25 @@ struct SeqExt {              // an input no op of the walk writes: stats at kern
 
 struct SeqPlan {
     uint64_t magic;
-    int32_t n_phases, n_ops, n_ext, n_ext_rb;
-    int32_t waves;           // total waves of the launch
+    int32_t n_phases, n_ext, n_ext_rb;
+    int32_t waves;           // waves of the launch
+    int32_t grid;            // workgroups
     int32_t slots;           // LDS partial slots per wave (segments one wave's range touches)
     int32_t q_stride;        // LDS bytes per activation row
-    int32_t parts;           // memory partial slots per segment (workgroups touching one segment)
-    const SeqOp *ops;
+    int32_t blk_bytes;       // bytes of one (phase, workgroup) block
+    int32_t seg_cap;         // SeqWgSeg entries per block
+    int32_t part_stride;     // contributions per parity half of the partial area
     const SeqPhase *phases;
     const SeqExt *ext;
     uint32_t *err;           // nonzero after a wait gave up
     uint8_t *stats;          // stats records
-    uint64_t *partials;      // [segment][part][m][lane]: value bits | tag << 32
+    uint64_t *partials;      // [phase & 1][contribution][lane][m]: value bits | tag << 32
     const uint8_t *dummy;    // readable tile-sized area for loads past a stream's end
     const SeqRun *runs;      // every wave's runs, wave after wave, each in walk order
     const SeqWave *wtab;     // [waves]
+    const uint8_t *blocks;   // [phase][workgroup] blocks of blk_bytes
+    uint32_t *counters;      // [n_phases] finalised row blocks, then the exit count;
+                             // the last workgroup to exit clears them
 };
 
 }  // namespace mbq

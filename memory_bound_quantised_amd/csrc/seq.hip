@@ -40,10 +40,10 @@ __device__ __forceinline__ uint32_t make_tag(uint32_t gen, int phase) {
 __device__ __forceinline__ uint64_t tagged(uint32_t v, uint32_t tag) { return (uint64_t)v | ((uint64_t)tag << 32); }
 __device__ __forceinline__ uint32_t tag_of(uint64_t w) { return (uint32_t)(w >> 32); }
 
-// Plan data is read-only for the whole launch and always read at
-// wave-uniform addresses: reading it through the constant address space lets
-// the compiler use scalar loads, which keeps the vector-memory counter for the
-// weight stream alone (so waits on a tile never wait for plan reads).
+// Plan data is read-only for the whole launch.  Where it is read at
+// wave-uniform addresses it goes through the constant address space, so the
+// compiler uses scalar loads and the vector-memory counter stays with the
+// weight stream (waiting on a tile never waits on a plan read).
 #define MBQ_CONST __attribute__((address_space(4)))
 template <typename T>
 __device__ __forceinline__ T cload(const T *p, int64_t i = 0) {
@@ -56,39 +56,66 @@ __device__ __forceinline__ T cload(const T *p, int64_t i = 0) {
     return out;
 }
 
-// Waves split a phase's T tiles into ranges [T*w/W, T*(w+1)/W); the range
-// starts, first segments, segment owners and workgroup k ranges come from
-// host-computed tables.
+// Dynamic LDS: [activations: M rows x q_stride bytes][partial slots: waves x
+// slots x M x 64 floats][metadata slot 0][metadata slot 1].  A metadata slot
+// holds a phase record followed by the workgroup's block for that phase.
+extern __shared__ __align__(16) int8_t g_lds[];
 
-__device__ __forceinline__ int chunk_len(const SeqPhase &ph, int kc) {
-    return kc < ph.nkc - 1 ? kChunkGroups : ph.G - kChunkGroups * (ph.nkc - 1);
-}
-
-struct Pos {
-    int kc, rb, gi;   // k chunk, phase row block, group index inside the chunk
+struct Lay {
+    int qs;           // LDS bytes per activation row
+    int slots;        // LDS partial slots per wave
+    int meta_off;     // LDS offset of metadata slot 0
+    int meta_bytes;   // bytes per metadata slot
+    int seg_cap;      // segment entries per block
+    int blk_bytes;    // bytes per block
+    int grid;
+    int n_phases;
+    int part_stride;  // contributions per parity half of the partial area
 };
 
-__device__ __forceinline__ Pos decode(const SeqPhase &ph, int t) {
-    const int chunk_tiles = ph.R * kChunkGroups;
-    Pos p;
-    p.kc = t / chunk_tiles;
-    const int rem = t - p.kc * chunk_tiles;
-    const int len = chunk_len(ph, p.kc);
-    p.rb = rem / len;
-    p.gi = rem - p.rb * len;
-    return p;
+__device__ __forceinline__ float *lds_partials(const Lay &L, int M) { return reinterpret_cast<float *>(g_lds + M * L.qs); }
+__device__ __forceinline__ int8_t *lds_meta(const Lay &L, int p) { return g_lds + L.meta_off + (p & 1) * L.meta_bytes; }
+__device__ __forceinline__ const SeqPhase *meta_phase(const Lay &L, int p) {
+    return reinterpret_cast<const SeqPhase *>(lds_meta(L, p));
+}
+__device__ __forceinline__ const SeqWgHead *meta_head(const Lay &L, int p) {
+    return reinterpret_cast<const SeqWgHead *>(lds_meta(L, p) + sizeof(SeqPhase));
+}
+__device__ __forceinline__ const SeqWgSeg *meta_seg(const Lay &L, int p) {
+    return reinterpret_cast<const SeqWgSeg *>(lds_meta(L, p) + sizeof(SeqPhase) + sizeof(SeqWgHead));
+}
+__device__ __forceinline__ const SeqFin *meta_fin(const Lay &L, int p) {
+    return reinterpret_cast<const SeqFin *>(lds_meta(L, p) + sizeof(SeqPhase) + sizeof(SeqWgHead) +
+                                            L.seg_cap * sizeof(SeqWgSeg));
 }
 
-__device__ __forceinline__ int segment(const SeqPhase &ph, int kc, int rb) { return kc * ph.R + rb; }
-
-__device__ __forceinline__ int first_segment(const SeqPhase &ph, int w) { return cload(ph.wave_seg0, w); }
-__device__ __forceinline__ int seg_first_owner(const SeqPhase &ph, int seg) { return cload(ph.seg_owner, 2 * seg); }
-__device__ __forceinline__ int seg_last_owner(const SeqPhase &ph, int seg) { return cload(ph.seg_owner, 2 * seg + 1); }
-
-__device__ __forceinline__ int op_of_rb(const SeqPlan *P, const SeqPhase &ph, int rb) {
-    int j = ph.op_first;
-    while (j + 1 < ph.op_first + ph.op_count && rb >= cload(P->ops, j + 1).rb_base) ++j;
-    return j;
+// Metadata of phase p for this workgroup: every thread loads up to
+// kMetaIters dwords now and stores them into the LDS slot later, so the
+// loads overlap whatever the workgroup waits for in between.
+constexpr int kMetaIters = kMetaMaxBytes / 4 / kSeqThreads;
+__device__ __forceinline__ void fetch_meta(const SeqPlan *P, const Lay &L, int p, int wg,
+                                           uint32_t (&v)[kMetaIters]) {
+    if (p >= L.n_phases) return;
+    constexpr int kPhDw = (int)(sizeof(SeqPhase) / 4);
+    const int n_dw = kPhDw + L.blk_bytes / 4;
+    const uint32_t *ph = reinterpret_cast<const uint32_t *>(cload(&P->phases) + p);
+    const uint32_t *blk =
+        reinterpret_cast<const uint32_t *>(cload(&P->blocks) + ((int64_t)p * L.grid + wg) * L.blk_bytes);
+#pragma unroll
+    for (int it = 0; it < kMetaIters; ++it) {
+        const int i = (int)threadIdx.x + it * kSeqThreads;
+        if (i < n_dw) v[it] = i < kPhDw ? *gptr(ph + i) : *gptr(blk + (i - kPhDw));
+    }
+}
+__device__ __forceinline__ void store_meta(const Lay &L, int p, const uint32_t (&v)[kMetaIters]) {
+    if (p >= L.n_phases) return;
+    const int n_dw = (int)(sizeof(SeqPhase) / 4) + L.blk_bytes / 4;
+    uint32_t *dst = reinterpret_cast<uint32_t *>(lds_meta(L, p));
+#pragma unroll
+    for (int it = 0; it < kMetaIters; ++it) {
+        const int i = (int)threadIdx.x + it * kSeqThreads;
+        if (i < n_dw) dst[i] = v[it];
+    }
 }
 
 __device__ __forceinline__ bool gave_up(const SeqPlan *P, int64_t &spins) {
@@ -104,43 +131,14 @@ __device__ __forceinline__ bool gave_up(const SeqPlan *P, int64_t &spins) {
 // True if any lane of the wave passes true.
 __device__ __forceinline__ bool wave_any(bool b) { return __builtin_amdgcn_ballot_w64(b) != 0; }
 
-// Load a tagged word, re-polling until its tag is `want` (or the wait gives up).
-__device__ __forceinline__ uint64_t await_word(const SeqPlan *P, const uint64_t *p, uint64_t first, uint32_t want) {
-    uint64_t v = first;
-    int64_t spins = 0;
-    while (tag_of(v) != want) {
-        if (gave_up(P, spins)) break;
-        v = load_shared(p);
-    }
-    return v;
-}
-
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
-__device__ __forceinline__ uint64_t *stat_rec(const SeqPlan *P, int64_t r) {
-    return reinterpret_cast<uint64_t *>(P->stats + r * kStatRecBytes);
-}
-
 // Publish one stats record from per-lane values (lanes past the stats rows pass 0).
 template <int M>
-__device__ __forceinline__ void publish_stats(const SeqPlan *P, int64_t r, const float (&v)[M], uint32_t tag,
-                                              int lane) {
-    uint64_t *rec = stat_rec(P, r);
+__device__ __forceinline__ void publish_stats(uint64_t *rec, const float (&v)[M], uint32_t tag, int lane) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-        const double ss = wave_sum((double)v[m] * (double)v[m]);
-        const float am = wave_max(fabsf(v[m]));
-        if (lane == 0) {
+        const double ss = wave_sum63((double)v[m] * (double)v[m]);
+        const float am = wave_max63(fabsf(v[m]));
+        if (lane == 63) {
             const uint64_t bits = (uint64_t)__double_as_longlong(ss);
             store_shared(rec + 3 * m, tagged(__float_as_uint(am), tag));
             store_shared(rec + 3 * m + 1, tagged((uint32_t)bits, tag));
@@ -152,11 +150,14 @@ __device__ __forceinline__ void publish_stats(const SeqPlan *P, int64_t r, const
 // ---------------------------------------------------------------- kernel-start stats of external inputs
 
 template <int M>
-__device__ void external_stats(const SeqPlan *P, int w, int lane, uint32_t gen) {
-    for (int b = w; b < P->n_ext_rb; b += P->waves) {
+__device__ void external_stats(const SeqPlan *P, int w, int waves, int lane, uint32_t gen) {
+    const int n_ext_rb = cload(&P->n_ext_rb), n_ext = cload(&P->n_ext);
+    const SeqExt *ext = cload(&P->ext);
+    uint8_t *stats = cload(&P->stats);
+    for (int b = w; b < n_ext_rb; b += waves) {
         int e = 0;
-        while (e + 1 < P->n_ext && b >= cload(P->ext, e + 1).rb_first) ++e;
-        const SeqExt x = cload(P->ext, e);
+        while (e + 1 < n_ext && b >= cload(ext, e + 1).rb_first) ++e;
+        const SeqExt x = cload(ext, e);
         const int rb = b - x.rb_first;
         const int col = rb * 64 + lane;
         float v[M];
@@ -164,44 +165,58 @@ __device__ void external_stats(const SeqPlan *P, int w, int lane, uint32_t gen) 
         for (int m = 0; m < M; ++m) {
             v[m] = 0.0f;
             if (col < x.K) {
-                const uint32_t word = x.in[(int64_t)m * x.in_stride2 + (col >> 1)];
+                const uint32_t word = *gptr(x.in + (int64_t)m * x.in_stride2 + (col >> 1));
                 v[m] = bf16_bits_to_f32((word >> (16 * (col & 1))) & 0xFFFFu);
             }
         }
-        publish_stats<M>(P, x.rec + rb, v, make_tag(gen, -1), lane);
+        publish_stats<M>(reinterpret_cast<uint64_t *>(stats + (x.rec + rb) * kStatRecBytes), v, make_tag(gen, -1),
+                         lane);
     }
 }
 
 // ---------------------------------------------------------------- phase prologue (workgroup-wide)
 
-struct WgRange {
-    int k_lo, k_hi;   // columns this workgroup quantises; empty if k_hi == k_lo
-};
-
-__device__ __forceinline__ WgRange wg_range(const SeqPhase &ph, int wg) {
-    return WgRange{cload(ph.wg_k, 2 * wg), cload(ph.wg_k, 2 * wg + 1)};
-}
-
-constexpr int kStatBatch = 4;   // stats records per lane per round trip
+template <int M>
+constexpr int stat_batch() { return M < 3 ? 4 : 2; }   // stats records per lane per round trip
 constexpr int kXBatch = 4;      // input words (2 columns each) per thread per round trip
+
+// int8 code of t at scale s (rinv = 1 / s): rint(t / s) clamped to +-127.
+// The product t * rinv is within two ulps of the correctly rounded quotient,
+// so it rounds to the same integer unless it lies next to a half-integer;
+// only there (and when 1 / s overflows) is the quotient computed exactly.
+__device__ __forceinline__ float quant_code(float t, float s, float rinv, bool rinv_ok) {
+    float x = t * rinv;
+    const float fx = fabsf(x);
+    if (!rinv_ok || fabsf(fx - floorf(fx) - 0.5f) < 0x1p-14f) x = t / s;
+    return fminf(fmaxf(rintf(x), -127.0f), 127.0f);
+}
 
 // Quantise columns [k_lo, k_hi) of the phase input into LDS (int8, row stride
 // q_stride), after the optional weightless RMSNorm.  Row statistics come from
 // the producer's stats records, reduced in a fixed order so that every
-// workgroup derives bit-identical scales.  Returns k_lo.
+// workgroup derives bit-identical scales.  Wave 0 waits for the statistics
+// (and for the partial area of this phase's parity to be free; the scales
+// also serve the row blocks the workgroup finalises) while every
+// wave waits for its share of the input words; the next phase's metadata is
+// fetched meanwhile.
 template <int M>
-__device__ __noinline__ void enter_phase(const SeqPlan *P, int p, uint32_t gen, int wg, int8_t *q_lds,
-                                        float (*s_sh)[4], float (*r_sh)[4]) {
-    const SeqPhase ph = cload(P->phases, p);
-    const WgRange kr = wg_range(ph, wg);
+__device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int p, uint32_t gen, int wg,
+                                            float (*s_sh)[4], float (*r_sh)[4]) {
     const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    uint32_t pre[kMetaIters];
+    fetch_meta(P, L, p + 1, wg, pre);
+    const SeqPhase ph = *meta_phase(L, p);
+    const SeqWgHead h = *meta_head(L, p);
     const bool norm = ph.prologue == 1;
     const uint32_t want = make_tag(gen, ph.in_phase);
-    const int words = (kr.k_hi - kr.k_lo) >> 1;        // bf16 pairs per activation row
+    const int words = (h.k_hi - h.k_lo) >> 1;          // bf16 pairs per activation row
     const bool tagged_in = ph.in_xt != nullptr;
-    const bool has = kr.k_hi > kr.k_lo;
+    const bool has = h.k_hi > h.k_lo;
+    const bool need_scale = has || h.n_fin > 0;   // finalising rescales by the input scale
+    const uint64_t *xsrc = ph.in_xt + (h.k_lo >> 1);
 
-    // Issue the first batch of input loads now; they fly while wave 0 reduces the stats.
+    // first batch of input words: they fly while the statistics are awaited
     uint64_t xw[kXBatch][M];
 #pragma unroll
     for (int u = 0; u < kXBatch; ++u)
@@ -213,182 +228,173 @@ __device__ __noinline__ void enter_phase(const SeqPlan *P, int p, uint32_t gen, 
             const int j = threadIdx.x + u * kSeqThreads;
 #pragma unroll
             for (int m = 0; m < M; ++m)
-                if (j < words) xw[u][m] = load_shared(ph.in_xt + (int64_t)m * ph.in_stride2 + (kr.k_lo >> 1) + j);
+                if (j < words) xw[u][m] = load_shared(xsrc + (int64_t)m * ph.in_stride2 + j);
         }
     }
 
-    if (has && threadIdx.x < 64) {
-        double ss[M];
-        float am[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            ss[m] = 0.0;
-            am[m] = 0.0f;
-        }
-        for (int base = 0; base < ph.in_nrec; base += 64 * kStatBatch) {
-            uint64_t v[kStatBatch][3 * M];
-            const uint64_t *rp[kStatBatch];
-#pragma unroll
-            for (int u = 0; u < kStatBatch; ++u) {
-                const int i = base + lane + 64 * u;
-                rp[u] = stat_rec(P, ph.in_rec + (i < ph.in_nrec ? i : 0));
-#pragma unroll
-                for (int c = 0; c < 3 * M; ++c) v[u][c] = load_shared(rp[u] + c);
+    if (wave == 0) {
+        // the partial area of this phase's parity is free once the phase two back is finalised
+        if (ph.wait_n > 0) {
+            int64_t spins = 0;
+            while (load_shared(ph.wait_count) < (uint32_t)ph.wait_n && !gave_up(P, spins)) {
             }
+        }
+        if (need_scale) {
+            double ss[M];
+            float am[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                ss[m] = 0.0;
+                am[m] = 0.0f;
+            }
+            const uint8_t *stats = cload(&P->stats);
+            constexpr int kStatBatch = stat_batch<M>();
+            for (int base = 0; base < ph.in_nrec; base += 64 * kStatBatch) {
+                uint64_t v[kStatBatch][3 * M];
+                const uint64_t *rp[kStatBatch];
+#pragma unroll
+                for (int u = 0; u < kStatBatch; ++u) {
+                    const int i = base + lane + 64 * u;
+                    rp[u] = reinterpret_cast<const uint64_t *>(stats + (ph.in_rec + (i < ph.in_nrec ? i : 0)) *
+                                                                           kStatRecBytes);
+#pragma unroll
+                    for (int c = 0; c < 3 * M; ++c) v[u][c] = load_shared(rp[u] + c);
+                }
+                int64_t spins = 0;
+                for (;;) {
+                    bool stale = false;
+#pragma unroll
+                    for (int u = 0; u < kStatBatch; ++u)
+#pragma unroll
+                        for (int c = 0; c < 3 * M; ++c)
+                            stale |= base + lane + 64 * u < ph.in_nrec && tag_of(v[u][c]) != want;
+                    if (!wave_any(stale) || gave_up(P, spins)) break;
+#pragma unroll
+                    for (int u = 0; u < kStatBatch; ++u)
+#pragma unroll
+                        for (int c = 0; c < 3 * M; ++c)
+                            if (base + lane + 64 * u < ph.in_nrec && tag_of(v[u][c]) != want)
+                                v[u][c] = load_shared(rp[u] + c);
+                }
+#pragma unroll
+                for (int u = 0; u < kStatBatch; ++u) {
+                    if (base + lane + 64 * u < ph.in_nrec) {
+#pragma unroll
+                        for (int m = 0; m < M; ++m) {
+                            const uint64_t lo = v[u][3 * m + 1], hi = v[u][3 * m + 2];
+                            am[m] = fmaxf(am[m], __uint_as_float((uint32_t)v[u][3 * m]));
+                            ss[m] += __longlong_as_double(
+                                (long long)(((hi & 0xFFFFFFFFull) << 32) | (lo & 0xFFFFFFFFull)));
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const double tot = wave_sum63(ss[m]);
+                const float amax = wave_max63(am[m]);
+                float r = 1.0f, amax_t = amax;
+                if (norm) {
+                    const float ms = (float)(tot / (double)ph.K);
+                    r = 1.0f / sqrtf(ms + 1e-6f);
+                    // max |bf16(x * r)| = bf16(max|x| * r): rounding is monotonic
+                    amax_t = bf16_bits_to_f32(f32_to_bf16_bits(amax * r));
+                }
+                if (lane == 63) {
+                    s_sh[p & 1][m] = amax_t / 127.0f;
+                    r_sh[p & 1][m] = r;
+                }
+            }
+        }
+    }
+    float s[M], r[M], rinv[M];
+    bool rinv_ok[M];
+    for (int j0 = 0; has && j0 < words; j0 += kXBatch * kSeqThreads) {
+        if (j0 > 0 && tagged_in) {
+#pragma unroll
+            for (int u = 0; u < kXBatch; ++u) {
+                const int j = j0 + threadIdx.x + u * kSeqThreads;
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    if (j < words) xw[u][m] = load_shared(xsrc + (int64_t)m * ph.in_stride2 + j);
+            }
+        }
+        if (tagged_in) {
             int64_t spins = 0;
             for (;;) {
                 bool stale = false;
 #pragma unroll
-                for (int u = 0; u < kStatBatch; ++u)
+                for (int u = 0; u < kXBatch; ++u)
 #pragma unroll
-                    for (int c = 0; c < 3 * M; ++c)
-                        stale |= base + lane + 64 * u < ph.in_nrec && tag_of(v[u][c]) != want;
+                    for (int m = 0; m < M; ++m)
+                        stale |= j0 + threadIdx.x + u * kSeqThreads < words && tag_of(xw[u][m]) != want;
                 if (!wave_any(stale) || gave_up(P, spins)) break;
-#pragma unroll
-                for (int u = 0; u < kStatBatch; ++u)
-#pragma unroll
-                    for (int c = 0; c < 3 * M; ++c)
-                        if (base + lane + 64 * u < ph.in_nrec && tag_of(v[u][c]) != want)
-                            v[u][c] = load_shared(rp[u] + c);
-            }
-#pragma unroll
-            for (int u = 0; u < kStatBatch; ++u) {
-                if (base + lane + 64 * u < ph.in_nrec) {
-#pragma unroll
-                    for (int m = 0; m < M; ++m) {
-                        const uint64_t lo = v[u][3 * m + 1], hi = v[u][3 * m + 2];
-                        am[m] = fmaxf(am[m], __uint_as_float((uint32_t)v[u][3 * m]));
-                        ss[m] += __longlong_as_double((long long)(((hi & 0xFFFFFFFFull) << 32) | (lo & 0xFFFFFFFFull)));
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const double tot = wave_sum(ss[m]);
-            const float amax = wave_max(am[m]);
-            float r = 1.0f, amax_t = amax;
-            if (norm) {
-                const float ms = (float)(tot / (double)ph.K);
-                r = 1.0f / sqrtf(ms + 1e-6f);
-                // max |bf16(x * r)| = bf16(max|x| * r): rounding is monotonic
-                amax_t = bf16_bits_to_f32(f32_to_bf16_bits(amax * r));
-            }
-            if (lane == 0) {
-                s_sh[p & 1][m] = amax_t / 127.0f;
-                r_sh[p & 1][m] = r;
-            }
-        }
-    }
-    __syncthreads();
-    if (has) {
-        float s[M], r[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            s[m] = s_sh[p & 1][m];
-            r[m] = r_sh[p & 1][m];
-        }
-        for (int j0 = 0; j0 < words; j0 += kXBatch * kSeqThreads) {
-            if (j0 > 0 && tagged_in) {
 #pragma unroll
                 for (int u = 0; u < kXBatch; ++u) {
                     const int j = j0 + threadIdx.x + u * kSeqThreads;
 #pragma unroll
                     for (int m = 0; m < M; ++m)
-                        if (j < words)
-                            xw[u][m] = load_shared(ph.in_xt + (int64_t)m * ph.in_stride2 + (kr.k_lo >> 1) + j);
+                        if (j < words && tag_of(xw[u][m]) != want)
+                            xw[u][m] = load_shared(xsrc + (int64_t)m * ph.in_stride2 + j);
                 }
             }
-            if (tagged_in) {
-                int64_t spins = 0;
-                for (;;) {
-                    bool stale = false;
+        }
+        if (j0 == 0) {
+            __syncthreads();   // the scales from wave 0
 #pragma unroll
-                    for (int u = 0; u < kXBatch; ++u)
-#pragma unroll
-                        for (int m = 0; m < M; ++m)
-                            stale |= j0 + threadIdx.x + u * kSeqThreads < words && tag_of(xw[u][m]) != want;
-                    if (!wave_any(stale) || gave_up(P, spins)) break;
-#pragma unroll
-                    for (int u = 0; u < kXBatch; ++u) {
-                        const int j = j0 + threadIdx.x + u * kSeqThreads;
-#pragma unroll
-                        for (int m = 0; m < M; ++m)
-                            if (j < words && tag_of(xw[u][m]) != want)
-                                xw[u][m] = load_shared(ph.in_xt + (int64_t)m * ph.in_stride2 + (kr.k_lo >> 1) + j);
-                    }
-                }
+            for (int m = 0; m < M; ++m) {
+                s[m] = s_sh[p & 1][m];
+                r[m] = r_sh[p & 1][m];
+                rinv[m] = 1.0f / s[m];
+                rinv_ok[m] = fabsf(rinv[m]) < INFINITY;
             }
+        }
 #pragma unroll
-            for (int u = 0; u < kXBatch; ++u) {
-                const int j = j0 + threadIdx.x + u * kSeqThreads;
-                if (j >= words) continue;
+        for (int u = 0; u < kXBatch; ++u) {
+            const int j = j0 + threadIdx.x + u * kSeqThreads;
+            if (j >= words) continue;
 #pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    const uint32_t pair = tagged_in ? (uint32_t)xw[u][m]
-                                                    : ph.in[(int64_t)m * ph.in_stride2 + (kr.k_lo >> 1) + j];
-                    uint32_t packed = 0;
+            for (int m = 0; m < M; ++m) {
+                const uint32_t pair = tagged_in ? (uint32_t)xw[u][m]
+                                                : *gptr(ph.in + (int64_t)m * ph.in_stride2 + (h.k_lo >> 1) + j);
+                uint32_t packed = 0;
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        float t = bf16_bits_to_f32((pair >> (16 * e)) & 0xFFFFu);
-                        if (norm) t = bf16_bits_to_f32(f32_to_bf16_bits(t * r[m]));
-                        float qv = 0.0f;
-                        if (s[m] != 0.0f) qv = fminf(fmaxf(rintf(t / s[m]), -127.0f), 127.0f);
-                        packed |= ((uint32_t)(int)qv & 0xFFu) << (8 * e);
-                    }
-                    *reinterpret_cast<uint16_t *>(q_lds + m * P->q_stride + 2 * j) = (uint16_t)packed;
+                for (int e = 0; e < 2; ++e) {
+                    float t = bf16_bits_to_f32((pair >> (16 * e)) & 0xFFFFu);
+                    if (norm) t = bf16_bits_to_f32(f32_to_bf16_bits(t * r[m]));
+                    const float qv = s[m] != 0.0f ? quant_code(t, s[m], rinv[m], rinv_ok[m]) : 0.0f;
+                    packed |= ((uint32_t)(int)qv & 0xFFu) << (8 * e);
                 }
+                *reinterpret_cast<uint16_t *>(g_lds + m * L.qs + 2 * j) = (uint16_t)packed;
             }
         }
     }
+    if (!has) __syncthreads();     // keep the barrier count equal for every workgroup shape
+    store_meta(L, p + 1, pre);
     __syncthreads();
 }
 
-// ---------------------------------------------------------------- row-block finalisation (cold path)
+// ---------------------------------------------------------------- hand-over of a phase
 
-// The wave owning a row block's last tile gathers every part in (k chunk,
-// wave) order and writes the bf16 outputs, their tagged copy and the block's
-// stats record.  Out of line: it runs once per row block and phase.
+// Gather a row block's contributions (lane l's M tagged words of contribution
+// c at area + (c * 64 + l) * M) in their fixed order, write its bf16 outputs,
+// their tagged copy and its stats record, then count it as done.
 template <int BITS, int M>
-__device__ __noinline__ void finalize_rb(const SeqPlan *P, uint32_t gen, int phase, int rb, const float *s_act) {
-    using L = Layout<BITS>;
-    const SeqPhase ph = cload(P->phases, phase);
-    const int lane = threadIdx.x & 63;
-    const uint32_t tag = make_tag(gen, phase);
-    const int kcl = ph.nkc - 1;
+__device__ __forceinline__ void finalize_rb(const SeqPlan *P, const uint64_t *area, uint32_t tag, const SeqFin &f,
+                                            const float *s_act, uint32_t *fin_count, int lane) {
+    using Lt = Layout<BITS>;
     float tot[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) tot[m] = 0.0f;
-
-    // contributions (kc, part): the workgroups touching segment (kc, rb), in order
-    auto n_parts = [&](int kc) {
-        const int sg = segment(ph, kc, rb);
-        return cload(ph.seg_wg, 2 * sg + 1) - cload(ph.seg_wg, 2 * sg) + 1;
-    };
-    int ckc = 0, cp = 0;
-    while (ckc <= kcl) {
-        constexpr int B = 16;
-        const uint64_t *src[B];
-        bool valid[B];
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-            valid[u] = ckc <= kcl;
-            if (valid[u]) {
-                const int sg = segment(ph, ckc, rb);
-                src[u] = P->partials + ((int64_t)(sg * P->parts + cp) * M) * 64 + lane;
-                if (++cp == n_parts(ckc)) {
-                    cp = 0;
-                    ++ckc;
-                }
-            } else {
-                src[u] = src[0];
-            }
-        }
+    constexpr int B = 32 / M;   // contributions per round trip (within the vector-memory counter)
+    for (int c0 = 0; c0 < f.nc; c0 += B) {
         uint64_t v[B][M];
 #pragma unroll
-        for (int u = 0; u < B; ++u)
+        for (int u = 0; u < B; ++u) {
+            const uint64_t *src = area + ((int64_t)(f.c0 + c0 + u) * 64 + lane) * M;
 #pragma unroll
-            for (int m = 0; m < M; ++m) v[u][m] = load_shared(src[u] + m * 64);
+            for (int m = 0; m < M; ++m) v[u][m] = c0 + u < f.nc ? load_shared(src + m) : 0;
+        }
         // re-poll every stale word together: one round trip per round
         int64_t spins = 0;
         for (;;) {
@@ -396,43 +402,91 @@ __device__ __noinline__ void finalize_rb(const SeqPlan *P, uint32_t gen, int pha
 #pragma unroll
             for (int u = 0; u < B; ++u)
 #pragma unroll
-                for (int m = 0; m < M; ++m) stale |= valid[u] && tag_of(v[u][m]) != tag;
+                for (int m = 0; m < M; ++m) stale |= c0 + u < f.nc && tag_of(v[u][m]) != tag;
             if (!wave_any(stale) || gave_up(P, spins)) break;
 #pragma unroll
-            for (int u = 0; u < B; ++u)
+            for (int u = 0; u < B; ++u) {
+                const uint64_t *src = area + ((int64_t)(f.c0 + c0 + u) * 64 + lane) * M;
 #pragma unroll
                 for (int m = 0; m < M; ++m)
-                    if (valid[u] && tag_of(v[u][m]) != tag) v[u][m] = load_shared(src[u] + m * 64);
+                    if (c0 + u < f.nc && tag_of(v[u][m]) != tag) v[u][m] = load_shared(src + m);
+            }
         }
 #pragma unroll
         for (int u = 0; u < B; ++u) {
-            if (valid[u]) {
+            if (c0 + u < f.nc) {
 #pragma unroll
                 for (int m = 0; m < M; ++m) tot[m] += __uint_as_float((uint32_t)v[u][m]);
             }
         }
     }
-    const SeqOp op = cload(P->ops, op_of_rb(P, ph, rb));
-    const int rbl = rb - op.rb_base;
-    const int n = rbl * 64 + lane;
-    const float unscale = 1.0f / (float)(1 << L::kAccShift);
+    const float unscale = 1.0f / (float)(1 << Lt::kAccShift);
     float yv[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const uint32_t yb = f32_to_bf16_bits(s_act[m] * (tot[m] * unscale));
-        const uint32_t hi = (uint32_t)__shfl_xor((int)yb, 1, 64);
+        const uint32_t hi = dpp_u32<kDppQuadSwap1>(yb);   // the odd neighbour's value
         const uint32_t pair = yb | (hi << 16);
-        if (!(lane & 1) && n < op.N) {
-            const int64_t idx = (int64_t)m * (op.N >> 1) + (n >> 1);
-            op.out[idx] = pair;
-            if (op.xt) store_shared(op.xt + idx, tagged(pair, tag));
+        if (!(lane & 1) && lane < f.rows) {
+            const int64_t idx = (int64_t)m * f.row_words + (lane >> 1);
+            *gptr(f.out + idx) = pair;
+            if (f.xt) store_shared(f.xt + idx, tagged(pair, tag));
         }
-        yv[m] = n < min(op.N, op.stats_cols) ? bf16_bits_to_f32(yb) : 0.0f;
+        yv[m] = lane < f.stat_rows ? bf16_bits_to_f32(yb) : 0.0f;
     }
-    if (op.stats_cols > 0) publish_stats<M>(P, op.stats_rec + rbl, yv, tag, lane);
+    if (f.stats) publish_stats<M>(f.stats, yv, tag, lane);
+    if (lane == 0) counter_add(fin_count, 1u);   // its contributions have been read
 }
 
-// ---------------------------------------------------------------- the kernel
+// Workgroup-wide exit from phase p (every wave has parked its parts in LDS):
+// merge the waves' parts of every segment the workgroup touched (in wave
+// order) and publish one tagged partial per (segment, workgroup).
+template <int M>
+__device__ __forceinline__ void leave_phase(const SeqPlan *P, const Lay &L, int p, uint32_t gen) {
+    __syncthreads();
+    const SeqWgHead h = *meta_head(L, p);
+    const int lane = threadIdx.x & 63;
+    const int j = uniform(threadIdx.x >> 6);
+    const uint32_t tag = make_tag(gen, p);
+    const float *lp = lds_partials(L, M) + lane;
+    uint64_t *area = cload(&P->partials) + (int64_t)(p & 1) * L.part_stride * 64 * M;
+    for (int e = j; e < h.n_seg; e += kSeqWaves) {
+        const SeqWgSeg sg = meta_seg(L, p)[e];
+        float v[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) v[m] = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < kSeqWaves; ++ww) {
+            if (sg.slot[ww] != 0xFF) {
+                const float *src = lp + ((ww * L.slots + sg.slot[ww]) * M) * 64;
+#pragma unroll
+                for (int m = 0; m < M; ++m) v[m] += src[m * 64];
+            }
+        }
+        uint64_t *dst = area + ((int64_t)sg.cidx * 64 + lane) * M;
+#pragma unroll
+        for (int m = 0; m < M; ++m) store_shared(dst + m, tagged(__float_as_uint(v[m]), tag));
+    }
+}
+
+// A finalising workgroup's row blocks of phase p, spread over its waves.
+// Inline: a call would wait for every outstanding store on entry and exit.
+template <int BITS, int M>
+__device__ __forceinline__ void finalize_phase(const SeqPlan *P, const Lay &L, int p, uint32_t gen,
+                                            const float *s_act) {
+    const SeqWgHead h = *meta_head(L, p);
+    const int lane = threadIdx.x & 63;
+    const int j = uniform(threadIdx.x >> 6);
+    const uint32_t tag = make_tag(gen, p);
+    const uint64_t *area = cload(&P->partials) + (int64_t)(p & 1) * L.part_stride * 64 * M;
+    uint32_t *fin_count = meta_phase(L, p)->fin_count;
+    for (int i = j; i < h.n_fin; i += kSeqWaves) {
+        const SeqFin f = meta_fin(L, p)[i];
+        finalize_rb<BITS, M>(P, area, tag, f, s_act, fin_count, lane);
+    }
+}
+
+// ---------------------------------------------------------------- the weight stream
 
 template <int BITS>
 struct Slot {
@@ -442,39 +496,44 @@ struct Slot {
 };
 
 // Tiles in flight per wave.  A wave can have at most 63 vector loads
-// outstanding and a tile takes kSlabs + 1 of them (W4: 12 tiles, W6: 9);
-// larger M trims the ring to stay within 512 registers.
+// outstanding and a tile takes kSlabs + 1 of them; the ring stays well below
+// that: the in-flight bytes of the whole grid only need to cover the memory
+// latency, and every byte beyond that lengthens the queue that the phase
+// hand-over's own requests wait in.  M = 4 trims it to stay within 512
+// registers (vector plus accumulation registers).
+#ifndef MBQ_RING_W4
+#define MBQ_RING_W4 8
+#endif
+#ifndef MBQ_RING_W6
+#define MBQ_RING_W6 6
+#endif
 template <int BITS, int M>
 constexpr int ring_depth() {
-    return BITS == 4 ? (M < 4 ? 12 : 10) : (M < 3 ? 9 : (M < 4 ? 8 : 7));
+    return BITS == 4 ? (M < 4 ? MBQ_RING_W4 : (MBQ_RING_W4 < 6 ? MBQ_RING_W4 : 6))
+                     : (M < 4 ? MBQ_RING_W6 : (MBQ_RING_W6 < 5 ? MBQ_RING_W6 : 5));
 }
 static_assert(ring_depth<4, 1>() * (Layout<4>::kSlabs + 1) <= 63, "vmcnt limit");
 static_assert(ring_depth<6, 1>() * (Layout<6>::kSlabs + 1) <= 63, "vmcnt limit");
 
 // Issue side: a cursor over the wave's run list.  Everything here is
-// wave-uniform and read with scalar loads, so waiting on a tile never waits
-// on a plan read.
+// wave-uniform and read with scalar loads.
 struct Issue {
     const SeqRun *runs;
-    int next, count;       // next run to open; runs of this wave
+    int next;              // next run to open
     int left;              // tiles left in the open run
     const uint8_t *src;    // next tile
 };
 
+// Load the wave's next tile into slot s.
 template <int BITS>
-__device__ __forceinline__ void issue(Issue &is, const uint8_t *dummy, int lane, Slot<BITS> &s) {
+__device__ __forceinline__ void issue(Issue &is, int lane, Slot<BITS> &s) {
     uint32_t hdr = 0;
     if (is.left == 0) {
-        if (is.next < is.count) {
-            const SeqRun r = cload(is.runs, is.next);
-            ++is.next;
-            is.src = r.src;
-            is.left = (int)r.n;
-            hdr = r.hdr;
-        } else {                       // past the end: keep the ring's load count fixed
-            is.src = dummy;
-            is.left = 1;
-        }
+        const SeqRun r = cload(is.runs, is.next);
+        ++is.next;
+        is.src = r.src;
+        is.left = (int)r.n;
+        hdr = r.hdr;
     }
     s.hdr = hdr;
     load_tile<BITS>(is.src, lane, s.w, s.sc);
@@ -483,73 +542,31 @@ __device__ __forceinline__ void issue(Issue &is, const uint8_t *dummy, int lane,
 }
 
 // Park the open run's partial (segment sums of 4 rows x M per lane, reduced
-// over the wave's k slices) in its LDS slot; lane l holds row l.
+// over the wave's k slices) in its LDS slot, row r at index r.  lp_w is the
+// wave's slot area.
 template <int M>
 __device__ __forceinline__ void close_segment(int slot, float (&facc)[4][M], float *lp_w, int lane) {
     if (slot < 0) return;
-    float *dst = lp_w + slot * M * 64;
+    float *dst = lp_w + slot * M * 64 + slice_row(lane);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         float f[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = slice_sum(facc[i][m]);
-        dst[m * 64] = to_row_layout(f, lane);
+        for (int i = 0; i < 4; ++i) f[i] = facc[i][m];
+        dst[m * 64] = slice_reduce(f);
     }
-}
-
-// Workgroup-wide exit from phase p: merge the waves' LDS partials of every
-// segment the workgroup touched (in wave order), publish one tagged partial
-// per (segment, workgroup), then finalise the row blocks whose last tile the
-// workgroup owns.
-template <int BITS, int M>
-__device__ __noinline__ void leave_phase(const SeqPlan *P, int p, uint32_t gen, int wg, const float *lp,
-                                         const float *s_act) {
-    __syncthreads();
-    const SeqPhase ph = cload(P->phases, p);
-    const int lane = threadIdx.x & 63;
-    const int j = uniform(threadIdx.x >> 6);
-    const uint32_t tag = make_tag(gen, p);
-    const int w0 = wg * kSeqWaves;
-    const int w1 = min(w0 + kSeqWaves, ph.W) - 1;
-    const int s0 = cload(ph.wg_seg, 2 * wg), s1 = cload(ph.wg_seg, 2 * wg + 1);
-    for (int sg = s0 + j; sg <= s1; sg += kSeqWaves) {
-        const int wa = max(w0, seg_first_owner(ph, sg));
-        const int wb = min(w1, seg_last_owner(ph, sg));
-        float v[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) v[m] = 0.0f;
-        for (int ww = wa; ww <= wb; ++ww) {
-            const float *src = lp + (((ww - w0) * P->slots + sg - first_segment(ph, ww)) * M) * 64 + lane;
-#pragma unroll
-            for (int m = 0; m < M; ++m) v[m] += src[m * 64];
-        }
-        const int part = wg - cload(ph.seg_wg, 2 * sg);
-        uint64_t *dst = P->partials + ((int64_t)(sg * P->parts + part) * M) * 64 + lane;
-#pragma unroll
-        for (int m = 0; m < M; ++m) store_shared(dst + m * 64, tagged(__float_as_uint(v[m]), tag));
-    }
-    const int f0 = cload(ph.wg_fin, 2 * wg), fn = cload(ph.wg_fin, 2 * wg + 1);
-    for (int i = j; i < fn; i += kSeqWaves) finalize_rb<BITS, M>(P, gen, p, f0 + i, s_act);
 }
 
 struct Compute {
-    int active;   // phase whose prologue ran last
     int slot;     // LDS slot of the open run's segment; -1: none
     int q;        // LDS byte offset of the next tile's activation group
 };
 
 template <int BITS, int M>
-__device__ __forceinline__ void compute(const SeqPlan *P, uint32_t gen, int wg, int lane, Compute &c,
-                                        float (&facc)[4][M], const Slot<BITS> &s, int8_t *q_lds, int qs,
-                                        float *lp, float *lp_w, float (*s_sh)[4], float (*r_sh)[4]) {
-    if (s.hdr != 0) {   // the tile opens a run: close the previous segment, meet the run's phase
+__device__ __forceinline__ void compute(const Lay &L, int lane, Compute &c, float (&facc)[4][M], const Slot<BITS> &s,
+                                        float *lp_w) {
+    if (s.hdr != 0) {   // the tile opens a run: close the previous segment
         close_segment<M>(c.slot, facc, lp_w, lane);
-        const int phase = (int)(s.hdr & ((1u << kRunPhaseBits) - 1));
-        while (c.active < phase) {
-            if (c.active >= 0) leave_phase<BITS, M>(P, c.active, gen, wg, lp, s_sh[c.active & 1]);
-            ++c.active;
-            enter_phase<M>(P, c.active, gen, wg, q_lds, s_sh, r_sh);
-        }
         c.slot = (int)((s.hdr >> kRunPhaseBits) & ((1u << kRunSlotBits) - 1));
         c.q = (int)((s.hdr >> (kRunPhaseBits + kRunSlotBits)) & ((1u << kRunGroupBits) - 1)) * kGroup;
 #pragma unroll
@@ -562,7 +579,8 @@ __device__ __forceinline__ void compute(const SeqPlan *P, uint32_t gen, int wg, 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[i][m] = 0;
-    const int8_t *qg = q_lds + c.q + (lane >> 4) * 32;
+    const int8_t *qg = g_lds + c.q + (lane >> 4) * 32;
+    const int qs = L.qs;
     dot_tile<BITS, M>(s.w, [&](int m, int d) { return reinterpret_cast<const int *>(qg + m * qs)[d]; }, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -573,10 +591,49 @@ __device__ __forceinline__ void compute(const SeqPlan *P, uint32_t gen, int wg, 
     c.q += kGroup;
 }
 
+// Start a phase's stream: ring slots [A, B) with the wave's tiles A..B-1 of
+// n that exist (the ring may be primed in two steps).
+template <int BITS, int D, int A, int B>
+__device__ __forceinline__ void prime(Issue &is, int lane, int n, Slot<BITS> (&ring)[D]) {
+#pragma unroll
+    for (int i = A; i < B; ++i)
+        if (i < n) issue<BITS>(is, lane, ring[i]);
+}
+
+// One phase of the wave: n tiles through the ring, which was primed with the
+// first min(n, D).  No load of the next phase is issued here, so the wave's
+// memory queue is empty when the phase's partials go out.  While at least D
+// more tiles follow, every slot is refilled (a fixed load count, so each wait
+// leaves the later tiles in flight); the last two ring rounds refill only
+// what exists.  Nothing is loaded for nothing: even a load that reads no
+// memory costs address-unit time that the hand-over's own requests need.
+template <int BITS, int M, int D>
+__device__ __forceinline__ void stream_phase(const Lay &L, Issue &is, int lane, int n, Slot<BITS> (&ring)[D],
+                                             float (&facc)[4][M], float *lp_w) {
+    Compute c;
+    c.slot = -1;
+    c.q = 0;
+    int i0 = 0;
+    for (; i0 + 2 * D <= n; i0 += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            compute<BITS, M>(L, lane, c, facc, ring[i], lp_w);
+            issue<BITS>(is, lane, ring[i]);
+        }
+    }
+    for (; i0 < n; i0 += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            if (i0 + i < n) compute<BITS, M>(L, lane, c, facc, ring[i], lp_w);
+            if (i0 + i + D < n) issue<BITS>(is, lane, ring[i]);
+        }
+    }
+    close_segment<M>(c.slot, facc, lp_w, lane);
+}
+
 template <int BITS, int M>
 __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const SeqPlan *__restrict__ P, uint32_t *err,
                                                           uint32_t gen) {
-    extern __shared__ __align__(16) int8_t q_lds[];
     __shared__ float s_sh[2][4];
     __shared__ float r_sh[2][4];
     if (cload(&P->magic) != kPlanMagic) {   // workspace does not hold a prepared plan
@@ -586,56 +643,63 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const SeqPlan *__restr
     const int lane = threadIdx.x & 63;
     const int wi = uniform(threadIdx.x >> 6);
     const int wg = blockIdx.x;
-    const int w = wg * kSeqWaves + wi;
-    const int n_phases = cload(&P->n_phases);
-    const int qs = cload(&P->q_stride);
-    const int slots = cload(&P->slots);
-    const uint8_t *dummy = cload(&P->dummy);
+    Lay L;
+    L.qs = cload(&P->q_stride);
+    L.slots = cload(&P->slots);
+    L.seg_cap = cload(&P->seg_cap);
+    L.blk_bytes = cload(&P->blk_bytes);
+    L.grid = cload(&P->grid);
+    L.n_phases = cload(&P->n_phases);
+    L.part_stride = cload(&P->part_stride);
+    L.meta_off = M * L.qs + kSeqWaves * L.slots * M * 64 * 4;
+    L.meta_bytes = ((int)sizeof(SeqPhase) + L.blk_bytes + 15) & ~15;
+    const bool finaliser = is_final_wg(wg, L.grid);
 
-    external_stats<M>(P, w, lane, gen);
+    {   // metadata of the first phase
+        uint32_t pre[kMetaIters];
+        fetch_meta(P, L, 0, wg, pre);
+        store_meta(L, 0, pre);
+    }
+    external_stats<M>(P, wg * kSeqWaves + wi, L.grid * kSeqWaves, lane, gen);
+    __syncthreads();
 
-    const SeqWave wv = cload(cload(&P->wtab), w);
+    const SeqWave wv = cload(cload(&P->wtab), wg * kSeqWaves + wi);
     Issue is;
     is.runs = cload(&P->runs) + wv.run_begin;
     is.next = 0;
-    is.count = wv.run_count;
     is.left = 0;
-    is.src = dummy;
-    float *lp = reinterpret_cast<float *>(q_lds + M * qs);
-    float *lp_w = lp + (wi * slots * M) * 64 + lane;
-    Compute c;
-    c.active = -1;
-    c.slot = -1;
-    c.q = 0;
+    is.src = nullptr;
+    float *lp_w = lds_partials(L, M) + (wi * L.slots * M) * 64;
     float facc[4][M];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int m = 0; m < M; ++m) facc[i][m] = 0.0f;
-
     constexpr int D = ring_depth<BITS, M>();
     Slot<BITS> ring[D];
-#pragma unroll
-    for (int i = 0; i < D; ++i) issue<BITS>(is, dummy, lane, ring[i]);
-    int left = wv.tiles;
-    while (left > 0) {
-#pragma unroll
-        for (int i = 0; i < D; ++i) {
-            if (left > 0) {
-                compute<BITS, M>(P, gen, wg, lane, c, facc, ring[i], q_lds, qs, lp, lp_w, s_sh, r_sh);
-                --left;
-            }
-            issue<BITS>(is, dummy, lane, ring[i]);
-        }
+
+    // One code path per step, each step once per phase: the whole loop has
+    // to stay resident in the instruction cache, which two CUs share.
+    prime<BITS, D, 0, D>(is, lane, meta_head(L, 0)->tiles[wi], ring);
+    for (int p = 0;; ++p) {
+        enter_phase<M>(P, L, p, gen, wg, s_sh, r_sh);
+        stream_phase<BITS, M, D>(L, is, lane, uniform(meta_head(L, p)->tiles[wi]), ring, facc, lp_w);
+        leave_phase<M>(P, L, p, gen);
+        // Finalisers hand the phase over while their memory queue is empty;
+        // the others start the next phase's weight stream at once, after a
+        // barrier that keeps any wave's loads from queueing ahead of another
+        // wave's partials.
+        if (finaliser) finalize_phase<BITS, M>(P, L, p, gen, s_sh[p & 1]);
+        else __syncthreads();
+        if (p + 1 == L.n_phases) break;
+        prime<BITS, D, 0, D>(is, lane, uniform(meta_head(L, p + 1)->tiles[wi]), ring);
     }
-    // close the last segment and meet every remaining workgroup-wide prologue
-    close_segment<M>(c.slot, facc, lp_w, lane);
-    while (c.active < n_phases - 1) {
-        if (c.active >= 0) leave_phase<BITS, M>(P, c.active, gen, wg, lp, s_sh[c.active & 1]);
-        ++c.active;
-        enter_phase<M>(P, c.active, gen, wg, q_lds, s_sh, r_sh);
+
+    // The last workgroup to exit clears the counters for the next launch
+    // (every wave's counter increments have completed before it counts out).
+    wait_memory();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t *cnt = cload(&P->counters);
+        if (counter_add(cnt + L.n_phases, 1u) == (uint32_t)(L.grid - 1))
+            for (int i = 0; i <= L.n_phases; ++i) store_shared(cnt + i, 0u);
     }
-    leave_phase<BITS, M>(P, c.active, gen, wg, lp, s_sh[c.active & 1]);
 }
 
 }  // namespace

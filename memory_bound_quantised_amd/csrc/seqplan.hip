@@ -1,6 +1,7 @@
 // Host side of the fused decode-step walk: turns an mbq_op list into the
 // device plan the persistent kernel reads (see mbq_seq.h), and sizes the
 // workspace.  Pure host code; no HIP call happens here.
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -21,9 +22,10 @@ int64_t up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 // Tile ranges and chunking, mirroring the kernel's arithmetic.
 struct PhaseGeom {
     int R, G, nkc, T, W;
+    std::vector<int> st;   // [W + 1]: first tile of each wave's range
     int chunk_len(int kc) const { return kc < nkc - 1 ? kChunkGroups : G - kChunkGroups * (nkc - 1); }
-    int start(int w) const { return (int)(((int64_t)T * w) / W); }
-    int owner(int t) const { return (int)((((int64_t)t + 1) * W - 1) / T); }
+    int start(int w) const { return st[w]; }
+    int owner(int t) const { return (int)(std::upper_bound(st.begin(), st.end(), t) - st.begin()) - 1; }
     void decode(int t, int &kc, int &rb) const {
         const int chunk_tiles = R * kChunkGroups;
         kc = t / chunk_tiles;
@@ -34,7 +36,33 @@ struct PhaseGeom {
         decode(t, kc, rb);
         return kc * R + rb;
     }
+    // Cut the T tiles into W = min(T, waves) contiguous ranges, the waves of
+    // non-finalising workgroups weighted by w_other, every range non-empty.
+    void cut(int waves, int grid, double w_other) {
+        W = T < waves ? T : waves;
+        std::vector<double> cum(W + 1, 0.0);
+        for (int w = 0; w < W; ++w) cum[w + 1] = cum[w] + (is_final_wg(w / kSeqWaves, grid) ? 1.0 : w_other);
+        st.assign(W + 1, 0);
+        for (int w = 1; w < W; ++w) {
+            int v = (int)((double)T * cum[w] / cum[W] + 0.5);
+            v = std::max(v, st[w - 1] + 1);
+            v = std::min(v, T - (W - w));
+            st[w] = v;
+        }
+        st[W] = T;
+    }
 };
+
+// Share of a phase's tiles given to a wave of a non-finalising workgroup,
+// relative to a finalising one.
+double other_weight() {
+    static const double w = [] {
+        const char *e = getenv("MBQ_SPLIT_WEIGHT");
+        const double v = e ? atof(e) : 1.0;
+        return v > 0.05 && v < 20.0 ? v : 1.0;
+    }();
+    return w;
+}
 
 }  // namespace
 
@@ -118,7 +146,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
         ext_rb += e.n_rb;
     }
 
-    // ---- geometry, partial slots, LDS activation span
+    // ---- geometry and per-wave run lists
     const int grid = n_cu;
     const int waves = grid * kSeqWaves;
     std::vector<PhaseGeom> geo(n_ph);
@@ -138,40 +166,24 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
         const int64_t T = R * g.G;
         if (T >= ((int64_t)1 << 31)) return MBQ_ERR_SHAPE;
         g.T = (int)T;
-        g.W = (int)(T < waves ? T : waves);
+        g.cut(waves, grid, other_weight());
         for (int w = 0; w < g.W; ++w) {
             const int t0 = g.start(w), t1 = g.start(w + 1) - 1;
-            const int s = g.segment(t1) - g.segment(t0) + 1;
-            if (s > slots) slots = s;
+            const int sc = g.segment(t1) - g.segment(t0) + 1;
+            if (sc > slots) slots = sc;
         }
         for (int wg = 0; wg * kSeqWaves < g.W; ++wg) {
-            const int w1 = (wg + 1) * kSeqWaves < g.W ? (wg + 1) * kSeqWaves : g.W;
-            const int t0 = g.start(wg * kSeqWaves), t1 = g.start(w1) - 1;
+            const int t0 = g.start(wg * kSeqWaves), t1 = g.start(std::min((wg + 1) * kSeqWaves, g.W)) - 1;
             int kc0, kc1, rb;
             g.decode(t0, kc0, rb);
             g.decode(t1, kc1, rb);
-            int64_t hi = (int64_t)(kc1 + 1) * kChunkGroups * kGroup;
-            if (hi > ops[ph[p].first].K) hi = ops[ph[p].first].K;
-            const int span = (int)(hi - (int64_t)kc0 * kChunkGroups * kGroup);
-            if (span > q_span) q_span = span;
+            const int64_t hi = std::min<int64_t>((int64_t)(kc1 + 1) * kChunkGroups * kGroup, ops[ph[p].first].K);
+            q_span = std::max(q_span, (int)(hi - (int64_t)kc0 * kChunkGroups * kGroup));
         }
     }
-    // workgroups touching one segment (memory partial slots per segment)
-    int parts = 1;
-    int64_t max_seg = 1;
-    for (int p = 0; p < n_ph; ++p) {
-        const PhaseGeom &g = geo[p];
-        max_seg = std::max<int64_t>(max_seg, (int64_t)g.nkc * g.R);
-        for (int kc = 0; kc < g.nkc; ++kc)
-            for (int rb = 0; rb < g.R; ++rb) {
-                const int t0 = kc * g.R * kChunkGroups + rb * g.chunk_len(kc);
-                const int t1 = t0 + g.chunk_len(kc) - 1;
-                parts = std::max(parts, g.owner(t1) / kSeqWaves - g.owner(t0) / kSeqWaves + 1);
-            }
-    }
-    // ---- per-wave run lists: each wave's tile range of each phase, cut at
-    // segment boundaries (a run's tiles are consecutive groups of one row
-    // block, so they are contiguous in the packed matrix)
+    if (slots > 255) return MBQ_ERR_SHAPE;
+    // A run is a wave's part of one segment: consecutive groups of one row
+    // block, so its tiles are contiguous in the packed matrix.
     const int64_t tile_bytes = bits == 4 ? Layout<4>::kTileBytes : Layout<6>::kTileBytes;
     std::vector<std::vector<SeqRun>> wruns(waves);
     std::vector<int> wtiles(waves, 0);
@@ -193,7 +205,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
                 const int g0 = kc * kChunkGroups + gi;
                 const int slot = kc * g.R + rb - seg0;
                 const int gl = g0 - wg_g0;
-                if (slot >= (1 << kRunSlotBits) || gl >= (1 << kRunGroupBits)) return MBQ_ERR_SHAPE;
+                if (gl >= (1 << kRunGroupBits)) return MBQ_ERR_SHAPE;
                 int op = ph[p].first;
                 while (op + 1 < ph[p].first + ph[p].count && rb >= rb_base[p][op + 1 - ph[p].first]) ++op;
                 SeqRun r;
@@ -210,9 +222,58 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     }
     int64_t n_runs = 0;
     for (int w = 0; w < waves; ++w) n_runs += (int64_t)wruns[w].size();
+    if (n_runs >= ((int64_t)1 << 31)) return MBQ_ERR_SHAPE;
 
+    // ---- contributions: segment (kc, rb) gets one partial per workgroup
+    // touching it; a row block's partials are contiguous, in (kc, workgroup)
+    // order.
+    std::vector<std::vector<int>> seg_c0(n_ph), seg_wg0(n_ph), rb_c0(n_ph), rb_nc(n_ph), rb_fin(n_ph);
+    int part_stride = 1, seg_cap = 1, fin_cap = 1;
+    for (int p = 0; p < n_ph; ++p) {
+        const PhaseGeom &g = geo[p];
+        const int nseg = g.nkc * g.R;
+        seg_c0[p].assign(nseg, 0);
+        seg_wg0[p].assign(nseg, 0);
+        rb_c0[p].assign(g.R, 0);
+        rb_nc[p].assign(g.R, 0);
+        rb_fin[p].assign(g.R, 0);
+        int c = 0;
+        for (int rb = 0; rb < g.R; ++rb) {
+            rb_c0[p][rb] = c;
+            for (int kc = 0; kc < g.nkc; ++kc) {
+                const int t0 = kc * g.R * kChunkGroups + rb * g.chunk_len(kc);
+                const int t1 = t0 + g.chunk_len(kc) - 1;
+                const int wga = g.owner(t0) / kSeqWaves, wgb = g.owner(t1) / kSeqWaves;
+                seg_c0[p][kc * g.R + rb] = c;
+                seg_wg0[p][kc * g.R + rb] = wga;
+                c += wgb - wga + 1;
+
+            }
+            rb_nc[p][rb] = c - rb_c0[p][rb];
+        }
+        part_stride = std::max(part_stride, c);
+        // row block rb is finalised by the finalising workgroups in turn
+        {
+            std::vector<int> fwg;
+            for (int wg = 0; wg < grid; ++wg)
+                if (is_final_wg(wg, grid)) fwg.push_back(wg);
+            for (int rb = 0; rb < g.R; ++rb) rb_fin[p][rb] = fwg[rb % fwg.size()];
+        }
+        std::vector<int> nfin(grid, 0);
+        for (int rb = 0; rb < g.R; ++rb) fin_cap = std::max(fin_cap, ++nfin[rb_fin[p][rb]]);
+        for (int wg = 0; wg * kSeqWaves < g.W; ++wg) {
+            const int t0 = g.start(wg * kSeqWaves), t1 = g.start(std::min((wg + 1) * kSeqWaves, g.W)) - 1;
+            if (t1 >= t0) seg_cap = std::max(seg_cap, g.segment(t1) - g.segment(t0) + 1);
+        }
+    }
+    const int blk_bytes = (int)up(sizeof(SeqWgHead) + seg_cap * sizeof(SeqWgSeg) + fin_cap * sizeof(SeqFin), 16);
+    const int fin_off = (int)(sizeof(SeqWgHead) + seg_cap * sizeof(SeqWgSeg));
+    if ((int64_t)sizeof(SeqPhase) + blk_bytes > kMetaMaxBytes) return MBQ_ERR_SHAPE;
+
+    // ---- LDS: activations, partial slots, two metadata slots
     const int q_stride = (int)up(q_span, 16);
-    const int64_t lds = M * q_stride + (int64_t)kSeqWaves * slots * M * 64 * 4;
+    const int64_t meta_bytes = up(sizeof(SeqPhase) + blk_bytes, 16);
+    const int64_t lds = M * q_stride + (int64_t)kSeqWaves * slots * M * 64 * 4 + 2 * meta_bytes;
     if (lds > 150 * 1024) return MBQ_ERR_SHAPE;
 
     // ---- workspace layout
@@ -221,21 +282,15 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     const int64_t off_stats = off_dummy + 8192;
     const int64_t off_xt = up(off_stats + n_rec * kStatRecBytes, 256);
     const int64_t off_part = up(off_xt + n_xt * 8, 256);
-    const int64_t off_plan = up(off_part + max_seg * parts * M * 64 * 8, 256);
-    const int64_t off_ext = up(off_plan + (int64_t)sizeof(SeqPlan), 64);
+    const int64_t off_plan = up(off_part + 2 * (int64_t)part_stride * M * 64 * 8, 256);
+    // the counters sit inside the plan blob, so preparing a plan clears them
+    const int64_t off_cnt = up(off_plan + (int64_t)sizeof(SeqPlan), 64);
+    const int64_t off_ext = up(off_cnt + 4 * (int64_t)(n_ph + 1), 64);
     const int64_t off_phases = up(off_ext + (int64_t)ext.size() * sizeof(SeqExt), 64);
-    const int64_t off_ops = up(off_phases + (int64_t)n_ph * sizeof(SeqPhase), 64);
-    const int64_t off_wtab = up(off_ops + (int64_t)n_ops * sizeof(SeqOp), 64);
+    const int64_t off_wtab = up(off_phases + (int64_t)n_ph * sizeof(SeqPhase), 64);
     const int64_t off_runs = up(off_wtab + (int64_t)waves * sizeof(SeqWave), 64);
-    // per-phase tables: wave_start, wave_seg0, seg_owner, wg_k (int32)
-    std::vector<int64_t> off_tab(n_ph);
-    int64_t tab = up(off_runs + n_runs * (int64_t)sizeof(SeqRun), 64);
-    for (int p = 0; p < n_ph; ++p) {
-        off_tab[p] = tab;
-        const int64_t ints = (geo[p].W + 1) + geo[p].W + 4LL * geo[p].nkc * geo[p].R + 6LL * grid;
-        tab = up(tab + 4 * ints, 64);
-    }
-    const int64_t total = up(tab, 256);
+    const int64_t off_blocks = up(off_runs + n_runs * (int64_t)sizeof(SeqRun), 64);
+    const int64_t total = up(off_blocks + (int64_t)n_ph * grid * blk_bytes, 256);
     if (!out) return total;
 
     out->ws_bytes = total;
@@ -248,18 +303,20 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
 
     uint8_t *blob = out->blob.data();
     auto dev = [&](int64_t off) { return ws + off; };
+    auto put = [&](int64_t off, const void *src, size_t n) { memcpy(blob + (off - off_plan), src, n); };
     SeqPlan plan;
     memset(&plan, 0, sizeof(plan));
     plan.magic = kPlanMagic;
     plan.n_phases = n_ph;
-    plan.n_ops = n_ops;
     plan.n_ext = (int)ext.size();
     plan.n_ext_rb = ext_rb;
     plan.waves = waves;
+    plan.grid = grid;
     plan.slots = slots;
-    plan.parts = parts;
     plan.q_stride = q_stride;
-    plan.ops = reinterpret_cast<const SeqOp *>(dev(off_ops));
+    plan.blk_bytes = blk_bytes;
+    plan.seg_cap = seg_cap;
+    plan.part_stride = part_stride;
     plan.phases = reinterpret_cast<const SeqPhase *>(dev(off_phases));
     plan.ext = reinterpret_cast<const SeqExt *>(dev(off_ext));
     plan.err = reinterpret_cast<uint32_t *>(dev(off_err));
@@ -268,22 +325,9 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     plan.dummy = dev(off_dummy);
     plan.runs = reinterpret_cast<const SeqRun *>(dev(off_runs));
     plan.wtab = reinterpret_cast<const SeqWave *>(dev(off_wtab));
-    memcpy(blob, &plan, sizeof(plan));
-    {
-        int64_t r0 = 0;
-        for (int w = 0; w < waves; ++w) {
-            SeqWave sw;
-            sw.run_begin = (int32_t)r0;
-            sw.run_count = (int32_t)wruns[w].size();
-            sw.tiles = wtiles[w];
-            sw.pad = 0;
-            memcpy(blob + (off_wtab - off_plan) + w * sizeof(SeqWave), &sw, sizeof(sw));
-            if (!wruns[w].empty())
-                memcpy(blob + (off_runs - off_plan) + r0 * sizeof(SeqRun), wruns[w].data(),
-                       wruns[w].size() * sizeof(SeqRun));
-            r0 += (int64_t)wruns[w].size();
-        }
-    }
+    plan.blocks = dev(off_blocks);
+    plan.counters = reinterpret_cast<uint32_t *>(dev(off_cnt));
+    put(off_plan, &plan, sizeof(plan));
     for (size_t j = 0; j < ext.size(); ++j) {
         SeqExt e;
         memset(&e, 0, sizeof(e));
@@ -293,111 +337,104 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
         e.rec = ext[j].rec;
         e.n_rb = ext[j].n_rb;
         e.rb_first = ext[j].rb_first;
-        memcpy(blob + (off_ext - off_plan) + j * sizeof(SeqExt), &e, sizeof(e));
+        put(off_ext + j * sizeof(SeqExt), &e, sizeof(e));
     }
+    {
+        int64_t r0 = 0;
+        for (int w = 0; w < waves; ++w) {
+            SeqWave sw;
+            sw.run_begin = (int32_t)r0;
+            sw.run_count = (int32_t)wruns[w].size();
+            sw.tiles = wtiles[w];
+            sw.pad = 0;
+            put(off_wtab + w * sizeof(SeqWave), &sw, sizeof(sw));
+            if (!wruns[w].empty()) put(off_runs + r0 * sizeof(SeqRun), wruns[w].data(), wruns[w].size() * sizeof(SeqRun));
+            r0 += (int64_t)wruns[w].size();
+        }
+    }
+    uint32_t *cnt_dev = reinterpret_cast<uint32_t *>(dev(off_cnt));
+    uint64_t *xt_dev = reinterpret_cast<uint64_t *>(dev(off_xt));
     for (int p = 0; p < n_ph; ++p) {
         const mbq_op &o0 = ops[ph[p].first];
+        const PhaseGeom &g = geo[p];
         SeqPhase s;
         memset(&s, 0, sizeof(s));
         s.in = reinterpret_cast<const uint32_t *>(bufs[o0.in_buf]);
         s.in_stride2 = (int32_t)(widths[o0.in_buf] / 2);
         s.K = (int32_t)o0.K;
-        s.G = geo[p].G;
-        s.nkc = geo[p].nkc;
         s.prologue = o0.prologue;
-        s.op_first = ph[p].first;
-        s.op_count = ph[p].count;
-        s.R = geo[p].R;
-        s.W = geo[p].W;
-        s.T = geo[p].T;
         s.in_nrec = (int32_t)((o0.K + 63) / 64);
         if (in_prod[p] >= 0) {
             s.in_phase = phase_of[in_prod[p]];
             s.in_rec = op_rec[in_prod[p]];
-            s.in_xt = reinterpret_cast<const uint64_t *>(dev(off_xt)) + op_xt[in_prod[p]];
+            s.in_xt = xt_dev + op_xt[in_prod[p]];
         } else {
             s.in_xt = nullptr;
             s.in_phase = -1;
             s.in_rec = ext[in_ext[p]].rec;
         }
-        {
-            const PhaseGeom &g = geo[p];
-            int32_t *t = reinterpret_cast<int32_t *>(blob + (off_tab[p] - off_plan));
-            int32_t *t_start = t, *t_seg0 = t + (g.W + 1), *t_own = t_seg0 + g.W, *t_wgk = t_own + 2 * g.nkc * g.R;
-            int32_t *t_wgseg = t_wgk + 2 * grid;
-            int32_t *t_segwg = t_wgseg + 2 * grid;
-            int32_t *t_fin = t_segwg + 2 * g.nkc * g.R;
-            for (int w = 0; w <= g.W; ++w) t_start[w] = g.start(w);
-            for (int w = 0; w < g.W; ++w) t_seg0[w] = g.segment(g.start(w));
-            for (int kc = 0; kc < g.nkc; ++kc)
-                for (int rb = 0; rb < g.R; ++rb) {
-                    const int t0 = kc * g.R * kChunkGroups + rb * g.chunk_len(kc);
-                    const int t1 = t0 + g.chunk_len(kc) - 1;
-                    t_own[2 * (kc * g.R + rb)] = g.owner(t0);
-                    t_own[2 * (kc * g.R + rb) + 1] = g.owner(t1);
-                }
-            for (int wg = 0; wg < grid; ++wg) {
-                int lo = 0, hi = 0;
-                if (wg * kSeqWaves < g.W) {
-                    const int w1 = (wg + 1) * kSeqWaves < g.W ? (wg + 1) * kSeqWaves : g.W;
-                    const int t0 = g.start(wg * kSeqWaves), t1 = g.start(w1) - 1;
-                    if (t1 >= t0) {
-                        int kc0, kc1, rb;
-                        g.decode(t0, kc0, rb);
-                        g.decode(t1, kc1, rb);
-                        lo = kc0 * kChunkGroups * kGroup;
-                        const int64_t h = (int64_t)(kc1 + 1) * kChunkGroups * kGroup;
-                        hi = (int)(h < o0.K ? h : o0.K);
+        s.wait_n = p >= 2 ? geo[p - 2].R : 0;
+        s.wait_count = p >= 2 ? cnt_dev + (p - 2) : nullptr;
+        s.fin_count = cnt_dev + p;
+        put(off_phases + p * sizeof(SeqPhase), &s, sizeof(s));
+
+        // per-workgroup blocks
+        std::vector<std::vector<int>> fins(grid);
+        for (int rb = 0; rb < g.R; ++rb) fins[rb_fin[p][rb]].push_back(rb);
+        for (int wg = 0; wg < grid; ++wg) {
+            std::vector<uint8_t> blk(blk_bytes, 0);
+            SeqWgHead h;
+            memset(&h, 0, sizeof(h));
+            const int w0 = wg * kSeqWaves, w1 = std::min(w0 + kSeqWaves, g.W);   // waves [w0, w1)
+            for (int j = 0; j < kSeqWaves; ++j)
+                h.tiles[j] = w0 + j < g.W ? g.start(w0 + j + 1) - g.start(w0 + j) : 0;
+            if (w0 < g.W && g.start(w1) > g.start(w0)) {
+                const int t0 = g.start(w0), t1 = g.start(w1) - 1;
+                int kc0, kc1, rb;
+                g.decode(t0, kc0, rb);
+                g.decode(t1, kc1, rb);
+                h.k_lo = kc0 * kChunkGroups * kGroup;
+                h.k_hi = (int)std::min<int64_t>((int64_t)(kc1 + 1) * kChunkGroups * kGroup, o0.K);
+                const int s0 = g.segment(t0), s1 = g.segment(t1);
+                for (int sg = s0; sg <= s1; ++sg) {
+                    SeqWgSeg e;
+                    e.cidx = seg_c0[p][sg] + (wg - seg_wg0[p][sg]);
+                    const int kc = sg / g.R, srb = sg % g.R;
+                    const int ts0 = kc * g.R * kChunkGroups + srb * g.chunk_len(kc);
+                    const int ts1 = ts0 + g.chunk_len(kc) - 1;
+                    for (int j = 0; j < kSeqWaves; ++j) {
+                        const int w = w0 + j;
+                        e.slot[j] = 0xFF;
+                        if (w < w1 && g.start(w) <= ts1 && g.start(w + 1) > ts0)
+                            e.slot[j] = (uint8_t)(sg - g.segment(g.start(w)));
                     }
-                }
-                t_wgk[2 * wg] = lo;
-                t_wgk[2 * wg + 1] = hi;
-            }
-            for (int wg = 0; wg < grid; ++wg) {
-                t_wgseg[2 * wg] = 0;
-                t_wgseg[2 * wg + 1] = -1;
-                t_fin[2 * wg] = 0;
-                t_fin[2 * wg + 1] = 0;
-                if (wg * kSeqWaves < g.W) {
-                    const int w1 = (wg + 1) * kSeqWaves < g.W ? (wg + 1) * kSeqWaves : g.W;
-                    const int t0 = g.start(wg * kSeqWaves), t1 = g.start(w1) - 1;
-                    if (t1 >= t0) {
-                        t_wgseg[2 * wg] = g.segment(t0);
-                        t_wgseg[2 * wg + 1] = g.segment(t1);
-                    }
+                    memcpy(blk.data() + sizeof(SeqWgHead) + h.n_seg * sizeof(SeqWgSeg), &e, sizeof(e));
+                    h.n_seg++;
                 }
             }
-            for (int sg = 0; sg < g.nkc * g.R; ++sg) {
-                t_segwg[2 * sg] = t_own[2 * sg] / kSeqWaves;
-                t_segwg[2 * sg + 1] = t_own[2 * sg + 1] / kSeqWaves;
+            for (int rb : fins[wg]) {
+                int op = ph[p].first;
+                while (op + 1 < ph[p].first + ph[p].count && rb >= rb_base[p][op + 1 - ph[p].first]) ++op;
+                const int rbl = rb - rb_base[p][op - ph[p].first];
+                const int64_t N = ops[op].N;
+                SeqFin f;
+                memset(&f, 0, sizeof(f));
+                f.out = reinterpret_cast<uint32_t *>(bufs[ops[op].out_buf]) + rbl * 32;
+                f.xt = op_xt[op] >= 0 ? xt_dev + op_xt[op] + rbl * 32 : nullptr;
+                f.stats = stats_cols[op] > 0
+                              ? reinterpret_cast<uint64_t *>(dev(off_stats + (op_rec[op] + rbl) * kStatRecBytes))
+                              : nullptr;
+                f.row_words = (int32_t)(N / 2);
+                f.rows = (int32_t)std::min<int64_t>(64, N - (int64_t)rbl * 64);
+                f.stat_rows = (int32_t)std::max<int64_t>(
+                    0, std::min<int64_t>(f.rows, std::min<int64_t>(N, stats_cols[op]) - (int64_t)rbl * 64));
+                f.c0 = rb_c0[p][rb];
+                f.nc = rb_nc[p][rb];
+                memcpy(blk.data() + fin_off + h.n_fin * sizeof(SeqFin), &f, sizeof(f));
+                h.n_fin++;
             }
-            for (int rb = 0; rb < g.R; ++rb) {    // finalising workgroups are non-decreasing in rb
-                const int o = t_segwg[2 * ((g.nkc - 1) * g.R + rb) + 1];
-                if (t_fin[2 * o + 1] == 0) t_fin[2 * o] = rb;
-                t_fin[2 * o + 1]++;
-            }
-            const int32_t *dt = reinterpret_cast<const int32_t *>(dev(off_tab[p]));
-            s.wave_start = dt;
-            s.wave_seg0 = dt + (g.W + 1);
-            s.seg_owner = dt + (g.W + 1) + g.W;
-            s.wg_k = dt + (g.W + 1) + g.W + 2 * g.nkc * g.R;
-            s.wg_seg = s.wg_k + 2 * grid;
-            s.seg_wg = s.wg_seg + 2 * grid;
-            s.wg_fin = s.seg_wg + 2 * g.nkc * g.R;
-        }
-        memcpy(blob + (off_phases - off_plan) + p * sizeof(SeqPhase), &s, sizeof(s));
-        for (int i = ph[p].first; i < ph[p].first + ph[p].count; ++i) {
-            SeqOp d;
-            memset(&d, 0, sizeof(d));
-            d.packed = reinterpret_cast<const uint8_t *>(ops[i].packed);
-            d.out = reinterpret_cast<uint32_t *>(bufs[ops[i].out_buf]);
-            d.N = (int32_t)ops[i].N;
-            d.n_rb = (int32_t)row_blocks(ops[i].N);
-            d.rb_base = rb_base[p][i - ph[p].first];
-            d.stats_cols = stats_cols[i];
-            d.stats_rec = op_rec[i];
-            d.xt = op_xt[i] >= 0 ? reinterpret_cast<uint64_t *>(dev(off_xt)) + op_xt[i] : nullptr;
-            memcpy(blob + (off_ops - off_plan) + i * sizeof(SeqOp), &d, sizeof(d));
+            memcpy(blk.data(), &h, sizeof(h));
+            put(off_blocks + ((int64_t)p * grid + wg) * blk_bytes, blk.data(), blk_bytes);
         }
     }
     return total;
