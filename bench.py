@@ -85,8 +85,37 @@ def time_sequence(mbq, dev_ops, widths, M, steps, warmup, fused=True):
                 event_ms_best=float(per.min()), event_ms_mean=float(per.mean()))
 
 
-def cpu_baseline(set_name, bits, n_layers, budget_s=12.0):
-    """The oracle on the host cores, layer by layer until about budget_s of work."""
+KERNEL_SOURCES = ["seq.hip", "seqplan.hip", "mbq_seq.h", "mbq_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "seq_kernel_traffic.json")
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "memory_bound_quantised_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the committed counter runs (FETCH_SIZE + WRITE_SIZE, each
+    scaled by what the counter reads for a copy kernel of known size), or None when there
+    is none for this workload or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = rec.get("workloads", {}).get(key)
+    if not e or rec.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    return e["fetch_bytes_per_launch"] + e["write_bytes_per_launch"]
+
+
+def cpu_baseline(set_name, bits, n_layers, budget_s=10.0):
+    """The oracle on the host cores: the same M=1 walk, layer after layer (starting over after
+    the last layer), until about budget_s seconds of oracle time have been spent."""
     import oracle
     shapes_fn, _ = synth.WEIGHT_SETS[set_name]
     ops, widths = synth.layer_program(shapes_fn, n_layers)
@@ -95,21 +124,24 @@ def cpu_baseline(set_name, bits, n_layers, budget_s=12.0):
     bufs[0] = synth.activations(M, widths[0])
     per_layer = len(shapes_fn())
     spent, done_bytes, layers = 0.0, 0, 0
-    for layer in range(n_layers):
+    mats = {}
+    while spent < budget_s:
+        layer = layers % n_layers
         lops = ops[layer * per_layer:(layer + 1) * per_layer]
-        mats = {o["matrix"]: synth.weights(bits, o["N"], o["K"], seed=1 + o["matrix"]) for o in lops}
+        for o in lops:
+            if o["matrix"] not in mats:
+                mats[o["matrix"]] = synth.weights(bits, o["N"], o["K"], seed=1 + o["matrix"])
         t0 = time.perf_counter()
         oracle.layer_sequence(bits, lops, bufs, lambda i: mats[i])
         spent += time.perf_counter() - t0
         done_bytes += synth.weight_bytes(bits, [(o["name"], o["K"], o["N"]) for o in lops])
         layers += 1
-        if spent >= budget_s:
-            break
     gbs = done_bytes / spent / 1e9
+    step_bytes = synth.weight_bytes(bits, [(o["name"], o["K"], o["N"]) for o in ops])
     return dict(value=round(gbs, 4), unit="GB/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"first {layers} of {n_layers} layers of the same walk at M=1 "
-                       f"({done_bytes / 1e9:.3f} GB of weights, {spent:.1f} s), scaled to GB/s; "
-                       f"equivalent {gbs * 1e9 / synth.weight_bytes(bits, [(o['name'], o['K'], o['N']) for o in ops]):.4f} steps/s")
+                sample=f"{layers} layers of the {n_layers}-layer walk at M=1 ({layers / n_layers:.1f} passes, "
+                       f"{done_bytes / 1e9:.3f} GB of weights, {spent:.1f} s of oracle time), scaled to GB/s; "
+                       f"equivalent {gbs * 1e9 / step_bytes:.4f} steps/s")
 
 
 def main():
@@ -124,6 +156,9 @@ def main():
     ap.add_argument("--extra-m", type=int, nargs="*", default=[3])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--unfused", action="store_true", help="also time the one-launch-per-op walk")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device-to-device three times (a plain copy kernel of known "
+                         "size, to calibrate hardware byte counters against)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -135,6 +170,15 @@ def main():
     mbq.lib()   # fails loudly if the HIP library is not built
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+
+    if args.calib_copy > 0:
+        src = torch.ones(args.calib_copy << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calib_copy} MiB x 3")
+        del src, dst
 
     n_layers = args.layers or synth.WEIGHT_SETS[args.set][1]
     shapes = synth.weight_set(args.set, n_layers)
@@ -191,7 +235,8 @@ def main():
     # recorded on the stream it is launched on.
     out["roofline"] = {"bound": "hbm", "kernel": "seq_kernel (fused decode-step walk, 1 launch per step)",
                        "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                       "frac": round(gbs / HBM_PEAK_GBS, 4),
+                       "traffic": measured_traffic(f"{args.set}/w{args.bits}/m{args.m}/l{n_layers}"),
                        "bytes_per_launch": wbytes, "launch_ms": round(main_r["event_ms_median"], 4)}
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample")
