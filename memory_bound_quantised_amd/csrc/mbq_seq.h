@@ -16,7 +16,7 @@ constexpr int kSeqThreads = 64 * kSeqWaves;
 // the finalisers (whose memory queues are then empty) run the phase hand-over.
 __host__ __device__ inline bool is_final_wg(int wg, int grid) { return grid == 1 || (wg & 1) != 0; }
 constexpr int kChunkGroups = 8;                // k groups per k chunk (1024 k)
-constexpr int kStatRecBytes = 128;             // one per (producer op, row block)
+constexpr int kCounterStride = 32;             // u32 words between phase counters (one 128-B line each)
 constexpr int kMaxPhases = 1000;               // < 2^kRunPhaseBits
 constexpr int kMetaMaxBytes = 4096;           // phase record + workgroup block, per LDS slot
 constexpr uint64_t kPlanMagic = 0x6d62712d73657132ull;  // "mbq-seq2"
@@ -27,7 +27,9 @@ constexpr uint64_t kPlanMagic = 0x6d62712d73657132ull;  // "mbq-seq2"
 //
 // Stats record of one row block of an op's output (rows n < stats_cols), for
 // activation row m: word 3m = max|y| bits, 3m+1 / 3m+2 = low / high half of
-// the fp64 sum of y^2; each word's high half is the tag.
+// the fp64 sum of y^2; each word's high half is the tag.  The records are
+// stored word-major (word c of record r at stats[c * stat_stride + r]) so that
+// a wave reading 64 consecutive records fetches contiguous memory.
 
 struct SeqPhase {            // 64 bytes
     const uint32_t *in;      // bf16 pairs of the input rows (inputs written before the launch)
@@ -76,7 +78,7 @@ struct SeqWgSeg {            // a segment the workgroup's tiles touch
 struct SeqFin {              // a row block the workgroup finalises (48 bytes)
     uint32_t *out;           // its first bf16 pair in output row 0
     uint64_t *xt;            // same in the tagged copy, or null
-    uint64_t *stats;         // its stats record, or null
+    uint64_t *stats;         // word 0 of its stats record, or null
     int32_t row_words;       // output row stride in pairs (N / 2)
     int32_t rows;            // valid rows (<= 64, even)
     int32_t stat_rows;       // rows feeding the stats (0 .. rows)
@@ -104,14 +106,15 @@ struct SeqPlan {
     const SeqPhase *phases;
     const SeqExt *ext;
     uint32_t *err;           // nonzero after a wait gave up
-    uint8_t *stats;          // stats records
+    uint64_t *stats;         // stats records, word-major
+    int64_t stat_stride;     // records (words per stats word index)
     uint64_t *partials;      // [phase & 1][contribution][lane][m]: value bits | tag << 32
     const uint8_t *dummy;    // readable tile-sized area for loads past a stream's end
     const SeqRun *runs;      // every wave's runs, wave after wave, each in walk order
     const SeqWave *wtab;     // [waves]
     const uint8_t *blocks;   // [phase][workgroup] blocks of blk_bytes
-    uint32_t *counters;      // [n_phases] finalised row blocks, then the exit count;
-                             // the last workgroup to exit clears them
+    uint32_t *counters;      // [n_phases] finalised row blocks, then the exit count, each
+                             // kCounterStride words apart; the last workgroup to exit clears them
 };
 
 }  // namespace mbq

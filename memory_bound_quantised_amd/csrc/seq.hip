@@ -131,18 +131,20 @@ __device__ __forceinline__ bool gave_up(const SeqPlan *P, int64_t &spins) {
 // True if any lane of the wave passes true.
 __device__ __forceinline__ bool wave_any(bool b) { return __builtin_amdgcn_ballot_w64(b) != 0; }
 
-// Publish one stats record from per-lane values (lanes past the stats rows pass 0).
+// Publish one stats record (word 0 at rec, word c at rec + c * stride) from
+// per-lane values (lanes past the stats rows pass 0).
 template <int M>
-__device__ __forceinline__ void publish_stats(uint64_t *rec, const float (&v)[M], uint32_t tag, int lane) {
+__device__ __forceinline__ void publish_stats(uint64_t *rec, int64_t stride, const float (&v)[M], uint32_t tag,
+                                              int lane) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const double ss = wave_sum63((double)v[m] * (double)v[m]);
         const float am = wave_max63(fabsf(v[m]));
         if (lane == 63) {
             const uint64_t bits = (uint64_t)__double_as_longlong(ss);
-            store_shared(rec + 3 * m, tagged(__float_as_uint(am), tag));
-            store_shared(rec + 3 * m + 1, tagged((uint32_t)bits, tag));
-            store_shared(rec + 3 * m + 2, tagged((uint32_t)(bits >> 32), tag));
+            store_shared(rec + (3 * m) * stride, tagged(__float_as_uint(am), tag));
+            store_shared(rec + (3 * m + 1) * stride, tagged((uint32_t)bits, tag));
+            store_shared(rec + (3 * m + 2) * stride, tagged((uint32_t)(bits >> 32), tag));
         }
     }
 }
@@ -153,7 +155,8 @@ template <int M>
 __device__ void external_stats(const SeqPlan *P, int w, int waves, int lane, uint32_t gen) {
     const int n_ext_rb = cload(&P->n_ext_rb), n_ext = cload(&P->n_ext);
     const SeqExt *ext = cload(&P->ext);
-    uint8_t *stats = cload(&P->stats);
+    uint64_t *stats = cload(&P->stats);
+    const int64_t stride = cload(&P->stat_stride);
     for (int b = w; b < n_ext_rb; b += waves) {
         int e = 0;
         while (e + 1 < n_ext && b >= cload(ext, e + 1).rb_first) ++e;
@@ -169,8 +172,7 @@ __device__ void external_stats(const SeqPlan *P, int w, int waves, int lane, uin
                 v[m] = bf16_bits_to_f32((word >> (16 * (col & 1))) & 0xFFFFu);
             }
         }
-        publish_stats<M>(reinterpret_cast<uint64_t *>(stats + (x.rec + rb) * kStatRecBytes), v, make_tag(gen, -1),
-                         lane);
+        publish_stats<M>(stats + x.rec + rb, stride, v, make_tag(gen, -1), lane);
     }
 }
 
@@ -194,11 +196,15 @@ __device__ __forceinline__ float quant_code(float t, float s, float rinv, bool r
 // Quantise columns [k_lo, k_hi) of the phase input into LDS (int8, row stride
 // q_stride), after the optional weightless RMSNorm.  Row statistics come from
 // the producer's stats records, reduced in a fixed order so that every
-// workgroup derives bit-identical scales.  Wave 0 waits for the statistics
-// (and for the partial area of this phase's parity to be free; the scales
-// also serve the row blocks the workgroup finalises) while every
-// wave waits for its share of the input words; the next phase's metadata is
-// fetched meanwhile.
+// workgroup derives bit-identical scales.  Wave 0 alone waits, first for the
+// partial area of this phase's parity to be free, then for the statistics
+// (the scales also serve the row blocks the workgroup finalises); the other
+// waves sleep in the barrier.  Only then does every wave read its share of
+// the input words: the producer wrote them before the statistics, so they are
+// all but always current by then.  Keeping the waiting to one wave with
+// contiguous reads keeps the polling traffic small: every workgroup polls at
+// once, and a flood of polls slows every other memory request.  The next
+// phase's metadata is fetched meanwhile.
 template <int M>
 __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int p, uint32_t gen, int wg,
                                             float (*s_sh)[4], float (*r_sh)[4]) {
@@ -214,23 +220,6 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
     const bool tagged_in = ph.in_xt != nullptr;
     const bool has = h.k_hi > h.k_lo;
     const bool need_scale = has || h.n_fin > 0;   // finalising rescales by the input scale
-    const uint64_t *xsrc = ph.in_xt + (h.k_lo >> 1);
-
-    // first batch of input words: they fly while the statistics are awaited
-    uint64_t xw[kXBatch][M];
-#pragma unroll
-    for (int u = 0; u < kXBatch; ++u)
-#pragma unroll
-        for (int m = 0; m < M; ++m) xw[u][m] = 0;
-    if (has && tagged_in) {
-#pragma unroll
-        for (int u = 0; u < kXBatch; ++u) {
-            const int j = threadIdx.x + u * kSeqThreads;
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-                if (j < words) xw[u][m] = load_shared(xsrc + (int64_t)m * ph.in_stride2 + j);
-        }
-    }
 
     if (wave == 0) {
         // the partial area of this phase's parity is free once the phase two back is finalised
@@ -247,18 +236,16 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
                 ss[m] = 0.0;
                 am[m] = 0.0f;
             }
-            const uint8_t *stats = cload(&P->stats);
+            const int64_t stride = cload(&P->stat_stride);
+            const uint64_t *stats = cload(&P->stats) + ph.in_rec;
             constexpr int kStatBatch = stat_batch<M>();
             for (int base = 0; base < ph.in_nrec; base += 64 * kStatBatch) {
                 uint64_t v[kStatBatch][3 * M];
-                const uint64_t *rp[kStatBatch];
 #pragma unroll
                 for (int u = 0; u < kStatBatch; ++u) {
                     const int i = base + lane + 64 * u;
-                    rp[u] = reinterpret_cast<const uint64_t *>(stats + (ph.in_rec + (i < ph.in_nrec ? i : 0)) *
-                                                                           kStatRecBytes);
 #pragma unroll
-                    for (int c = 0; c < 3 * M; ++c) v[u][c] = load_shared(rp[u] + c);
+                    for (int c = 0; c < 3 * M; ++c) v[u][c] = i < ph.in_nrec ? load_shared(stats + c * stride + i) : 0;
                 }
                 int64_t spins = 0;
                 for (;;) {
@@ -270,11 +257,12 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
                             stale |= base + lane + 64 * u < ph.in_nrec && tag_of(v[u][c]) != want;
                     if (!wave_any(stale) || gave_up(P, spins)) break;
 #pragma unroll
-                    for (int u = 0; u < kStatBatch; ++u)
+                    for (int u = 0; u < kStatBatch; ++u) {
+                        const int i = base + lane + 64 * u;
 #pragma unroll
                         for (int c = 0; c < 3 * M; ++c)
-                            if (base + lane + 64 * u < ph.in_nrec && tag_of(v[u][c]) != want)
-                                v[u][c] = load_shared(rp[u] + c);
+                            if (i < ph.in_nrec && tag_of(v[u][c]) != want) v[u][c] = load_shared(stats + c * stride + i);
+                    }
                 }
 #pragma unroll
                 for (int u = 0; u < kStatBatch; ++u) {
@@ -307,16 +295,28 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
             }
         }
     }
+    __syncthreads();   // the scales from wave 0
     float s[M], r[M], rinv[M];
     bool rinv_ok[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        s[m] = s_sh[p & 1][m];
+        r[m] = r_sh[p & 1][m];
+        rinv[m] = 1.0f / s[m];
+        rinv_ok[m] = fabsf(rinv[m]) < INFINITY;
+    }
+    const uint64_t *xsrc = ph.in_xt + (h.k_lo >> 1);
     for (int j0 = 0; has && j0 < words; j0 += kXBatch * kSeqThreads) {
-        if (j0 > 0 && tagged_in) {
+        uint64_t xw[kXBatch][M];
 #pragma unroll
-            for (int u = 0; u < kXBatch; ++u) {
-                const int j = j0 + threadIdx.x + u * kSeqThreads;
+        for (int u = 0; u < kXBatch; ++u) {
+            const int j = j0 + threadIdx.x + u * kSeqThreads;
 #pragma unroll
-                for (int m = 0; m < M; ++m)
-                    if (j < words) xw[u][m] = load_shared(xsrc + (int64_t)m * ph.in_stride2 + j);
+            for (int m = 0; m < M; ++m) {
+                xw[u][m] = 0;
+                if (j < words)
+                    xw[u][m] = tagged_in ? load_shared(xsrc + (int64_t)m * ph.in_stride2 + j)
+                                         : (uint64_t)*gptr(ph.in + (int64_t)m * ph.in_stride2 + (h.k_lo >> 1) + j);
             }
         }
         if (tagged_in) {
@@ -339,24 +339,13 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
                 }
             }
         }
-        if (j0 == 0) {
-            __syncthreads();   // the scales from wave 0
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                s[m] = s_sh[p & 1][m];
-                r[m] = r_sh[p & 1][m];
-                rinv[m] = 1.0f / s[m];
-                rinv_ok[m] = fabsf(rinv[m]) < INFINITY;
-            }
-        }
 #pragma unroll
         for (int u = 0; u < kXBatch; ++u) {
             const int j = j0 + threadIdx.x + u * kSeqThreads;
             if (j >= words) continue;
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                const uint32_t pair = tagged_in ? (uint32_t)xw[u][m]
-                                                : *gptr(ph.in + (int64_t)m * ph.in_stride2 + (h.k_lo >> 1) + j);
+                const uint32_t pair = (uint32_t)xw[u][m];
                 uint32_t packed = 0;
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
@@ -369,7 +358,6 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
             }
         }
     }
-    if (!has) __syncthreads();     // keep the barrier count equal for every workgroup shape
     store_meta(L, p + 1, pre);
     __syncthreads();
 }
@@ -381,7 +369,7 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
 // their tagged copy and its stats record, then count it as done.
 template <int BITS, int M>
 __device__ __forceinline__ void finalize_rb(const SeqPlan *P, const uint64_t *area, uint32_t tag, const SeqFin &f,
-                                            const float *s_act, uint32_t *fin_count, int lane) {
+                                            const float *s_act, uint32_t *fin_count, int64_t stat_stride, int lane) {
     using Lt = Layout<BITS>;
     float tot[M];
 #pragma unroll
@@ -434,7 +422,7 @@ __device__ __forceinline__ void finalize_rb(const SeqPlan *P, const uint64_t *ar
         }
         yv[m] = lane < f.stat_rows ? bf16_bits_to_f32(yb) : 0.0f;
     }
-    if (f.stats) publish_stats<M>(f.stats, yv, tag, lane);
+    if (f.stats) publish_stats<M>(f.stats, stat_stride, yv, tag, lane);
     if (lane == 0) counter_add(fin_count, 1u);   // its contributions have been read
 }
 
@@ -480,9 +468,10 @@ __device__ __forceinline__ void finalize_phase(const SeqPlan *P, const Lay &L, i
     const uint32_t tag = make_tag(gen, p);
     const uint64_t *area = cload(&P->partials) + (int64_t)(p & 1) * L.part_stride * 64 * M;
     uint32_t *fin_count = meta_phase(L, p)->fin_count;
+    const int64_t stat_stride = cload(&P->stat_stride);
     for (int i = j; i < h.n_fin; i += kSeqWaves) {
         const SeqFin f = meta_fin(L, p)[i];
-        finalize_rb<BITS, M>(P, area, tag, f, s_act, fin_count, lane);
+        finalize_rb<BITS, M>(P, area, tag, f, s_act, fin_count, stat_stride, lane);
     }
 }
 
@@ -697,8 +686,8 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const SeqPlan *__restr
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t *cnt = cload(&P->counters);
-        if (counter_add(cnt + L.n_phases, 1u) == (uint32_t)(L.grid - 1))
-            for (int i = 0; i <= L.n_phases; ++i) store_shared(cnt + i, 0u);
+        if (counter_add(cnt + (int64_t)L.n_phases * kCounterStride, 1u) == (uint32_t)(L.grid - 1))
+            for (int i = 0; i <= L.n_phases; ++i) store_shared(cnt + (int64_t)i * kCounterStride, 0u);
     }
 }
 

@@ -280,12 +280,12 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     const int64_t off_err = 0;
     const int64_t off_dummy = 256;
     const int64_t off_stats = off_dummy + 8192;
-    const int64_t off_xt = up(off_stats + n_rec * kStatRecBytes, 256);
+    const int64_t off_xt = up(off_stats + n_rec * 3 * M * 8, 256);
     const int64_t off_part = up(off_xt + n_xt * 8, 256);
     const int64_t off_plan = up(off_part + 2 * (int64_t)part_stride * M * 64 * 8, 256);
     // the counters sit inside the plan blob, so preparing a plan clears them
     const int64_t off_cnt = up(off_plan + (int64_t)sizeof(SeqPlan), 64);
-    const int64_t off_ext = up(off_cnt + 4 * (int64_t)(n_ph + 1), 64);
+    const int64_t off_ext = up(off_cnt + 4 * (int64_t)kCounterStride * (n_ph + 1), 64);
     const int64_t off_phases = up(off_ext + (int64_t)ext.size() * sizeof(SeqExt), 64);
     const int64_t off_wtab = up(off_phases + (int64_t)n_ph * sizeof(SeqPhase), 64);
     const int64_t off_runs = up(off_wtab + (int64_t)waves * sizeof(SeqWave), 64);
@@ -320,7 +320,8 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     plan.phases = reinterpret_cast<const SeqPhase *>(dev(off_phases));
     plan.ext = reinterpret_cast<const SeqExt *>(dev(off_ext));
     plan.err = reinterpret_cast<uint32_t *>(dev(off_err));
-    plan.stats = dev(off_stats);
+    plan.stats = reinterpret_cast<uint64_t *>(dev(off_stats));
+    plan.stat_stride = n_rec;
     plan.partials = reinterpret_cast<uint64_t *>(dev(off_part));
     plan.dummy = dev(off_dummy);
     plan.runs = reinterpret_cast<const SeqRun *>(dev(off_runs));
@@ -374,8 +375,8 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
             s.in_rec = ext[in_ext[p]].rec;
         }
         s.wait_n = p >= 2 ? geo[p - 2].R : 0;
-        s.wait_count = p >= 2 ? cnt_dev + (p - 2) : nullptr;
-        s.fin_count = cnt_dev + p;
+        s.wait_count = p >= 2 ? cnt_dev + (int64_t)(p - 2) * kCounterStride : nullptr;
+        s.fin_count = cnt_dev + (int64_t)p * kCounterStride;
         put(off_phases + p * sizeof(SeqPhase), &s, sizeof(s));
 
         // per-workgroup blocks
@@ -422,7 +423,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
                 f.out = reinterpret_cast<uint32_t *>(bufs[ops[op].out_buf]) + rbl * 32;
                 f.xt = op_xt[op] >= 0 ? xt_dev + op_xt[op] + rbl * 32 : nullptr;
                 f.stats = stats_cols[op] > 0
-                              ? reinterpret_cast<uint64_t *>(dev(off_stats + (op_rec[op] + rbl) * kStatRecBytes))
+                              ? reinterpret_cast<uint64_t *>(dev(off_stats + (op_rec[op] + rbl) * 8))
                               : nullptr;
                 f.row_words = (int32_t)(N / 2);
                 f.rows = (int32_t)std::min<int64_t>(64, N - (int64_t)rbl * 64);
