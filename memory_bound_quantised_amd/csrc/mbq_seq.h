@@ -17,6 +17,7 @@ constexpr int kSeqThreads = 64 * kSeqWaves;
 __host__ __device__ inline bool is_final_wg(int wg, int grid) { return grid == 1 || (wg & 1) != 0; }
 constexpr int kChunkGroups = 8;                // k groups per k chunk (1024 k)
 constexpr int kCounterStride = 32;             // u32 words between phase counters (one 128-B line each)
+constexpr int kStatReplicas = 8;               // copies of the stats records, one per XCD
 constexpr int kMaxPhases = 1000;               // < 2^kRunPhaseBits
 constexpr int kMetaMaxBytes = 4096;           // phase record + workgroup block, per LDS slot
 constexpr uint64_t kPlanMagic = 0x6d62712d73657132ull;  // "mbq-seq2"
@@ -29,7 +30,10 @@ constexpr uint64_t kPlanMagic = 0x6d62712d73657132ull;  // "mbq-seq2"
 // activation row m: word 3m = max|y| bits, 3m+1 / 3m+2 = low / high half of
 // the fp64 sum of y^2; each word's high half is the tag.  The records are
 // stored word-major (word c of record r at stats[c * stat_stride + r]) so that
-// a wave reading 64 consecutive records fetches contiguous memory.
+// a wave reading 64 consecutive records fetches contiguous memory, and in
+// kStatReplicas copies (copy k at stats + k * stat_rep): every workgroup polls
+// every record, and a workgroup reads the copy of its XCD (workgroup index
+// mod 8), so no line is polled by more than one eighth of the grid.
 
 struct SeqPhase {            // 64 bytes
     const uint32_t *in;      // bf16 pairs of the input rows (inputs written before the launch)
@@ -108,6 +112,7 @@ struct SeqPlan {
     uint32_t *err;           // nonzero after a wait gave up
     uint64_t *stats;         // stats records, word-major
     int64_t stat_stride;     // records (words per stats word index)
+    int64_t stat_rep;        // words per copy of the records
     uint64_t *partials;      // [phase & 1][contribution][lane][m]: value bits | tag << 32
     const uint8_t *dummy;    // readable tile-sized area for loads past a stream's end
     const SeqRun *runs;      // every wave's runs, wave after wave, each in walk order

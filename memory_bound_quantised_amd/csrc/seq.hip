@@ -131,20 +131,26 @@ __device__ __forceinline__ bool gave_up(const SeqPlan *P, int64_t &spins) {
 // True if any lane of the wave passes true.
 __device__ __forceinline__ bool wave_any(bool b) { return __builtin_amdgcn_ballot_w64(b) != 0; }
 
-// Publish one stats record (word 0 at rec, word c at rec + c * stride) from
-// per-lane values (lanes past the stats rows pass 0).
+// Publish one stats record (word 0 of copy 0 at rec, word c of copy k at
+// rec + k * rep + c * stride) from per-lane values (lanes past the stats rows
+// pass 0).  Lane 63 holds the reductions; lanes 0 .. kStatReplicas-1 write
+// one copy each.
 template <int M>
-__device__ __forceinline__ void publish_stats(uint64_t *rec, int64_t stride, const float (&v)[M], uint32_t tag,
-                                              int lane) {
+__device__ __forceinline__ void publish_stats(uint64_t *rec, int64_t stride, int64_t rep, const float (&v)[M],
+                                              uint32_t tag, int lane) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const double ss = wave_sum63((double)v[m] * (double)v[m]);
         const float am = wave_max63(fabsf(v[m]));
-        if (lane == 63) {
-            const uint64_t bits = (uint64_t)__double_as_longlong(ss);
-            store_shared(rec + (3 * m) * stride, tagged(__float_as_uint(am), tag));
-            store_shared(rec + (3 * m + 1) * stride, tagged((uint32_t)bits, tag));
-            store_shared(rec + (3 * m + 2) * stride, tagged((uint32_t)(bits >> 32), tag));
+        const uint64_t bits = (uint64_t)__double_as_longlong(ss);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bits, 63);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), 63);
+        const uint32_t amb = (uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(am), 63);
+        if (lane < kStatReplicas) {
+            uint64_t *d = rec + lane * rep;
+            store_shared(d + (3 * m) * stride, tagged(amb, tag));
+            store_shared(d + (3 * m + 1) * stride, tagged(lo, tag));
+            store_shared(d + (3 * m + 2) * stride, tagged(hi, tag));
         }
     }
 }
@@ -156,7 +162,7 @@ __device__ void external_stats(const SeqPlan *P, int w, int waves, int lane, uin
     const int n_ext_rb = cload(&P->n_ext_rb), n_ext = cload(&P->n_ext);
     const SeqExt *ext = cload(&P->ext);
     uint64_t *stats = cload(&P->stats);
-    const int64_t stride = cload(&P->stat_stride);
+    const int64_t stride = cload(&P->stat_stride), rep = cload(&P->stat_rep);
     for (int b = w; b < n_ext_rb; b += waves) {
         int e = 0;
         while (e + 1 < n_ext && b >= cload(ext, e + 1).rb_first) ++e;
@@ -172,7 +178,7 @@ __device__ void external_stats(const SeqPlan *P, int w, int waves, int lane, uin
                 v[m] = bf16_bits_to_f32((word >> (16 * (col & 1))) & 0xFFFFu);
             }
         }
-        publish_stats<M>(stats + x.rec + rb, stride, v, make_tag(gen, -1), lane);
+        publish_stats<M>(stats + x.rec + rb, stride, rep, v, make_tag(gen, -1), lane);
     }
 }
 
@@ -237,7 +243,7 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
                 am[m] = 0.0f;
             }
             const int64_t stride = cload(&P->stat_stride);
-            const uint64_t *stats = cload(&P->stats) + ph.in_rec;
+            const uint64_t *stats = cload(&P->stats) + (wg % kStatReplicas) * cload(&P->stat_rep) + ph.in_rec;
             constexpr int kStatBatch = stat_batch<M>();
             for (int base = 0; base < ph.in_nrec; base += 64 * kStatBatch) {
                 uint64_t v[kStatBatch][3 * M];
@@ -366,10 +372,10 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
 
 // Gather a row block's contributions (lane l's M tagged words of contribution
 // c at area + (c * 64 + l) * M) in their fixed order, write its bf16 outputs,
-// their tagged copy and its stats record, then count it as done.
+// their tagged copy and its stats record (the caller counts it as done).
 template <int BITS, int M>
 __device__ __forceinline__ void finalize_rb(const SeqPlan *P, const uint64_t *area, uint32_t tag, const SeqFin &f,
-                                            const float *s_act, uint32_t *fin_count, int64_t stat_stride, int lane) {
+                                            const float *s_act, int64_t stat_stride, int64_t stat_rep, int lane) {
     using Lt = Layout<BITS>;
     float tot[M];
 #pragma unroll
@@ -422,8 +428,7 @@ __device__ __forceinline__ void finalize_rb(const SeqPlan *P, const uint64_t *ar
         }
         yv[m] = lane < f.stat_rows ? bf16_bits_to_f32(yb) : 0.0f;
     }
-    if (f.stats) publish_stats<M>(f.stats, stat_stride, yv, tag, lane);
-    if (lane == 0) counter_add(fin_count, 1u);   // its contributions have been read
+    if (f.stats) publish_stats<M>(f.stats, stat_stride, stat_rep, yv, tag, lane);
 }
 
 // Workgroup-wide exit from phase p (every wave has parked its parts in LDS):
@@ -468,11 +473,15 @@ __device__ __forceinline__ void finalize_phase(const SeqPlan *P, const Lay &L, i
     const uint32_t tag = make_tag(gen, p);
     const uint64_t *area = cload(&P->partials) + (int64_t)(p & 1) * L.part_stride * 64 * M;
     uint32_t *fin_count = meta_phase(L, p)->fin_count;
-    const int64_t stat_stride = cload(&P->stat_stride);
+    const int64_t stat_stride = cload(&P->stat_stride), stat_rep = cload(&P->stat_rep);
+    uint32_t done = 0;
     for (int i = j; i < h.n_fin; i += kSeqWaves) {
         const SeqFin f = meta_fin(L, p)[i];
-        finalize_rb<BITS, M>(P, area, tag, f, s_act, fin_count, stat_stride, lane);
+        finalize_rb<BITS, M>(P, area, tag, f, s_act, stat_stride, stat_rep, lane);
+        ++done;
     }
+    // one count per wave: the row blocks whose contributions it has read
+    if (done > 0 && lane == 0) counter_add(fin_count, done);
 }
 
 // ---------------------------------------------------------------- the weight stream

@@ -280,7 +280,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     const int64_t off_err = 0;
     const int64_t off_dummy = 256;
     const int64_t off_stats = off_dummy + 8192;
-    const int64_t off_xt = up(off_stats + n_rec * 3 * M * 8, 256);
+    const int64_t off_xt = up(off_stats + (int64_t)kStatReplicas * n_rec * 3 * M * 8, 256);
     const int64_t off_part = up(off_xt + n_xt * 8, 256);
     const int64_t off_plan = up(off_part + 2 * (int64_t)part_stride * M * 64 * 8, 256);
     // the counters sit inside the plan blob, so preparing a plan clears them
@@ -322,6 +322,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     plan.err = reinterpret_cast<uint32_t *>(dev(off_err));
     plan.stats = reinterpret_cast<uint64_t *>(dev(off_stats));
     plan.stat_stride = n_rec;
+    plan.stat_rep = n_rec * 3 * M;
     plan.partials = reinterpret_cast<uint64_t *>(dev(off_part));
     plan.dummy = dev(off_dummy);
     plan.runs = reinterpret_cast<const SeqRun *>(dev(off_runs));
