@@ -591,11 +591,17 @@ __device__ __forceinline__ void compute(const Lay &L, int lane, Compute &c, floa
 
 // Start a phase's stream: ring slots [A, B) with the wave's tiles A..B-1 of
 // n that exist (the ring may be primed in two steps).
+// Issue the first min(n, B) - A tiles of a phase into the ring.  Paced
+// priming spaces the tiles ~0.2 us apart: the grid primes all at once when a
+// phase ends, and a burst of that size delays the hand-over's own requests.
 template <int BITS, int D, int A, int B>
-__device__ __forceinline__ void prime(Issue &is, int lane, int n, Slot<BITS> (&ring)[D]) {
+__device__ __forceinline__ void prime(Issue &is, int lane, int n, Slot<BITS> (&ring)[D], bool paced = false) {
 #pragma unroll
     for (int i = A; i < B; ++i)
-        if (i < n) issue<BITS>(is, lane, ring[i]);
+        if (i < n) {
+            issue<BITS>(is, lane, ring[i]);
+            if (paced) __builtin_amdgcn_s_sleep(8);
+        }
 }
 
 // One phase of the wave: n tiles through the ring, which was primed with the
@@ -680,13 +686,13 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const SeqPlan *__restr
         stream_phase<BITS, M, D>(L, is, lane, uniform(meta_head(L, p)->tiles[wi]), ring, facc, lp_w);
         leave_phase<M>(P, L, p, gen);
         // Finalisers hand the phase over while their memory queue is empty;
-        // the others start the next phase's weight stream at once, after a
-        // barrier that keeps any wave's loads from queueing ahead of another
-        // wave's partials.
+        // the others start the next phase's weight stream (wave 0 at once,
+        // the rest paced), after a barrier that keeps any wave's loads from
+        // queueing ahead of another wave's partials.
         if (finaliser) finalize_phase<BITS, M>(P, L, p, gen, s_sh[p & 1]);
         else __syncthreads();
         if (p + 1 == L.n_phases) break;
-        prime<BITS, D, 0, D>(is, lane, uniform(meta_head(L, p + 1)->tiles[wi]), ring);
+        prime<BITS, D, 0, D>(is, lane, uniform(meta_head(L, p + 1)->tiles[wi]), ring, wi != 0);
     }
 
     // The last workgroup to exit clears the counters for the next launch
