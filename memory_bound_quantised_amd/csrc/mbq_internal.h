@@ -198,6 +198,60 @@ __device__ __forceinline__ void dot_tile_w6(const v4i (&w)[6], Act act, int (&ac
         }
 }
 
+// ------------------------------------------------------------------ one tile on the matrix cores
+//
+// The same products through v_mfma_i32_16x16x64_i8 (16 x 16 int32 outputs, a
+// 64-deep int8 dot each).  Lane l supplies bytes b = 0..15 of k group
+// (l >> 4) for row l & 15 of A and column l & 15 of B; the product pairs A and
+// B bytes of the same lane group and byte, so any fixed map from (lane group,
+// byte) to k serves, provided A and B use the same one.  Here the lane's k
+// slice s = l >> 4 (32 k) is split into two halves h, one product each:
+//   B column n = l & 15 is weight row 4n + i of the tile (one product set per i),
+//   A row l & 15 is activation row m (rows >= M only feed unused outputs),
+// and output lane l holds D[4 * (l >> 4) + j][l & 15]: lanes 0..15 hold
+// activation rows j = 0..3 of weight row 4 * l + i.  Rows past M cost nothing
+// extra: a 16-row product is one instruction whatever M is.
+
+// The lane's unpacked weights (2^kAccShift * w) of row i, k half h (k = 32s +
+// 16h + 0..15, in order) as four int8x4 dwords.
+template <int BITS>
+__device__ __forceinline__ v4i unpack_half(const v4i (&w)[Layout<BITS>::kSlabs], int i, int h) {
+    if constexpr (BITS == 4) {
+        const uint32_t wd[4] = {(uint32_t)w[i].x, (uint32_t)w[i].y, (uint32_t)w[i].z, (uint32_t)w[i].w};
+        const uint32_t d0 = wd[2 * h], d1 = wd[2 * h + 1];
+        return v4i{(int)((d0 << 4) & 0xF0F0F0F0u), (int)(d0 & 0xF0F0F0F0u), (int)((d1 << 4) & 0xF0F0F0F0u),
+                   (int)(d1 & 0xF0F0F0F0u)};
+    } else {
+        uint32_t wd[24];
+#pragma unroll
+        for (int j = 0; j < 6; ++j) {
+            wd[4 * j + 0] = (uint32_t)w[j].x;
+            wd[4 * j + 1] = (uint32_t)w[j].y;
+            wd[4 * j + 2] = (uint32_t)w[j].z;
+            wd[4 * j + 3] = (uint32_t)w[j].w;
+        }
+        const uint32_t x0 = wd[6 * i + 3 * h], x1 = wd[6 * i + 3 * h + 1], x2 = wd[6 * i + 3 * h + 2];
+        const uint32_t m6 = 0xFCFCFCFCu;
+        return v4i{(int)(x0 & m6), (int)(x1 & m6), (int)(x2 & m6),
+                   (int)(((x0 << 6) & 0xC0C0C0C0u) | ((x1 << 4) & 0x30303030u) | ((x2 << 2) & 0x0C0C0C0Cu))};
+    }
+}
+
+// acc[i][j] (output lanes 0..15 only) = group sums of weight row 4 * lane + i
+// against activation row j; qa points at the lane's 32 activation bytes
+// (row (lane & 15) of the group's k slice lane >> 4).
+template <int BITS>
+__device__ __forceinline__ void mfma_tile(const v4i (&w)[Layout<BITS>::kSlabs], const int8_t *qa, v4i (&acc)[4]) {
+    const v4i a0 = *reinterpret_cast<const v4i *>(qa);
+    const v4i a1 = *reinterpret_cast<const v4i *>(qa + 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const v4i z = {0, 0, 0, 0};
+        acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, unpack_half<BITS>(w, i, 0), z, 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, unpack_half<BITS>(w, i, 1), acc[i], 0, 0, 0);
+    }
+}
+
 template <int BITS, int M, typename Act>
 __device__ __forceinline__ void dot_tile(const v4i (&w)[Layout<BITS>::kSlabs], Act act, int (&acc)[4][M]) {
     if constexpr (BITS == 4)

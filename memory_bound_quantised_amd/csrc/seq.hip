@@ -555,6 +555,27 @@ __device__ __forceinline__ void close_segment(int slot, float (&facc)[4][M], flo
     }
 }
 
+// Matrix-core products from this many activation rows on (a 16-row product
+// costs one instruction whatever M is; below it, v_dot4 is cheaper).
+#ifndef MBQ_MFMA_MIN_M
+#define MBQ_MFMA_MIN_M 2
+#endif
+template <int M>
+constexpr bool use_mfma() { return M >= MBQ_MFMA_MIN_M; }
+
+// The matrix-core form of close_segment: lanes 0..15 hold complete sums of
+// rows 4 * lane + i.
+template <int M>
+__device__ __forceinline__ void close_segment_mfma(int slot, float (&facc)[4][M], float *lp_w, int lane) {
+    if (slot < 0 || lane >= 16) return;
+    float *dst = lp_w + slot * M * 64 + 4 * lane;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        float4 v = {facc[0][m], facc[1][m], facc[2][m], facc[3][m]};
+        *reinterpret_cast<float4 *>(dst + m * 64) = v;
+    }
+}
+
 struct Compute {
     int slot;     // LDS slot of the open run's segment; -1: none
     int q;        // LDS byte offset of the next tile's activation group
@@ -564,7 +585,10 @@ template <int BITS, int M>
 __device__ __forceinline__ void compute(const Lay &L, int lane, Compute &c, float (&facc)[4][M], const Slot<BITS> &s,
                                         float *lp_w) {
     if (s.hdr != 0) {   // the tile opens a run: close the previous segment
-        close_segment<M>(c.slot, facc, lp_w, lane);
+        if constexpr (use_mfma<M>())
+            close_segment_mfma<M>(c.slot, facc, lp_w, lane);
+        else
+            close_segment<M>(c.slot, facc, lp_w, lane);
         c.slot = (int)((s.hdr >> kRunPhaseBits) & ((1u << kRunSlotBits) - 1));
         c.q = (int)((s.hdr >> (kRunPhaseBits + kRunSlotBits)) & ((1u << kRunGroupBits) - 1)) * kGroup;
 #pragma unroll
@@ -572,19 +596,32 @@ __device__ __forceinline__ void compute(const Lay &L, int lane, Compute &c, floa
 #pragma unroll
             for (int m = 0; m < M; ++m) facc[i][m] = 0.0f;
     }
-    int acc[4][M];
+    if constexpr (use_mfma<M>()) {
+        // activation row lane & 15; rows past M read row 0 and feed unused outputs
+        const int am = (lane & 15) < M ? (lane & 15) : 0;
+        v4i acc[4];
+        mfma_tile<BITS>(s.w, g_lds + am * L.qs + c.q + (lane >> 4) * 32, acc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+            const float S = row_scale(s.sc, i);
 #pragma unroll
-        for (int m = 0; m < M; ++m) acc[i][m] = 0;
-    const int8_t *qg = g_lds + c.q + (lane >> 4) * 32;
-    const int qs = L.qs;
-    dot_tile<BITS, M>(s.w, [&](int m, int d) { return reinterpret_cast<const int *>(qg + m * qs)[d]; }, acc);
+            for (int m = 0; m < M; ++m) facc[i][m] = fmaf((float)acc[i][m], S, facc[i][m]);
+        }
+    } else {
+        int acc[4][M];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float S = row_scale(s.sc, i);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int m = 0; m < M; ++m) facc[i][m] = fmaf((float)acc[i][m], S, facc[i][m]);
+            for (int m = 0; m < M; ++m) acc[i][m] = 0;
+        const int8_t *qg = g_lds + c.q + (lane >> 4) * 32;
+        const int qs = L.qs;
+        dot_tile<BITS, M>(s.w, [&](int m, int d) { return reinterpret_cast<const int *>(qg + m * qs)[d]; }, acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float S = row_scale(s.sc, i);
+#pragma unroll
+            for (int m = 0; m < M; ++m) facc[i][m] = fmaf((float)acc[i][m], S, facc[i][m]);
+        }
     }
     c.q += kGroup;
 }
@@ -632,7 +669,10 @@ __device__ __forceinline__ void stream_phase(const Lay &L, Issue &is, int lane, 
             if (i0 + i + D < n) issue<BITS>(is, lane, ring[i]);
         }
     }
-    close_segment<M>(c.slot, facc, lp_w, lane);
+    if constexpr (use_mfma<M>())
+        close_segment_mfma<M>(c.slot, facc, lp_w, lane);
+    else
+        close_segment<M>(c.slot, facc, lp_w, lane);
 }
 
 template <int BITS, int M>
