@@ -4,7 +4,7 @@
  * The hot path of batch-of-one LLM token generation as described on the page
  * "Doubling LLM token rates in ComfyUI" (blog.comfy.org):
  *   - section "What is the bottleneck?": a dense, often square weight matrix
- *     times one activation row (M = 1) or a thin block (M = 2..4) for a
+ *     times one activation row (M = 1) or a thin block (M = 2..8) for a
  *     multi-token-prediction verify step; every weight is read once per step
  *     for about one operation, so HBM read speed bounds the step;
  *   - section "Optimizing the Linear Kernel": W4A8 / W6A8 weights (4- or 6-bit
@@ -41,7 +41,7 @@
  *   - Return value: MBQ_OK (0) or a negative mbq_status.  On any non-zero
  *     status nothing has been enqueued, except MBQ_ERR_HIP, which reports a
  *     launch failure (the HIP error code is then in mbq_last_hip_error()).
- *   - Shapes: M in [1, 4]; K a positive multiple of 128 (at most 2^24);
+ *   - Shapes: M in [1, 8]; K a positive multiple of 128 (at most 2^24);
  *     1 <= N <= 2^20; bits 4 or 6.
  *   - Alignment: packed weights 256-byte aligned; activation, q and y
  *     pointers 16-byte aligned; workspaces 256-byte aligned.

@@ -25,7 +25,7 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 bool bits_ok(int bits) { return bits == 4 || bits == 6; }
 bool k_ok(int64_t K) { return K >= kGroup && K % kGroup == 0 && K <= (int64_t)1 << 24; }
 bool n_ok(int64_t N) { return N >= 1 && N <= kMaxN; }
-bool m_ok(int64_t M) { return M >= 1 && M <= 4; }
+bool m_ok(int64_t M) { return M >= 1 && M <= kMaxM; }
 
 // 0 = unknown, 1 = gfx950, -1 = other; cached per device ordinal.
 std::atomic<int> g_dev_ok[64];
@@ -117,7 +117,7 @@ const char *mbq_status_string(int status) {
     switch (status) {
         case MBQ_OK: return "ok";
         case MBQ_ERR_NULL: return "null pointer";
-        case MBQ_ERR_SHAPE: return "unsupported shape (M in 1..4, K multiple of 128, 1 <= N <= 2^20)";
+        case MBQ_ERR_SHAPE: return "unsupported shape (M in 1..8, K multiple of 128, 1 <= N <= 2^20)";
         case MBQ_ERR_BITS: return "bits must be 4 or 6";
         case MBQ_ERR_ALIGN: return "misaligned pointer";
         case MBQ_ERR_WORKSPACE: return "workspace missing or too small";
@@ -276,7 +276,7 @@ int mbq_sequence_prepare(const mbq_op *ops, int32_t n_ops, void *const *bufs, co
 int mbq_sequence_run(const mbq_sequence_info *info, void *ws, void *stream) {
     if (!info || !ws) return MBQ_ERR_NULL;
     if (info->magic != 0x6d62712d73657131ull || (info->bits != 4 && info->bits != 6) || info->M < 1 ||
-        info->M > 4 || info->grid < 1)
+        info->M > kMaxM || info->grid < 1)
         return MBQ_ERR_PROGRAM;
     if (!aligned(ws, 256)) return MBQ_ERR_ALIGN;
     uint32_t gen = (g_generation.fetch_add(1, std::memory_order_relaxed) % ((1u << 22) - 1)) + 1;

@@ -1,7 +1,7 @@
 // The skinny W4A8 / W6A8 linear, one launch per matrix.
 //
 // "What is the bottleneck?" (page "Doubling LLM token rates in ComfyUI"):
-// one activation row (M = 1) or a thin block (M = 2..4) times a dense weight
+// one activation row (M = 1) or a thin block (M = 2..8) times a dense weight
 // matrix; every weight is read once for about one operation, so the kernel is
 // a stream over the packed weights.
 //
@@ -182,7 +182,11 @@ hipError_t launch_linear_bits(int64_t M, int64_t N, int64_t K, const int8_t *q, 
         case 1: MBQ_LAUNCH(1); break;
         case 2: MBQ_LAUNCH(2); break;
         case 3: MBQ_LAUNCH(3); break;
-        default: MBQ_LAUNCH(4); break;
+        case 4: MBQ_LAUNCH(4); break;
+        case 5: MBQ_LAUNCH(5); break;
+        case 6: MBQ_LAUNCH(6); break;
+        case 7: MBQ_LAUNCH(7); break;
+        default: MBQ_LAUNCH(8); break;
     }
 #undef MBQ_LAUNCH
     return hipGetLastError();
@@ -197,7 +201,11 @@ hipError_t launch_group_acc_bits(int64_t M, int64_t N, int64_t K, const int8_t *
         case 1: group_acc_kernel<BITS, 1><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
         case 2: group_acc_kernel<BITS, 2><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
         case 3: group_acc_kernel<BITS, 3><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
-        default: group_acc_kernel<BITS, 4><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
+        case 4: group_acc_kernel<BITS, 4><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
+        case 5: group_acc_kernel<BITS, 5><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
+        case 6: group_acc_kernel<BITS, 6><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
+        case 7: group_acc_kernel<BITS, 7><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
+        default: group_acc_kernel<BITS, 8><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
     }
     return hipGetLastError();
 }

@@ -49,6 +49,7 @@ constexpr int kSlab = 1024;   // bytes of one wave-wide dwordx4 load
 // on the call's shape, counters that one call leaves at zero are still zero
 // for any later call, whatever its shape.
 constexpr int64_t kMaxN = (int64_t)1 << 20;
+constexpr int kMaxM = 8;      // activation rows per call (a token plus up to 7 verify rows)
 constexpr int64_t kCounterBytes = (kMaxN / kRows) * 4;   // 64 KiB
 
 template <int BITS> struct Layout;

@@ -213,7 +213,7 @@ __device__ __forceinline__ float quant_code(float t, float s, float rinv, bool r
 // phase's metadata is fetched meanwhile.
 template <int M>
 __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int p, uint32_t gen, int wg,
-                                            float (*s_sh)[4], float (*r_sh)[4]) {
+                                            float (*s_sh)[kMaxM], float (*r_sh)[kMaxM]) {
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     uint32_t pre[kMetaIters];
@@ -562,17 +562,25 @@ __device__ __forceinline__ void close_segment(int slot, float (&facc)[4][M], flo
 #endif
 template <int M>
 constexpr bool use_mfma() { return M >= MBQ_MFMA_MIN_M; }
-
-// The matrix-core form of close_segment: lanes 0..15 hold complete sums of
-// rows 4 * lane + i.
+// Accumulator columns per lane: the dot path keeps all M rows in every lane;
+// the matrix-core path keeps rows 4 * (lane >> 4) + j, j < 4.
 template <int M>
-__device__ __forceinline__ void close_segment_mfma(int slot, float (&facc)[4][M], float *lp_w, int lane) {
-    if (slot < 0 || lane >= 16) return;
-    float *dst = lp_w + slot * M * 64 + 4 * lane;
+constexpr int acc_rows() { return use_mfma<M>() && M > 4 ? 4 : M; }
+
+// The matrix-core form of close_segment: lane l holds complete sums of
+// weight rows 4 * (l & 15) + i for activation rows 4 * (l >> 4) + j.
+template <int M>
+__device__ __forceinline__ void close_segment_mfma(int slot, float (&facc)[4][acc_rows<M>()], float *lp_w,
+                                                   int lane) {
+    if (slot < 0) return;
+    float *dst = lp_w + slot * M * 64 + 4 * (lane & 15);
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-        float4 v = {facc[0][m], facc[1][m], facc[2][m], facc[3][m]};
-        *reinterpret_cast<float4 *>(dst + m * 64) = v;
+    for (int j = 0; j < acc_rows<M>(); ++j) {
+        const int m = 4 * (lane >> 4) + j;
+        if (m < M) {
+            float4 v = {facc[0][j], facc[1][j], facc[2][j], facc[3][j]};
+            *reinterpret_cast<float4 *>(dst + m * 64) = v;
+        }
     }
 }
 
@@ -582,8 +590,8 @@ struct Compute {
 };
 
 template <int BITS, int M>
-__device__ __forceinline__ void compute(const Lay &L, int lane, Compute &c, float (&facc)[4][M], const Slot<BITS> &s,
-                                        float *lp_w) {
+__device__ __forceinline__ void compute(const Lay &L, int lane, Compute &c, float (&facc)[4][acc_rows<M>()],
+                                        const Slot<BITS> &s, float *lp_w) {
     if (s.hdr != 0) {   // the tile opens a run: close the previous segment
         if constexpr (use_mfma<M>())
             close_segment_mfma<M>(c.slot, facc, lp_w, lane);
@@ -594,7 +602,7 @@ __device__ __forceinline__ void compute(const Lay &L, int lane, Compute &c, floa
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int m = 0; m < M; ++m) facc[i][m] = 0.0f;
+            for (int m = 0; m < acc_rows<M>(); ++m) facc[i][m] = 0.0f;
     }
     if constexpr (use_mfma<M>()) {
         // activation row lane & 15; rows past M read row 0 and feed unused outputs
@@ -605,7 +613,7 @@ __device__ __forceinline__ void compute(const Lay &L, int lane, Compute &c, floa
         for (int i = 0; i < 4; ++i) {
             const float S = row_scale(s.sc, i);
 #pragma unroll
-            for (int m = 0; m < M; ++m) facc[i][m] = fmaf((float)acc[i][m], S, facc[i][m]);
+            for (int j = 0; j < acc_rows<M>(); ++j) facc[i][j] = fmaf((float)acc[i][j], S, facc[i][j]);
         }
     } else {
         int acc[4][M];
@@ -650,7 +658,7 @@ __device__ __forceinline__ void prime(Issue &is, int lane, int n, Slot<BITS> (&r
 // memory costs address-unit time that the hand-over's own requests need.
 template <int BITS, int M, int D>
 __device__ __forceinline__ void stream_phase(const Lay &L, Issue &is, int lane, int n, Slot<BITS> (&ring)[D],
-                                             float (&facc)[4][M], float *lp_w) {
+                                             float (&facc)[4][acc_rows<M>()], float *lp_w) {
     Compute c;
     c.slot = -1;
     c.q = 0;
@@ -678,8 +686,8 @@ __device__ __forceinline__ void stream_phase(const Lay &L, Issue &is, int lane, 
 template <int BITS, int M>
 __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const SeqPlan *__restrict__ P, uint32_t *err,
                                                           uint32_t gen) {
-    __shared__ float s_sh[2][4];
-    __shared__ float r_sh[2][4];
+    __shared__ float s_sh[2][kMaxM];
+    __shared__ float r_sh[2][kMaxM];
     if (cload(&P->magic) != kPlanMagic) {   // workspace does not hold a prepared plan
         if (threadIdx.x == 0 && blockIdx.x == 0) store_shared(err, 2u);
         return;
@@ -714,7 +722,7 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const SeqPlan *__restr
     is.left = 0;
     is.src = nullptr;
     float *lp_w = lds_partials(L, M) + (wi * L.slots * M) * 64;
-    float facc[4][M];
+    float facc[4][acc_rows<M>()];
     constexpr int D = ring_depth<BITS, M>();
     Slot<BITS> ring[D];
 
@@ -757,10 +765,14 @@ hipError_t launch_sequence(int bits, int64_t M, int grid, int lds_bytes, const v
 #define MBQ_PICK(B, MM) fn = reinterpret_cast<const void *>(&seq_kernel<B, MM>)
     if (bits == 4) {
         switch (M) { case 1: MBQ_PICK(4, 1); break; case 2: MBQ_PICK(4, 2); break;
-                     case 3: MBQ_PICK(4, 3); break; default: MBQ_PICK(4, 4); break; }
+                     case 3: MBQ_PICK(4, 3); break; case 4: MBQ_PICK(4, 4); break;
+                     case 5: MBQ_PICK(4, 5); break; case 6: MBQ_PICK(4, 6); break;
+                     case 7: MBQ_PICK(4, 7); break; default: MBQ_PICK(4, 8); break; }
     } else {
         switch (M) { case 1: MBQ_PICK(6, 1); break; case 2: MBQ_PICK(6, 2); break;
-                     case 3: MBQ_PICK(6, 3); break; default: MBQ_PICK(6, 4); break; }
+                     case 3: MBQ_PICK(6, 3); break; case 4: MBQ_PICK(6, 4); break;
+                     case 5: MBQ_PICK(6, 5); break; case 6: MBQ_PICK(6, 6); break;
+                     case 7: MBQ_PICK(6, 7); break; default: MBQ_PICK(6, 8); break; }
     }
 #undef MBQ_PICK
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kSeqThreads), args, (unsigned)lds_bytes, st);

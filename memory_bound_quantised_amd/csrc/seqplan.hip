@@ -70,7 +70,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
                             int32_t n_bufs, int64_t M, int n_cu, uint8_t *ws, SeqBuild *out) {
     if (!ops || !widths) return MBQ_ERR_NULL;
     if (n_ops < 1 || n_bufs < 1) return MBQ_ERR_PROGRAM;
-    if (M < 1 || M > 4) return MBQ_ERR_SHAPE;
+    if (M < 1 || M > kMaxM) return MBQ_ERR_SHAPE;
     for (int32_t b = 0; b < n_bufs; ++b)
         if (widths[b] < 8 || widths[b] % 8 || widths[b] > kMaxN) return MBQ_ERR_PROGRAM;
     const int bits = ops[0].bits;

@@ -69,7 +69,7 @@ def test_linear_argument_validation():
     f = L.mbq_w4a8_linear
     assert f(1, 4096, 4096, None, A, A, A, A, ws_need, None) == -1          # null q
     assert f(0, 4096, 4096, A, A, A, A, A, ws_need, None) == -2             # M = 0
-    assert f(5, 4096, 4096, A, A, A, A, A, ws_need, None) == -2             # M = 5
+    assert f(9, 4096, 4096, A, A, A, A, A, ws_need, None) == -2             # M = 9
     assert f(1, 4096, 4000, A, A, A, A, A, ws_need, None) == -2             # K % 128
     assert f(1, 0, 4096, A, A, A, A, A, ws_need, None) == -2                # N = 0
     assert f(1, 4096, 4096, A, A, A + 16, A, A, ws_need, None) == -4        # packed not 256-aligned
@@ -85,7 +85,7 @@ def test_linear_argument_validation():
 def test_quant_and_pack_validation():
     L = mbq.lib()
     assert L.mbq_quantize_act(1, 4096, None, A, A, None) == -1
-    assert L.mbq_quantize_act(5, 4096, A, A, A, None) == -2
+    assert L.mbq_quantize_act(9, 4096, A, A, A, None) == -2
     assert L.mbq_rmsnorm_quantize_act(1, 64, A, A, A, None) == -2
     assert L.mbq_quantize_act(1, 4096, A + 2, A, A, None) == -4
     assert L.mbq_pack_weights(3, 64, 128, A, A, A, None) == -3
@@ -120,7 +120,8 @@ def test_sequence_program_validation():
     }
     for name, (ops, want) in bad_cases.items():
         assert L.mbq_sequence_workspace_bytes(_program(ops), len(ops), W, 3, 1) == want, name
-    assert L.mbq_sequence_workspace_bytes(good, 2, W, 3, 5) == -2
+    assert L.mbq_sequence_workspace_bytes(good, 2, W, 3, 9) == -2
+    assert L.mbq_sequence_workspace_bytes(good, 2, W, 3, 8) > 0
     assert L.mbq_sequence_workspace_bytes(good, 0, W, 3, 1) == -6
     W_bad = (ctypes.c_int64 * 3)(256, 500, 256)
     assert L.mbq_sequence_workspace_bytes(good, 2, W_bad, 3, 1) == -6

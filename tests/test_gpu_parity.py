@@ -46,7 +46,7 @@ def special_rows(K):
 
 @pytest.mark.parametrize("rmsnorm", [False, True])
 @pytest.mark.parametrize("K", [128, 4096, 5120, 17408])
-@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
 def test_quantize_bit_exact(M, K, rmsnorm):
     x = synth.activations(M, K, seed=K + M)
     q, s = mbq.quantize_act(dev(x), rmsnorm=rmsnorm)
@@ -106,7 +106,7 @@ def test_pack_pads_rows_with_zeros(bits):
 # ---------------------------------------------------------------- exact integer sums
 
 @pytest.mark.parametrize("bits", [4, 6])
-@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("N,K", [(64, 128), (200, 1152)])
 def test_group_acc_bit_exact(bits, M, N, K):
     canon, S = synth.weights(bits, N, K, seed=11 + N)
@@ -133,7 +133,7 @@ def test_group_acc_extreme_codes(bits):
 # ---------------------------------------------------------------- the linear
 
 @pytest.mark.parametrize("bits", [4, 6])
-@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
 @pytest.mark.parametrize("N,K", [(1, 128), (200, 1152), (1000, 4096), (4096, 4096)])
 def test_linear_vs_oracle(bits, M, N, K):
     canon, S = synth.weights(bits, N, K, seed=1)
@@ -240,7 +240,7 @@ def _small_shapes():
 
 @pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("bits", [4, 6])
-@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_layer_sequence_teacher_forced_small(bits, M, fused):
     ops, mats, bufs, _ = _run_sequence(bits, _small_shapes, 3, M, distinct=True, fused=fused)
     for o in ops:
@@ -262,7 +262,7 @@ def test_layer_sequence_9b_layers_teacher_forced(bits, M):
         assert_close_bf16(bufs[o["out_buf"]][:, rows], ref, o["name"])
 
 
-@pytest.mark.parametrize("M", [1, 3])
+@pytest.mark.parametrize("M", [1, 3, 8])
 def test_layer_sequence_27b_layer_teacher_forced(M):
     """One 27B-shaped layer: q is 16384 wide and o reads its first 8192 columns."""
     ops, mats, bufs, _ = _run_sequence(4, synth.layer_shapes_27b, 1, M, distinct=True)
