@@ -47,6 +47,8 @@ def _load():
         lib.oracle_decode.argtypes = [ctypes.c_int, I64, I64, P, P]
         lib.oracle_quantize_act.argtypes = [I64, I64, P, P, P]
         lib.oracle_rmsnorm_bf16.argtypes = [I64, I64, P, P]
+        lib.oracle_wrmsnorm_bf16.argtypes = [I64, I64, P, P, P]
+        lib.oracle_swiglu_bf16.argtypes = [I64, P, P, P]
         lib.oracle_group_acc.argtypes = [ctypes.c_int, I64, I64, I64, P, P, P]
         lib.oracle_linear.argtypes = [ctypes.c_int, I64, I64, I64, P, P, P, P, P, P]
         lib.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
@@ -140,31 +142,68 @@ def f16_to_f64(h: int) -> float:
     return float(_load().oracle_f16_to_f64(int(h)))
 
 
+def wrmsnorm_bf16(x_bf16: np.ndarray, w_bf16: np.ndarray) -> np.ndarray:
+    """Weighted RMSNorm of bf16 rows with bf16 per-column weights (see oracle.c)."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    w = _c(w_bf16, np.uint16).reshape(-1)
+    assert w.size == K
+    t = np.empty((M, K), np.uint16)
+    _load().oracle_wrmsnorm_bf16(M, K, _p(x), _p(w), _p(t))
+    return t
+
+
+def swiglu_bf16(g_bf16: np.ndarray, u_bf16: np.ndarray) -> np.ndarray:
+    """h = bf16(silu(g) * u), evaluated in fp64 (see oracle.c)."""
+    g = _c(g_bf16, np.uint16)
+    u = _c(u_bf16, np.uint16)
+    assert g.shape == u.shape
+    h = np.empty(g.shape, np.uint16)
+    _load().oracle_swiglu_bf16(g.size, _p(g), _p(u), _p(h))
+    return h
+
+
 PRO_QUANT = 0
 PRO_RMSNORM_QUANT = 1
+PRO_WRMSNORM_QUANT = 2
+PRO_SWIGLU_QUANT = 3
 
 
-def prologue_quant(x_bf16: np.ndarray, prologue: int):
-    """The quantisation in front of a linear, with the optional weightless RMSNorm."""
-    t = rmsnorm_bf16(x_bf16) if prologue == PRO_RMSNORM_QUANT else x_bf16
-    return quantize_act(t)
+def prologue_input(x_bf16: np.ndarray, prologue: int, norm_w=None, u_bf16=None) -> np.ndarray:
+    """The bf16 values a prologue hands to the quantisation."""
+    if prologue == PRO_RMSNORM_QUANT:
+        return rmsnorm_bf16(x_bf16)
+    if prologue == PRO_WRMSNORM_QUANT:
+        return wrmsnorm_bf16(x_bf16, norm_w)
+    if prologue == PRO_SWIGLU_QUANT:
+        return swiglu_bf16(x_bf16, u_bf16)
+    return x_bf16
 
 
-def op(bits: int, x_bf16: np.ndarray, prologue: int, canon: np.ndarray, scales: np.ndarray):
-    q, s = prologue_quant(x_bf16, prologue)
+def prologue_quant(x_bf16: np.ndarray, prologue: int, norm_w=None, u_bf16=None):
+    """The quantisation in front of a linear, with its optional prologue."""
+    return quantize_act(prologue_input(x_bf16, prologue, norm_w, u_bf16))
+
+
+def op(bits: int, x_bf16: np.ndarray, prologue: int, canon: np.ndarray, scales: np.ndarray,
+       norm_w=None, u_bf16=None):
+    q, s = prologue_quant(x_bf16, prologue, norm_w, u_bf16)
     return linear(bits, q, s, canon, scales)
 
 
 def layer_sequence(bits: int, ops: list[dict], bufs: dict, weights) -> dict:
     """Run a decode-step walk op by op.
 
-    ``ops``: dicts with K, N, in_buf, out_buf, prologue, matrix.  ``bufs``:
-    buffer index -> bf16 array [M][width] (modified in place and returned).
-    ``weights(matrix_index) -> (canon, scales)``.  Op i reads columns [0, K)
-    of its input buffer and overwrites its whole output buffer.
+    ``ops``: dicts with K, N, in_buf, out_buf, prologue, matrix, and for the
+    weighted RMSNorm ``norm_w`` (bf16 [K]), for SwiGLU ``in_buf2`` (the up
+    buffer).  ``bufs``: buffer index -> bf16 array [M][width] (modified in
+    place and returned).  ``weights(matrix_index) -> (canon, scales)``.  Op i
+    reads columns [0, K) of its input buffer(s) and overwrites its whole
+    output buffer.
     """
     for o in ops:
         x = np.ascontiguousarray(bufs[o["in_buf"]][:, : o["K"]])
+        u = np.ascontiguousarray(bufs[o["in_buf2"]][:, : o["K"]]) if o["prologue"] == PRO_SWIGLU_QUANT else None
         canon, scales = weights(o["matrix"])
-        bufs[o["out_buf"]] = op(bits, x, o["prologue"], canon, scales)
+        bufs[o["out_buf"]] = op(bits, x, o["prologue"], canon, scales, o.get("norm_w"), u)
     return bufs

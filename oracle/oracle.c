@@ -27,7 +27,17 @@
  *   - the optional weightless RMSNorm in front of a quantisation (the page's
  *     prologue fusion absorbs the RMSNorm that precedes the quantisation):
  *     ss = sum_k x^2 in fp64, r = 1/sqrtf(f32(ss/K) + 1e-6f) in fp32,
- *     t = bf16_round(f32(x) * r).
+ *     t = bf16_round(f32(x) * r);
+ *   - the weighted RMSNorm (same section; a norm with a learned per-column
+ *     weight w, bf16): the same ss and r, then t = bf16_round(f32((x*w) * r)),
+ *     where x*w of two bf16 values is exact in fp32, so t carries a single
+ *     fp32 rounding before the bf16 one (the pages fix no order; this one makes
+ *     max|t| = bf16_round(f32(max|x*w| * r)), since both roundings are monotone);
+ *   - the SwiGLU gate in front of the down projection (same section: the
+ *     quantisation absorbs the SwiGLU that precedes it): h = bf16_round(
+ *     g / (1 + exp(-g)) * u) for bf16 g (gate) and u (up), evaluated in fp64
+ *     here; the GPU's fp32 evaluation may land one bf16 step away where the
+ *     value sits next to a rounding boundary.
  * Every loop below is the plain definition: no blocking, no reordering.
  */
 #include <math.h>
@@ -153,6 +163,37 @@ int oracle_rmsnorm_bf16(int64_t M, int64_t K, const uint16_t *x, uint16_t *t) {
         float ms = (float)(ss / (double)K);
         float r = 1.0f / sqrtf(ms + 1e-6f);
         for (int64_t k = 0; k < K; ++k) t[m * K + k] = f32_to_bf16(bf16_to_f32(xr[k]) * r);
+    }
+    return 0;
+}
+
+/* ---- weighted RMSNorm (w: bf16 [K], one weight per input column) --------- */
+
+int oracle_wrmsnorm_bf16(int64_t M, int64_t K, const uint16_t *x, const uint16_t *w, uint16_t *t) {
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *xr = x + m * K;
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = (double)bf16_to_f32(xr[k]);
+            ss += v * v;
+        }
+        float ms = (float)(ss / (double)K);
+        float r = 1.0f / sqrtf(ms + 1e-6f);
+        for (int64_t k = 0; k < K; ++k) {
+            float a = bf16_to_f32(xr[k]) * bf16_to_f32(w[k]);   /* exact */
+            t[m * K + k] = f32_to_bf16(a * r);
+        }
+    }
+    return 0;
+}
+
+/* ---- SwiGLU: h = silu(g) * u, rounded to bf16 ----------------------------- */
+
+int oracle_swiglu_bf16(int64_t n, const uint16_t *g, const uint16_t *u, uint16_t *h) {
+    for (int64_t i = 0; i < n; ++i) {
+        double gv = (double)bf16_to_f32(g[i]);
+        double uv = (double)bf16_to_f32(u[i]);
+        h[i] = f64_to_bf16(gv / (1.0 + exp(-gv)) * uv);
     }
     return 0;
 }

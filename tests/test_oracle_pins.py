@@ -296,6 +296,84 @@ def test_rmsnorm_random_rows():
     assert np.all(np.abs(t - ref) <= 2 ** -8 * np.abs(ref) + 1e-30)
 
 
+# ---------------------------------------------------------------- weighted RMSNorm and SwiGLU prologues
+
+def test_wrmsnorm_unit_weights_is_the_weightless_norm():
+    rng = np.random.default_rng(21)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((3, 640)).astype(np.float32))
+    ones = synth.f32_to_bf16_bits(np.ones(640, np.float32))
+    assert np.array_equal(oracle.wrmsnorm_bf16(x, ones), oracle.rmsnorm_bf16(x))
+
+
+@pytest.mark.parametrize("j", [-3, 1, 4])
+def test_wrmsnorm_power_of_two_weights_scale_exactly(j):
+    # w = 2^j everywhere: every t is 2^j times the weightless one, exactly
+    # (scaling by a power of two commutes with both roundings away from overflow)
+    rng = np.random.default_rng(22 + j)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((2, 256)).astype(np.float32))
+    w = synth.f32_to_bf16_bits(np.full(256, 2.0 ** j, np.float32))
+    t = bf16_to_f64(oracle.wrmsnorm_bf16(x, w))
+    assert np.array_equal(t, bf16_to_f64(oracle.rmsnorm_bf16(x)) * 2.0 ** j)
+
+
+def test_wrmsnorm_weights_act_per_column_and_not_on_the_scale():
+    # a one-hot weight keeps one column and zeroes the rest, while the norm
+    # factor still comes from the whole row (the weight is not in the mean square)
+    rng = np.random.default_rng(23)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((2, 384)).astype(np.float32))
+    w = np.zeros(384, np.float32)
+    w[77] = 1.0
+    t = oracle.wrmsnorm_bf16(x, synth.f32_to_bf16_bits(w))
+    ref = oracle.rmsnorm_bf16(x)
+    assert np.array_equal(t[:, 77], ref[:, 77])
+    assert not np.any(bf16_to_f64(np.delete(t, 77, axis=1)))
+
+
+def test_wrmsnorm_close_to_float64_definition_and_amax_identity():
+    rng = np.random.default_rng(24)
+    x = synth.f32_to_bf16_bits((rng.standard_normal((3, 1024)) * [[0.02], [1], [30]]).astype(np.float32))
+    w = synth.f32_to_bf16_bits(rng.uniform(-2, 2, 1024).astype(np.float32))
+    xf, wf = bf16_to_f64(x), bf16_to_f64(w)
+    r = 1.0 / np.sqrt((xf ** 2).mean(axis=1, keepdims=True) + 1e-6)
+    ref = xf * wf * r
+    t = bf16_to_f64(oracle.wrmsnorm_bf16(x, w))
+    assert np.all(np.abs(t - ref) <= 2 ** -8 * np.abs(ref) + 1e-30)
+    # the largest |t| is the rounded largest |x w| times the row's factor
+    # (what a producer that only knows |x w| and sum x^2 can publish)
+    for m in range(3):
+        a = np.max(np.abs(xf[m] * wf))
+        rf = np.float32(1.0) / np.sqrt(np.float32((xf[m] ** 2).sum() / 1024) + np.float32(1e-6))
+        amax_t = bf16_to_f64(np.array([f64_to_bf16_bits_via_f32(np.float32(a) * rf)]))[0]
+        assert np.max(np.abs(t[m])) == amax_t
+
+
+def test_swiglu_closed_forms():
+    import math
+    g = _bf16([[0.0, 1.0, -1.0, 48.0, -100.0, 2.0, 1.0]])
+    u = _bf16([[5.0, 1.0, 1.0, 0.75, 1.0, 0.0, -3.0]])
+    h = oracle.swiglu_bf16(g, u)[0]
+    assert h[0] in (0x0000, 0x8000)                      # silu(0) = 0
+    assert h[1] == 0x3F3B                                 # 1/(1+e^-1) = 0.7310... -> 0.73046875
+    assert bf16_to_f64(h[2:3])[0] == pytest.approx(-1 / (1 + math.e), rel=2 ** -8)
+    assert bf16_to_f64(h[3:4])[0] == 36.0                 # sigmoid(48) = 1 - 1.4e-21: exactly 48 * 0.75
+    assert h[4] in (0x0000, 0x8000)                       # -100 e^-100 is below every bf16
+    assert bf16_to_f64(h[5:6])[0] == 0.0                  # u = 0
+    s1 = 1 / (1 + math.exp(-1.0))
+    assert bf16_to_f64(h[6:7])[0] == pytest.approx(-3 * s1, rel=2 ** -8)
+
+
+def test_swiglu_reflection_identity():
+    # silu(g) - silu(-g) = g, so h(g, u) - h(-g, u) = g u up to the two roundings
+    rng = np.random.default_rng(25)
+    g = synth.f32_to_bf16_bits(rng.uniform(-6, 6, 512).astype(np.float32))
+    u = synth.f32_to_bf16_bits(rng.standard_normal(512).astype(np.float32))
+    gf, uf = bf16_to_f64(g), bf16_to_f64(u)
+    ng = synth.f32_to_bf16_bits(-gf.astype(np.float32))
+    d = bf16_to_f64(oracle.swiglu_bf16(g, u)) - bf16_to_f64(oracle.swiglu_bf16(ng, u))
+    bound = 2 ** -8 * (np.abs(gf * uf) + np.abs(gf * uf) / (1 + np.exp(-np.abs(gf)))) + 1e-30
+    assert np.all(np.abs(d - gf * uf) <= bound)
+
+
 # ---------------------------------------------------------------- decode-step walk wiring
 
 def test_layer_sequence_wiring_with_permutation_weights():
