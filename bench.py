@@ -1,13 +1,14 @@
 """Benchmark: decode-step weight-read bandwidth of the skinny W4A8/W6A8 linears.
 
 One step is one mbq_layer_sequence call: the whole decode-step walk (per layer:
-RMSNorm+quant -> q/k/v, quant -> o, quant -> gate/up, quant -> down) over a
-synthetic 9B-shaped (default) or 27B-shaped weight set, every weight matrix
+RMSNorm+quant -> q/k/v, quant -> o, quant -> gate/up, quant -> down; with
+--dataflow swiglu the norms carry weights and down reads silu(gate) * up) over
+a synthetic 9B-shaped (default) or 27B-shaped weight set, every weight matrix
 read once.  Weights, buffers and the workspace are resident in HBM before the
 timed region.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--set 9b|27b] [--bits 4|6]
-                  [--m 1] [--extra-m 3] [--no-cpu]
+                  [--m 1] [--extra-m 3] [--dataflow plain|swiglu] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -40,18 +41,26 @@ def to_dev(a):
     return torch.from_numpy(a).cuda()
 
 
-def build_set(mbq, set_name, bits, n_layers):
+def build_set(mbq, set_name, bits, n_layers, dataflow="plain"):
     """Pack every matrix of the weight set on the GPU; returns (ops, widths, dev_ops)."""
     import torch
     shapes_fn, _ = synth.WEIGHT_SETS[set_name]
-    ops, widths = synth.layer_program(shapes_fn, n_layers)
+    ops, widths = synth.layer_program(shapes_fn, n_layers, dataflow=dataflow)
     dev_ops = []
+    norms = {}   # one device copy per norm: the ops behind one norm share its weights
     t0 = time.time()
     for o in ops:
         canon, S = synth.weights(bits, o["N"], o["K"], seed=1 + o["matrix"])
         packed = mbq.pack_weights(bits, to_dev(canon), to_dev(S), o["N"], o["K"])
-        dev_ops.append(dict(bits=bits, prologue=o["prologue"], N=o["N"], K=o["K"], packed=packed,
-                            in_buf=o["in_buf"], out_buf=o["out_buf"]))
+        d = dict(bits=bits, prologue=o["prologue"], N=o["N"], K=o["K"], packed=packed,
+                 in_buf=o["in_buf"], out_buf=o["out_buf"])
+        if "norm_seed" in o:
+            if o["norm_seed"] not in norms:
+                norms[o["norm_seed"]] = to_dev(synth.norm_weights(o["K"], o["norm_seed"]))
+            d["norm_w"] = norms[o["norm_seed"]]
+        if "in_buf2" in o:
+            d["in_buf2"] = o["in_buf2"]
+        dev_ops.append(d)
         if o["matrix"] % 28 == 27:
             log(f"packed {o['matrix'] + 1}/{len(ops)} matrices ({time.time() - t0:.0f} s)")
     torch.cuda.synchronize()
@@ -85,7 +94,7 @@ def time_sequence(mbq, dev_ops, widths, M, steps, warmup, fused=True):
                 event_ms_best=float(per.min()), event_ms_mean=float(per.mean()))
 
 
-KERNEL_SOURCES = ["seq.hip", "seqplan.hip", "mbq_seq.h", "mbq_internal.h"]
+KERNEL_SOURCES = ["seq_walk.h", "seq_plain.hip", "seqplan.hip", "mbq_seq.h", "mbq_internal.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "seq_kernel_traffic.json")
 
 
@@ -113,12 +122,15 @@ def measured_traffic(key):
     return e["fetch_bytes_per_launch"] + e["write_bytes_per_launch"]
 
 
-def cpu_baseline(set_name, bits, n_layers, budget_s=10.0):
+def cpu_baseline(set_name, bits, n_layers, dataflow="plain", budget_s=10.0):
     """The oracle on the host cores: the same M=1 walk, layer after layer (starting over after
     the last layer), until about budget_s seconds of oracle time have been spent."""
     import oracle
     shapes_fn, _ = synth.WEIGHT_SETS[set_name]
-    ops, widths = synth.layer_program(shapes_fn, n_layers)
+    ops, widths = synth.layer_program(shapes_fn, n_layers, dataflow=dataflow)
+    for o in ops:
+        if "norm_seed" in o:
+            o["norm_w"] = synth.norm_weights(o["K"], o["norm_seed"])
     M = 1
     bufs = {i: np.zeros((M, w), np.uint16) for i, w in enumerate(widths)}
     bufs[0] = synth.activations(M, widths[0])
@@ -154,6 +166,8 @@ def main():
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--m", type=int, default=1)
     ap.add_argument("--extra-m", type=int, nargs="*", default=[3])
+    ap.add_argument("--dataflow", default="plain", choices=["plain", "swiglu"],
+                    help="swiglu: weighted RMSNorms before q/k/v and gate/up, silu(gate) * up before down")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--unfused", action="store_true", help="also time the one-launch-per-op walk")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
@@ -185,7 +199,7 @@ def main():
     wbytes = synth.weight_bytes(args.bits, shapes)
     log(f"set {args.set} W{args.bits}A8, {n_layers} layers, {len(shapes)} matrices, "
         f"{wbytes / 1e9:.3f} GB of weights + scales")
-    ops, widths, dev_ops = build_set(mbq, args.set, args.bits, n_layers)
+    ops, widths, dev_ops = build_set(mbq, args.set, args.bits, n_layers, args.dataflow)
 
     results = {}
     for M in [args.m] + [m for m in args.extra_m if m != args.m]:
@@ -214,8 +228,9 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": f"{args.set}-shaped decode step, {n_layers} layers x 7 W{args.bits}A8 "
-                               f"linears, M={args.m}",
-                   "weight_bytes": wbytes, "layers": n_layers, "bits": args.bits, "M": args.m},
+                               f"linears, M={args.m}" + (", SwiGLU dataflow" if args.dataflow == "swiglu" else ""),
+                   "weight_bytes": wbytes, "layers": n_layers, "bits": args.bits, "M": args.m,
+                   "dataflow": args.dataflow},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(1.0 / t_s, 2),
         "event_ms": {k: round(v, 4) for k, v in main_r.items()},
@@ -236,11 +251,12 @@ def main():
     out["roofline"] = {"bound": "hbm", "kernel": "seq_kernel (fused decode-step walk, 1 launch per step)",
                        "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(gbs / HBM_PEAK_GBS, 4),
-                       "traffic": measured_traffic(f"{args.set}/w{args.bits}/m{args.m}/l{n_layers}"),
+                       "traffic": measured_traffic(f"{args.set}/w{args.bits}/m{args.m}/l{n_layers}"
+                                                   + ("/swiglu" if args.dataflow == "swiglu" else "")),
                        "bytes_per_launch": wbytes, "launch_ms": round(main_r["event_ms_median"], 4)}
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(args.set, args.bits, n_layers)
+        out["cpu_baseline"] = cpu_baseline(args.set, args.bits, n_layers, args.dataflow)
     print(json.dumps(out), flush=True)
 
 

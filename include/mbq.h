@@ -118,6 +118,21 @@ int mbq_quantize_act(int64_t M, int64_t K, const void *x_bf16, int8_t *q, float 
 int mbq_rmsnorm_quantize_act(int64_t M, int64_t K, const void *x_bf16, int8_t *q, float *s,
                              void *stream);
 
+/* Same, preceded by the weighted RMSNorm of each row: r = 1/sqrt(mean(x^2) +
+ * 1e-6) (sum of squares in fp64, r in fp32), t = bf16(fp32(x * w * r)) where
+ * the product x * w of two bf16 values is exact.  w_bf16: device bf16 [K]
+ * norm weights, 16-byte aligned.  Other arguments as mbq_quantize_act. */
+int mbq_wrmsnorm_quantize_act(int64_t M, int64_t K, const void *x_bf16, const void *w_bf16,
+                              int8_t *q, float *s, void *stream);
+
+/* Same, preceded by the SwiGLU gate in front of a down projection (the
+ * prologue fusion of "Optimizing the Linear Kernel"): h = bf16(silu(g) * u)
+ * with silu(g) = g / (1 + exp(-g)) in fp32.  g_bf16, u_bf16: device bf16
+ * [M][K]; h_bf16: device bf16 [M][K] receiving h, or null.  Other arguments
+ * as mbq_quantize_act. */
+int mbq_swiglu_quantize_act(int64_t M, int64_t K, const void *g_bf16, const void *u_bf16,
+                            void *h_bf16, int8_t *q, float *s, void *stream);
+
 /* ---------------------------------------------------------------- the skinny linear
  * "What is the bottleneck?" / "Optimizing the Linear Kernel": y = rescale(q x W^T).
  * q: device int8 [M][K]; s: device fp32 [M]; packed: device, from
@@ -141,26 +156,34 @@ int mbq_linear_group_acc(int bits, int64_t M, int64_t N, int64_t K, const int8_t
 /* ---------------------------------------------------------------- decode-step walk
  * "What is the bottleneck?": one decode step reads every weight matrix of the
  * model once.  An op list describes the walk: op i quantises columns [0, K) of
- * buffer in_buf (optionally after the weightless RMSNorm), multiplies by its
- * packed matrix and writes all N columns of buffer out_buf.  Consecutive ops
- * with the same in_buf, prologue and K share one quantisation (a phase, e.g.
- * q/k/v or gate/up).  Semantics are those of running the ops one after the
- * other.  Buffers are device bf16 [M][width] with row stride width. */
-enum { MBQ_PRO_QUANT = 0, MBQ_PRO_RMSNORM_QUANT = 1 };
+ * buffer in_buf after its prologue (none, the weightless or weighted RMSNorm,
+ * or the SwiGLU gate of in_buf and in_buf2, as in the quantisation calls
+ * above), multiplies by its packed matrix and writes all N columns of buffer
+ * out_buf.  Consecutive ops with the same inputs, prologue, norm_w pointer and
+ * K share one quantisation (a phase, e.g. q/k/v or gate/up).  Semantics
+ * are those of running the ops one after the other.  Buffers are device bf16
+ * [M][width] with row stride width. */
+enum { MBQ_PRO_QUANT = 0, MBQ_PRO_RMSNORM_QUANT = 1, MBQ_PRO_WRMSNORM_QUANT = 2, MBQ_PRO_SWIGLU_QUANT = 3 };
 
 typedef struct mbq_op {
     int32_t bits;        /* 4 or 6 */
-    int32_t prologue;    /* MBQ_PRO_QUANT or MBQ_PRO_RMSNORM_QUANT */
+    int32_t prologue;    /* MBQ_PRO_* */
     int64_t N;           /* output columns; must equal the width of out_buf */
     int64_t K;           /* input columns read; multiple of 128, <= width of in_buf */
     const void *packed;  /* device, from mbq_pack_weights(bits, N, K) */
-    int32_t in_buf;      /* index into bufs */
-    int32_t out_buf;     /* index into bufs; differs from in_buf and from the
+    int32_t in_buf;      /* index into bufs (the gate for MBQ_PRO_SWIGLU_QUANT) */
+    int32_t out_buf;     /* index into bufs; differs from the inputs and from the
                             out_buf of every other op of the same phase */
+    int32_t in_buf2;     /* MBQ_PRO_SWIGLU_QUANT: the up buffer; otherwise ignored */
+    int32_t reserved;    /* 0 */
+    const void *norm_w;  /* MBQ_PRO_WRMSNORM_QUANT: device bf16 [K] norm weights,
+                            16-byte aligned; otherwise ignored */
 } mbq_op;
 
-/* Workspace bytes for the walk (fused and unfused forms), or a negative
- * mbq_status (MBQ_ERR_PROGRAM for a malformed op list).  ops, buf_widths: host. */
+/* Workspace bytes for the walk (fused and unfused forms; only the unfused
+ * form's when the fused walk rejects the list, see mbq_sequence_prepare), or a
+ * negative mbq_status (MBQ_ERR_PROGRAM for a malformed op list).  ops,
+ * buf_widths: host. */
 int64_t mbq_sequence_workspace_bytes(const mbq_op *ops, int32_t n_ops,
                                      const int64_t *buf_widths, int32_t n_bufs, int64_t M);
 
@@ -171,6 +194,8 @@ typedef struct mbq_sequence_info {
     int32_t grid, lds_bytes;
     int64_t ws_bytes;
     int64_t plan_offset;
+    int32_t full;        /* 1: the walk uses the weighted-RMSNorm or SwiGLU prologue */
+    int32_t reserved;
 } mbq_sequence_info;
 
 /* Validate the walk and write its execution plan into ws (device), then wait
@@ -180,8 +205,13 @@ typedef struct mbq_sequence_info {
  * MBQ_ERR_PROGRAM if an op reads a buffer index out of range, N != width of
  * out_buf, K > width of in_buf, a phase writes its own input or the same
  * buffer twice, the bit widths differ, or one op's output is read with two
- * different K.  The plan stays valid while ws, bufs and the packed weights
- * stay where they are. */
+ * different K.  The fused walk also returns MBQ_ERR_PROGRAM (the unfused call
+ * takes such lists) when the consumers of one op's output disagree on the norm
+ * weights, or use a weighted RMSNorm and no weights, or when a SwiGLU op's
+ * gate and up buffers are not either both written before the walk or both
+ * written by ops of one phase with equal N whose outputs nothing else in the
+ * walk reads.  The plan stays valid while ws, bufs, the packed weights and
+ * the norm weights stay where they are. */
 int mbq_sequence_prepare(const mbq_op *ops, int32_t n_ops, void *const *bufs,
                          const int64_t *buf_widths, int32_t n_bufs, int64_t M, void *ws,
                          int64_t ws_bytes, void *stream, mbq_sequence_info *info);

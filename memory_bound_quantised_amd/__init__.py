@@ -23,7 +23,8 @@ STATUS = {0: "MBQ_OK", -1: "MBQ_ERR_NULL", -2: "MBQ_ERR_SHAPE", -3: "MBQ_ERR_BIT
 
 EXPORTS = ["mbq_status_string", "mbq_last_hip_error", "mbq_version", "mbq_packed_bytes",
            "mbq_pack_weights", "mbq_unpack_weights", "mbq_quantize_act",
-           "mbq_rmsnorm_quantize_act", "mbq_linear_workspace_bytes", "mbq_w4a8_linear",
+           "mbq_rmsnorm_quantize_act", "mbq_wrmsnorm_quantize_act", "mbq_swiglu_quantize_act",
+           "mbq_linear_workspace_bytes", "mbq_w4a8_linear",
            "mbq_w6a8_linear", "mbq_linear_group_acc", "mbq_sequence_workspace_bytes",
            "mbq_sequence_prepare", "mbq_sequence_run", "mbq_sequence_check", "mbq_layer_sequence",
            "mbq_layer_sequence_unfused"]
@@ -41,13 +42,17 @@ class MbqError(RuntimeError):
 class MbqOp(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("prologue", ctypes.c_int32), ("N", ctypes.c_int64),
                 ("K", ctypes.c_int64), ("packed", ctypes.c_void_p), ("in_buf", ctypes.c_int32),
-                ("out_buf", ctypes.c_int32)]
+                ("out_buf", ctypes.c_int32), ("in_buf2", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("norm_w", ctypes.c_void_p)]
+
+
+PRO_QUANT, PRO_RMSNORM_QUANT, PRO_WRMSNORM_QUANT, PRO_SWIGLU_QUANT = 0, 1, 2, 3
 
 
 class MbqSequenceInfo(ctypes.Structure):
     _fields_ = [("magic", ctypes.c_uint64), ("bits", ctypes.c_int32), ("M", ctypes.c_int32),
                 ("grid", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("ws_bytes", ctypes.c_int64),
-                ("plan_offset", ctypes.c_int64)]
+                ("plan_offset", ctypes.c_int64), ("full", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _lib_handle = None
@@ -72,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.mbq_unpack_weights.argtypes = [ctypes.c_int, I64, I64, P, P, P, P]
         L.mbq_quantize_act.argtypes = [I64, I64, P, P, P, P]
         L.mbq_rmsnorm_quantize_act.argtypes = [I64, I64, P, P, P, P]
+        L.mbq_wrmsnorm_quantize_act.argtypes = [I64, I64, P, P, P, P, P]
+        L.mbq_swiglu_quantize_act.argtypes = [I64, I64, P, P, P, P, P, P]
         L.mbq_linear_workspace_bytes.argtypes = [ctypes.c_int, I64, I64, I64]
         L.mbq_linear_workspace_bytes.restype = I64
         for fn in (L.mbq_w4a8_linear, L.mbq_w6a8_linear):
@@ -154,14 +161,25 @@ def unpack_weights(bits: int, packed, N: int, K: int):
     return canon, scales
 
 
-def quantize_act(x_bf16, rmsnorm: bool = False):
-    """bf16 [M][K] -> (q int8 [M][K], s fp32 [M])."""
+def quantize_act(x_bf16, rmsnorm: bool = False, norm_w=None, up=None, h_out=None):
+    """bf16 [M][K] -> (q int8 [M][K], s fp32 [M]) after the optional prologue:
+    rmsnorm (weightless), norm_w (bf16 [K]: weighted RMSNorm), or up (bf16
+    [M][K]: SwiGLU of x_bf16 as the gate; h_out receives the gated values)."""
     import torch
     M, K = x_bf16.shape
     q = torch.empty((M, K), dtype=torch.int8, device=x_bf16.device)
     s = torch.empty((M,), dtype=torch.float32, device=x_bf16.device)
-    fn = lib().mbq_rmsnorm_quantize_act if rmsnorm else lib().mbq_quantize_act
-    _check("mbq_quantize_act", fn(M, K, _ptr(x_bf16), _ptr(q), _ptr(s), _stream()))
+    L = lib()
+    if up is not None:
+        _check("mbq_swiglu_quantize_act", L.mbq_swiglu_quantize_act(
+            M, K, _ptr(x_bf16), _ptr(up), _ptr(h_out) if h_out is not None else None, _ptr(q), _ptr(s),
+            _stream()))
+    elif norm_w is not None:
+        _check("mbq_wrmsnorm_quantize_act", L.mbq_wrmsnorm_quantize_act(
+            M, K, _ptr(x_bf16), _ptr(norm_w), _ptr(q), _ptr(s), _stream()))
+    else:
+        fn = L.mbq_rmsnorm_quantize_act if rmsnorm else L.mbq_quantize_act
+        _check("mbq_quantize_act", fn(M, K, _ptr(x_bf16), _ptr(q), _ptr(s), _stream()))
     return q, s
 
 
@@ -201,7 +219,9 @@ class LayerSequence:
     """A decode-step walk: an op list over bf16 buffers.
 
     ops: iterable of dicts with bits, prologue, N, K, packed (uint8 tensor),
-    in_buf, out_buf.  bufs: list of bf16 tensors [M][width].  The workspace is
+    in_buf, out_buf, and in_buf2 (SwiGLU's up buffer) or norm_w (bf16 tensor
+    [K], weighted RMSNorm) where the prologue needs them.  bufs: list of bf16
+    tensors [M][width].  The workspace is
     allocated (zero-filled) once here.  fused=True prepares the persistent
     kernel's plan once (mbq_sequence_prepare) and run() is one launch
     (mbq_sequence_run); fused=False runs mbq_layer_sequence_unfused.
@@ -211,11 +231,13 @@ class LayerSequence:
         self.M = M
         self.fused = fused
         self.bufs = list(bufs)
-        self._keep = [o["packed"] for o in ops]
+        self._keep = [o["packed"] for o in ops] + [o["norm_w"] for o in ops if o.get("norm_w") is not None]
         arr = (MbqOp * len(ops))()
         for i, o in enumerate(ops):
+            nw = o.get("norm_w")
             arr[i] = MbqOp(o["bits"], o["prologue"], o["N"], o["K"], o["packed"].data_ptr(),
-                           o["in_buf"], o["out_buf"])
+                           o["in_buf"], o["out_buf"], o.get("in_buf2", -1), 0,
+                           nw.data_ptr() if nw is not None else None)
         self._ops = arr
         self._n_ops = len(ops)
         self._widths = (ctypes.c_int64 * len(bufs))(*[b.shape[1] for b in bufs])

@@ -85,14 +85,21 @@ int64_t analyse_program(const mbq_op *ops, int32_t n_ops, const int64_t *widths,
         if (!bits_ok(o.bits)) return MBQ_ERR_BITS;
         if (!o.packed) return MBQ_ERR_NULL;
         if (!aligned(o.packed, 256)) return MBQ_ERR_ALIGN;
-        if (o.prologue != MBQ_PRO_QUANT && o.prologue != MBQ_PRO_RMSNORM_QUANT) return MBQ_ERR_PROGRAM;
+        if (o.prologue < MBQ_PRO_QUANT || o.prologue > MBQ_PRO_SWIGLU_QUANT) return MBQ_ERR_PROGRAM;
         if (!k_ok(o.K) || !n_ok(o.N)) return MBQ_ERR_SHAPE;
         if (o.in_buf < 0 || o.in_buf >= n_bufs || o.out_buf < 0 || o.out_buf >= n_bufs)
             return MBQ_ERR_PROGRAM;
         if (o.out_buf == o.in_buf) return MBQ_ERR_PROGRAM;
         if (o.K > widths[o.in_buf] || o.N != widths[o.out_buf]) return MBQ_ERR_PROGRAM;
-        const bool joins = !ph.empty() && ops[ph.back().first].in_buf == o.in_buf &&
-                           ops[ph.back().first].prologue == o.prologue && ops[ph.back().first].K == o.K;
+        const bool swiglu = o.prologue == MBQ_PRO_SWIGLU_QUANT, wnorm = o.prologue == MBQ_PRO_WRMSNORM_QUANT;
+        if (swiglu && (o.in_buf2 < 0 || o.in_buf2 >= n_bufs || o.in_buf2 == o.out_buf ||
+                       o.in_buf2 == o.in_buf || o.K > widths[o.in_buf2]))
+            return MBQ_ERR_PROGRAM;
+        if (wnorm && !o.norm_w) return MBQ_ERR_NULL;
+        if (wnorm && !aligned(o.norm_w, 16)) return MBQ_ERR_ALIGN;
+        const mbq_op &f = ops[ph.empty() ? i : ph.back().first];
+        const bool joins = !ph.empty() && f.in_buf == o.in_buf && f.prologue == o.prologue && f.K == o.K &&
+                           (!swiglu || f.in_buf2 == o.in_buf2) && (!wnorm || f.norm_w == o.norm_w);
         if (joins) {
             for (int32_t j = ph.back().first; j < i; ++j)
                 if (ops[j].out_buf == o.out_buf) return MBQ_ERR_PROGRAM;
@@ -163,24 +170,36 @@ int mbq_unpack_weights(int bits, int64_t N, int64_t K, const void *packed, void 
     return e == hipSuccess ? MBQ_OK : hip_fail(e);
 }
 
-static int quant_common(bool norm, int64_t M, int64_t K, const void *x, int8_t *q, float *s,
-                        void *stream) {
+static int quant_common(int pro, int64_t M, int64_t K, const void *x, const void *u, const void *w, void *h,
+                        int8_t *q, float *s, void *stream) {
     if (!x || !q || !s) return MBQ_ERR_NULL;
+    if ((pro == MBQ_PRO_SWIGLU_QUANT && !u) || (pro == MBQ_PRO_WRMSNORM_QUANT && !w)) return MBQ_ERR_NULL;
     if (!m_ok(M) || !k_ok(K)) return MBQ_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return MBQ_ERR_ALIGN;
+    if ((u && !aligned(u, 16)) || (w && !aligned(w, 16)) || (h && !aligned(h, 16))) return MBQ_ERR_ALIGN;
     int st = check_device();
     if (st) return st;
-    hipError_t e = launch_prologue_quant(norm, M, K, x, K, q, s, (hipStream_t)stream);
+    hipError_t e = launch_prologue_quant(pro, M, K, x, K, u, K, w, h, q, s, (hipStream_t)stream);
     return e == hipSuccess ? MBQ_OK : hip_fail(e);
 }
 
 int mbq_quantize_act(int64_t M, int64_t K, const void *x_bf16, int8_t *q, float *s, void *stream) {
-    return quant_common(false, M, K, x_bf16, q, s, stream);
+    return quant_common(MBQ_PRO_QUANT, M, K, x_bf16, nullptr, nullptr, nullptr, q, s, stream);
 }
 
 int mbq_rmsnorm_quantize_act(int64_t M, int64_t K, const void *x_bf16, int8_t *q, float *s,
                              void *stream) {
-    return quant_common(true, M, K, x_bf16, q, s, stream);
+    return quant_common(MBQ_PRO_RMSNORM_QUANT, M, K, x_bf16, nullptr, nullptr, nullptr, q, s, stream);
+}
+
+int mbq_wrmsnorm_quantize_act(int64_t M, int64_t K, const void *x_bf16, const void *w_bf16, int8_t *q,
+                              float *s, void *stream) {
+    return quant_common(MBQ_PRO_WRMSNORM_QUANT, M, K, x_bf16, nullptr, w_bf16, nullptr, q, s, stream);
+}
+
+int mbq_swiglu_quantize_act(int64_t M, int64_t K, const void *g_bf16, const void *u_bf16, void *h_bf16,
+                            int8_t *q, float *s, void *stream) {
+    return quant_common(MBQ_PRO_SWIGLU_QUANT, M, K, g_bf16, u_bf16, nullptr, h_bf16, q, s, stream);
 }
 
 int64_t mbq_linear_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K) {
@@ -228,8 +247,8 @@ int64_t mbq_sequence_workspace_bytes(const mbq_op *ops, int32_t n_ops, const int
     } else {
         n_cu = 256;
     }
+    // a list the fused walk rejects still runs unfused
     const int64_t fused = build_sequence_plan(ops, n_ops, nullptr, buf_widths, n_bufs, M, n_cu, nullptr, nullptr);
-    if (fused < 0) return fused;
     return fused > unfused ? fused : unfused;
 }
 
@@ -247,6 +266,9 @@ int mbq_sequence_prepare(const mbq_op *ops, int32_t n_ops, void *const *bufs, co
     }
     if (!ws) return MBQ_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return MBQ_ERR_ALIGN;
+    // lists the fused walk rejects are refused before anything touches the device
+    const int64_t pre = build_sequence_plan(ops, n_ops, nullptr, buf_widths, n_bufs, M, 256, nullptr, nullptr);
+    if (pre < 0) return (int)pre;
     int st = check_device();
     if (st) return st;
     int n_cu = 0;
@@ -270,6 +292,7 @@ int mbq_sequence_prepare(const mbq_op *ops, int32_t n_ops, void *const *bufs, co
     info->lds_bytes = b.lds_bytes;
     info->ws_bytes = need;
     info->plan_offset = b.plan_offset;
+    info->full = b.full ? 1 : 0;
     return MBQ_OK;
 }
 
@@ -280,7 +303,7 @@ int mbq_sequence_run(const mbq_sequence_info *info, void *ws, void *stream) {
         return MBQ_ERR_PROGRAM;
     if (!aligned(ws, 256)) return MBQ_ERR_ALIGN;
     uint32_t gen = (g_generation.fetch_add(1, std::memory_order_relaxed) % ((1u << 22) - 1)) + 1;
-    hipError_t e = launch_sequence(info->bits, info->M, info->grid, info->lds_bytes,
+    hipError_t e = launch_sequence(info->bits, info->M, info->full != 0, info->grid, info->lds_bytes,
                                    (const char *)ws + info->plan_offset, (uint32_t *)ws, gen,
                                    (hipStream_t)stream);
     return e == hipSuccess ? MBQ_OK : hip_fail(e);
@@ -331,8 +354,12 @@ int mbq_layer_sequence_unfused(const mbq_op *ops, int32_t n_ops, void *const *bu
     void *lin_ws = (char *)ws + align256(M * k_max) + 256;
     for (const Phase &p : phases) {
         const mbq_op &o0 = ops[p.first];
-        hipError_t e = launch_prologue_quant(o0.prologue == MBQ_PRO_RMSNORM_QUANT, M, o0.K,
-                                             bufs[o0.in_buf], buf_widths[o0.in_buf], q, s, hs);
+        const bool swiglu = o0.prologue == MBQ_PRO_SWIGLU_QUANT;
+        hipError_t e = launch_prologue_quant(o0.prologue, M, o0.K, bufs[o0.in_buf], buf_widths[o0.in_buf],
+                                             swiglu ? bufs[o0.in_buf2] : nullptr,
+                                             swiglu ? buf_widths[o0.in_buf2] : 0,
+                                             o0.prologue == MBQ_PRO_WRMSNORM_QUANT ? o0.norm_w : nullptr, nullptr,
+                                             q, s, hs);
         if (e != hipSuccess) return hip_fail(e);
         for (int32_t i = p.first; i < p.first + p.count; ++i) {
             const mbq_op &o = ops[i];

@@ -81,6 +81,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// SwiGLU gate of one element, rounded to bf16 and returned as fp32:
+// silu(g) * u with silu(g) = g / (1 + exp(-g)) in fp32 (g -> -inf gives -0).
+__device__ __forceinline__ float swiglu_bf16f(float g, float u) {
+    const float sg = g / (1.0f + expf(-g));
+    return bf16_bits_to_f32(f32_to_bf16_bits(sg * u));
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
 }

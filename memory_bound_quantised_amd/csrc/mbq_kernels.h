@@ -15,10 +15,13 @@ hipError_t launch_pack(int bits, int64_t N, int64_t K, const void *canon, const 
 hipError_t launch_unpack(int bits, int64_t N, int64_t K, const void *packed, void *canon,
                          void *scales, hipStream_t s);
 
-// Per-row quantisation (optionally after the weightless RMSNorm) of columns
-// [0, K) of x (bf16, row stride x_stride elements).
-hipError_t launch_prologue_quant(bool rmsnorm, int64_t M, int64_t K, const void *x, int64_t x_stride,
-                                 int8_t *q, float *s, hipStream_t st);
+// Per-row quantisation of columns [0, K) of x (bf16, row stride x_stride
+// elements) after prologue `pro` (an MBQ_PRO_* value): w is the weighted
+// norm's bf16 [K] weights; u (row stride u_stride) the SwiGLU up rows, h an
+// optional bf16 [M][K] copy of the SwiGLU output.
+hipError_t launch_prologue_quant(int pro, int64_t M, int64_t K, const void *x, int64_t x_stride,
+                                 const void *u, int64_t u_stride, const void *w, void *h, int8_t *q,
+                                 float *s, hipStream_t st);
 
 // Per-op skinny linear: work split, workspace size and launch.
 struct LinearPlan {
@@ -41,6 +44,7 @@ struct SeqBuild {
     int grid = 0;
     int lds_bytes = 0;
     int bits = 0;
+    bool full = false;           // the walk needs the weighted-norm / SwiGLU form of the kernel
     std::vector<uint8_t> blob;   // plan bytes to copy to ws + plan_offset
 };
 // Validates the op list and lays out the workspace; with ws and bufs also fills
@@ -48,7 +52,11 @@ struct SeqBuild {
 int64_t build_sequence_plan(const struct mbq_op *ops, int32_t n_ops, void *const *bufs,
                             const int64_t *widths, int32_t n_bufs, int64_t M, int n_cu, uint8_t *ws,
                             SeqBuild *out);
-hipError_t launch_sequence(int bits, int64_t M, int grid, int lds_bytes, const void *plan, uint32_t *err,
+// The walk kernel of each form for (bits, M): the plain form (prologues 0 and
+// 1 only) and the full one (also weighted RMSNorms and SwiGLU inputs).
+const void *seq_kernel_plain(int bits, int64_t M);
+const void *seq_kernel_full(int bits, int64_t M);
+hipError_t launch_sequence(int bits, int64_t M, bool full, int grid, int lds_bytes, const void *plan, uint32_t *err,
                            uint32_t gen, hipStream_t st);
 
 }  // namespace mbq

@@ -20,14 +20,15 @@ constexpr int kCounterStride = 32;             // u32 words between phase counte
 constexpr int kStatReplicas = 8;               // copies of the stats records, one per XCD
 constexpr int kMaxPhases = 1000;               // < 2^kRunPhaseBits
 constexpr int kMetaMaxBytes = 4096;           // phase record + workgroup block, per LDS slot
-constexpr uint64_t kPlanMagic = 0x6d62712d73657132ull;  // "mbq-seq2"
+constexpr uint64_t kPlanMagic = 0x6d62712d73657133ull;  // "mbq-seq3"
 
 // Every value that one wave hands to another travels in a 64-bit word whose
 // high half is the epoch tag of the phase that wrote it, so a single load
 // both fetches and validates it.
 //
 // Stats record of one row block of an op's output (rows n < stats_cols), for
-// activation row m: word 3m = max|y| bits, 3m+1 / 3m+2 = low / high half of
+// activation row m: word 3m = max|y| bits (max|y w| when the consumer applies
+// a weighted RMSNorm with weights w), 3m+1 / 3m+2 = low / high half of
 // the fp64 sum of y^2; each word's high half is the tag.  The records are
 // stored word-major (word c of record r at stats[c * stat_stride + r]) so that
 // a wave reading 64 consecutive records fetches contiguous memory, and in
@@ -35,9 +36,13 @@ constexpr uint64_t kPlanMagic = 0x6d62712d73657132ull;  // "mbq-seq2"
 // every record, and a workgroup reads the copy of its XCD (workgroup index
 // mod 8), so no line is polled by more than one eighth of the grid.
 
-struct SeqPhase {            // 64 bytes
+struct SeqPhase {            // 72 bytes
     const uint32_t *in;      // bf16 pairs of the input rows (inputs written before the launch)
-    const uint64_t *in_xt;   // tagged copy written by the producer op, or null
+    // Tagged copy of the input, or null: written by the producer op (for a
+    // SwiGLU input, by the gate/up pair's finaliser, or by the kernel-start
+    // pass when both halves come from before the launch: the gated values).
+    const uint64_t *in_xt;
+    const uint32_t *norm_w;  // weighted RMSNorm: the norm's weights as bf16 pairs, else null
     int32_t in_stride2;      // input row stride in 32-bit words (and in tagged words)
     int32_t K, prologue;
     int32_t in_nrec;         // stats records describing the input: ceil(K / 64)
@@ -79,23 +84,35 @@ struct SeqWgSeg {            // a segment the workgroup's tiles touch
     int32_t cidx;            // its contribution (partial slot) in the phase's partial area
     uint8_t slot[kSeqWaves]; // each wave's LDS slot holding a part of it (0xFF: none)
 };
-struct SeqFin {              // a row block the workgroup finalises (48 bytes)
+struct SeqFin {              // a row block the workgroup finalises (64 bytes)
     uint32_t *out;           // its first bf16 pair in output row 0
+    // A gate row block paired with the same rows of the up projection (both
+    // ops of one phase, read only by one SwiGLU consumer): out2 is the up
+    // block's first pair, and xt and stats describe silu(gate) * up.  Else null.
+    uint32_t *out2;
     uint64_t *xt;            // same in the tagged copy, or null
     uint64_t *stats;         // word 0 of its stats record, or null
+    const uint16_t *norm_w;  // consumer's RMSNorm weights at these rows (stats hold max |y w|), or null
     int32_t row_words;       // output row stride in pairs (N / 2)
     int32_t rows;            // valid rows (<= 64, even)
     int32_t stat_rows;       // rows feeding the stats (0 .. rows)
     int32_t c0, nc;          // its contributions, summed in this order
-    int32_t pad;
+    int32_t nc_2;            // the up block's contributions, next in the area (pairs only)
 };
 
 struct SeqExt {              // an input no op of the walk writes: stats at kernel start
     const uint32_t *in;
-    int32_t in_stride2, K;
+    // SwiGLU consumer: the up input, and where the gated values silu(in) * in2
+    // go (tagged, row stride K / 2 words), which the stats then describe; else null.
+    const uint32_t *in2;
+    uint64_t *xt;
+    const uint16_t *norm_w;  // weighted-RMSNorm consumer: its weights (stats hold max |x w|), else null
+    int32_t in_stride2, in2_stride2, K, pad;
     int64_t rec;
     int32_t n_rb, rb_first;  // its row-block records are blocks rb_first.. of the pre-pass
 };
+
+static_assert(sizeof(SeqPhase) == 72 && sizeof(SeqFin) == 64 && sizeof(SeqExt) == 64, "plan record sizes");
 
 struct SeqPlan {
     uint64_t magic;
@@ -107,6 +124,11 @@ struct SeqPlan {
     int32_t blk_bytes;       // bytes of one (phase, workgroup) block
     int32_t seg_cap;         // SeqWgSeg entries per block
     int32_t part_stride;     // contributions per parity half of the partial area
+    // 1: the walk has weighted RMSNorms or SwiGLU inputs and runs the form of
+    // the kernel that handles them (the other form carries none of their
+    // instructions or registers); 0: only the plain and weightless-norm prologues
+    int32_t full;
+    int32_t pad;
     const SeqPhase *phases;
     const SeqExt *ext;
     uint32_t *err;           // nonzero after a wait gave up

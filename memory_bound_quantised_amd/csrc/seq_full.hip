@@ -1,0 +1,20 @@
+// The full form of the fused decode-step walk kernel (seq_walk.h): every
+// (bit width, M) instantiation, and its entry-point table.
+#include "seq_walk.h"
+
+namespace mbq {
+
+const void *seq_kernel_full(int bits, int64_t M) {
+#define MBQ_PICK(B, MM) return reinterpret_cast<const void *>(&seq_kernel<B, MM, true>)
+    if (bits == 4) {
+        switch (M) { case 1: MBQ_PICK(4, 1); case 2: MBQ_PICK(4, 2); case 3: MBQ_PICK(4, 3);
+                     case 4: MBQ_PICK(4, 4); case 5: MBQ_PICK(4, 5); case 6: MBQ_PICK(4, 6);
+                     case 7: MBQ_PICK(4, 7); default: MBQ_PICK(4, 8); }
+    }
+    switch (M) { case 1: MBQ_PICK(6, 1); case 2: MBQ_PICK(6, 2); case 3: MBQ_PICK(6, 3);
+                 case 4: MBQ_PICK(6, 4); case 5: MBQ_PICK(6, 5); case 6: MBQ_PICK(6, 6);
+                 case 7: MBQ_PICK(6, 7); default: MBQ_PICK(6, 8); }
+#undef MBQ_PICK
+}
+
+}  // namespace mbq

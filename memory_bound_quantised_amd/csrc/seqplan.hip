@@ -83,14 +83,21 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
         if (o.bits != bits) return MBQ_ERR_PROGRAM;   // one bit width per walk
         if (!o.packed) return MBQ_ERR_NULL;
         if (((uintptr_t)o.packed & 255) != 0) return MBQ_ERR_ALIGN;
-        if (o.prologue != MBQ_PRO_QUANT && o.prologue != MBQ_PRO_RMSNORM_QUANT) return MBQ_ERR_PROGRAM;
+        if (o.prologue < MBQ_PRO_QUANT || o.prologue > MBQ_PRO_SWIGLU_QUANT) return MBQ_ERR_PROGRAM;
         if (o.K < kGroup || o.K % kGroup || o.K > ((int64_t)1 << 24) || o.N < 1 || o.N > kMaxN)
             return MBQ_ERR_SHAPE;
         if (o.in_buf < 0 || o.in_buf >= n_bufs || o.out_buf < 0 || o.out_buf >= n_bufs) return MBQ_ERR_PROGRAM;
         if (o.out_buf == o.in_buf) return MBQ_ERR_PROGRAM;
         if (o.K > widths[o.in_buf] || o.N != widths[o.out_buf]) return MBQ_ERR_PROGRAM;
-        const bool joins = !ph.empty() && ops[ph.back().first].in_buf == o.in_buf &&
-                           ops[ph.back().first].prologue == o.prologue && ops[ph.back().first].K == o.K;
+        const bool swiglu = o.prologue == MBQ_PRO_SWIGLU_QUANT, wnorm = o.prologue == MBQ_PRO_WRMSNORM_QUANT;
+        if (swiglu && (o.in_buf2 < 0 || o.in_buf2 >= n_bufs || o.in_buf2 == o.out_buf || o.in_buf2 == o.in_buf ||
+                       o.K > widths[o.in_buf2]))
+            return MBQ_ERR_PROGRAM;
+        if (wnorm && !o.norm_w) return MBQ_ERR_NULL;
+        if (wnorm && ((uintptr_t)o.norm_w & 15) != 0) return MBQ_ERR_ALIGN;
+        const mbq_op *f = ph.empty() ? nullptr : &ops[ph.back().first];
+        const bool joins = f && f->in_buf == o.in_buf && f->prologue == o.prologue && f->K == o.K &&
+                           (!swiglu || f->in_buf2 == o.in_buf2) && (!wnorm || f->norm_w == o.norm_w);
         if (joins) {
             for (int j = ph.back().first; j < i; ++j)
                 if (ops[j].out_buf == o.out_buf) return MBQ_ERR_PROGRAM;
@@ -101,25 +108,53 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     }
     const int n_ph = (int)ph.size();
     if (n_ph > kMaxPhases) return MBQ_ERR_PROGRAM;
+    bool full = false;
+    for (int32_t i = 0; i < n_ops; ++i)
+        full |= ops[i].prologue == MBQ_PRO_WRMSNORM_QUANT || ops[i].prologue == MBQ_PRO_SWIGLU_QUANT;
 
     // ---- producers, stats records and external inputs
+    // Every consumer of an op must agree on the statistics it needs: the
+    // columns (its K) and the weights of a weighted RMSNorm (max |y w|).  A
+    // SwiGLU phase whose two inputs are written by the walk needs them written
+    // by two ops of one phase with equal N, read by nothing else: the pair's
+    // finaliser then hands over silu(gate) * up.  A SwiGLU phase whose two
+    // inputs both come from before the launch gates them as it quantises.
     std::vector<int> stats_cols(n_ops, 0), phase_of(n_ops, 0), in_prod(n_ph, -1), in_ext(n_ph, -1);
+    std::vector<int> uses(n_ops, 0), pair_of(n_ops, -1);   // pair_of[gate op] = its up op
+    std::vector<char> pair_up(n_ops, 0);
+    std::vector<const void *> stats_w(n_ops, nullptr);
     std::vector<int> last_writer(n_bufs, -1);
-    struct Ext { int buf; int64_t K; int64_t rec; int n_rb, rb_first; };
+    struct Ext { int buf, buf2; int64_t K; const void *w; int64_t rec, xt; int n_rb, rb_first; };
     std::vector<Ext> ext;
     for (int p = 0; p < n_ph; ++p) {
         const mbq_op &o0 = ops[ph[p].first];
+        const bool swiglu = o0.prologue == MBQ_PRO_SWIGLU_QUANT;
+        const void *cw = o0.prologue == MBQ_PRO_WRMSNORM_QUANT ? o0.norm_w : nullptr;
         const int prod = last_writer[o0.in_buf];
+        const int prod2 = swiglu ? last_writer[o0.in_buf2] : -1;
+        if (swiglu && (prod >= 0) != (prod2 >= 0)) return MBQ_ERR_PROGRAM;
         if (prod >= 0) {
-            if (stats_cols[prod] != 0 && stats_cols[prod] != o0.K) return MBQ_ERR_PROGRAM;
+            if (swiglu) {
+                if (phase_of[prod] != phase_of[prod2] || ops[prod].N != ops[prod2].N) return MBQ_ERR_PROGRAM;
+                if (uses[prod] || uses[prod2]) return MBQ_ERR_PROGRAM;
+                pair_of[prod] = prod2;
+                pair_up[prod2] = 1;
+                uses[prod2]++;
+            } else if (pair_of[prod] >= 0 || pair_up[prod]) {
+                return MBQ_ERR_PROGRAM;
+            }
+            if (uses[prod] && (stats_cols[prod] != o0.K || stats_w[prod] != cw)) return MBQ_ERR_PROGRAM;
+            uses[prod]++;
             stats_cols[prod] = (int)o0.K;
+            stats_w[prod] = cw;
             in_prod[p] = prod;
         } else {
+            const int buf2 = swiglu ? o0.in_buf2 : -1;
             int e = -1;
             for (size_t j = 0; j < ext.size(); ++j)
-                if (ext[j].buf == o0.in_buf && ext[j].K == o0.K) e = (int)j;
+                if (ext[j].buf == o0.in_buf && ext[j].buf2 == buf2 && ext[j].K == o0.K && ext[j].w == cw) e = (int)j;
             if (e < 0) {
-                ext.push_back(Ext{o0.in_buf, o0.K, 0, (int)((o0.K + 63) / 64), 0});
+                ext.push_back(Ext{o0.in_buf, buf2, o0.K, cw, 0, -1, (int)((o0.K + 63) / 64), 0});
                 e = (int)ext.size() - 1;
             }
             in_ext[p] = e;
@@ -140,6 +175,10 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
         }
     int ext_rb = 0;
     for (Ext &e : ext) {
+        if (e.buf2 >= 0) {                         // gated values: M rows of K/2 words
+            e.xt = n_xt;
+            n_xt += M * (e.K / 2);
+        }
         e.rec = n_rec;
         e.rb_first = ext_rb;
         n_rec += e.n_rb;
@@ -226,8 +265,17 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
 
     // ---- contributions: segment (kc, rb) gets one partial per workgroup
     // touching it; a row block's partials are contiguous, in (kc, workgroup)
-    // order.
-    std::vector<std::vector<int>> seg_c0(n_ph), seg_wg0(n_ph), rb_c0(n_ph), rb_nc(n_ph), rb_fin(n_ph);
+    // order.  Finalising units: a row block, or a gate row block together
+    // with the same rows of its up block, whose partials follow the gate's so
+    // that the unit's partials are one contiguous range.
+    auto op_of = [&](int p, int rb) {
+        int op = ph[p].first;
+        while (op + 1 < ph[p].first + ph[p].count && rb >= rb_base[p][op + 1 - ph[p].first]) ++op;
+        return op;
+    };
+    struct Unit { int rb, rb2; };
+    std::vector<std::vector<Unit>> units(n_ph);
+    std::vector<std::vector<int>> seg_c0(n_ph), seg_wg0(n_ph), rb_c0(n_ph), rb_nc(n_ph), unit_fin(n_ph);
     int part_stride = 1, seg_cap = 1, fin_cap = 1;
     for (int p = 0; p < n_ph; ++p) {
         const PhaseGeom &g = geo[p];
@@ -236,9 +284,15 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
         seg_wg0[p].assign(nseg, 0);
         rb_c0[p].assign(g.R, 0);
         rb_nc[p].assign(g.R, 0);
-        rb_fin[p].assign(g.R, 0);
-        int c = 0;
         for (int rb = 0; rb < g.R; ++rb) {
+            const int op = op_of(p, rb);
+            if (pair_up[op]) continue;   // finalised with its gate block
+            const int rb2 = pair_of[op] >= 0 ? rb_base[p][pair_of[op] - ph[p].first] + (rb - rb_base[p][op - ph[p].first])
+                                             : -1;
+            units[p].push_back(Unit{rb, rb2});
+        }
+        int c = 0;
+        auto number = [&](int rb) {
             rb_c0[p][rb] = c;
             for (int kc = 0; kc < g.nkc; ++kc) {
                 const int t0 = kc * g.R * kChunkGroups + rb * g.chunk_len(kc);
@@ -247,20 +301,24 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
                 seg_c0[p][kc * g.R + rb] = c;
                 seg_wg0[p][kc * g.R + rb] = wga;
                 c += wgb - wga + 1;
-
             }
             rb_nc[p][rb] = c - rb_c0[p][rb];
+        };
+        for (const Unit &u : units[p]) {
+            number(u.rb);
+            if (u.rb2 >= 0) number(u.rb2);
         }
         part_stride = std::max(part_stride, c);
-        // row block rb is finalised by the finalising workgroups in turn
+        // the units are finalised by the finalising workgroups in turn
         {
             std::vector<int> fwg;
             for (int wg = 0; wg < grid; ++wg)
                 if (is_final_wg(wg, grid)) fwg.push_back(wg);
-            for (int rb = 0; rb < g.R; ++rb) rb_fin[p][rb] = fwg[rb % fwg.size()];
+            unit_fin[p].assign(units[p].size(), 0);
+            for (size_t u = 0; u < units[p].size(); ++u) unit_fin[p][u] = fwg[u % fwg.size()];
         }
         std::vector<int> nfin(grid, 0);
-        for (int rb = 0; rb < g.R; ++rb) fin_cap = std::max(fin_cap, ++nfin[rb_fin[p][rb]]);
+        for (size_t u = 0; u < units[p].size(); ++u) fin_cap = std::max(fin_cap, ++nfin[unit_fin[p][u]]);
         for (int wg = 0; wg * kSeqWaves < g.W; ++wg) {
             const int t0 = g.start(wg * kSeqWaves), t1 = g.start(std::min((wg + 1) * kSeqWaves, g.W)) - 1;
             if (t1 >= t0) seg_cap = std::max(seg_cap, g.segment(t1) - g.segment(t0) + 1);
@@ -297,6 +355,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     out->grid = grid;
     out->lds_bytes = (int)lds;
     out->bits = bits;
+    out->full = full;
     out->plan_offset = off_plan;
     out->blob.assign(total - off_plan, 0);
     if (!ws || !bufs) return total;
@@ -317,6 +376,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     plan.blk_bytes = blk_bytes;
     plan.seg_cap = seg_cap;
     plan.part_stride = part_stride;
+    plan.full = full ? 1 : 0;
     plan.phases = reinterpret_cast<const SeqPhase *>(dev(off_phases));
     plan.ext = reinterpret_cast<const SeqExt *>(dev(off_ext));
     plan.err = reinterpret_cast<uint32_t *>(dev(off_err));
@@ -335,6 +395,12 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
         memset(&e, 0, sizeof(e));
         e.in = reinterpret_cast<const uint32_t *>(bufs[ext[j].buf]);
         e.in_stride2 = (int32_t)(widths[ext[j].buf] / 2);
+        if (ext[j].buf2 >= 0) {
+            e.in2 = reinterpret_cast<const uint32_t *>(bufs[ext[j].buf2]);
+            e.in2_stride2 = (int32_t)(widths[ext[j].buf2] / 2);
+            e.xt = reinterpret_cast<uint64_t *>(dev(off_xt)) + ext[j].xt;
+        }
+        e.norm_w = reinterpret_cast<const uint16_t *>(ext[j].w);
         e.K = (int32_t)ext[j].K;
         e.rec = ext[j].rec;
         e.n_rb = ext[j].n_rb;
@@ -365,15 +431,18 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
         s.in_stride2 = (int32_t)(widths[o0.in_buf] / 2);
         s.K = (int32_t)o0.K;
         s.prologue = o0.prologue;
+        if (o0.prologue == MBQ_PRO_WRMSNORM_QUANT) s.norm_w = reinterpret_cast<const uint32_t *>(o0.norm_w);
         s.in_nrec = (int32_t)((o0.K + 63) / 64);
         if (in_prod[p] >= 0) {
             s.in_phase = phase_of[in_prod[p]];
             s.in_rec = op_rec[in_prod[p]];
             s.in_xt = xt_dev + op_xt[in_prod[p]];
         } else {
-            s.in_xt = nullptr;
+            const Ext &e = ext[in_ext[p]];
+            s.in_xt = e.xt >= 0 ? xt_dev + e.xt : nullptr;
+            if (e.xt >= 0) s.in_stride2 = (int32_t)(e.K / 2);
             s.in_phase = -1;
-            s.in_rec = ext[in_ext[p]].rec;
+            s.in_rec = e.rec;
         }
         s.wait_n = p >= 2 ? geo[p - 2].R : 0;
         s.wait_count = p >= 2 ? cnt_dev + (int64_t)(p - 2) * kCounterStride : nullptr;
@@ -382,7 +451,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
 
         // per-workgroup blocks
         std::vector<std::vector<int>> fins(grid);
-        for (int rb = 0; rb < g.R; ++rb) fins[rb_fin[p][rb]].push_back(rb);
+        for (size_t u = 0; u < units[p].size(); ++u) fins[unit_fin[p][u]].push_back((int)u);
         for (int wg = 0; wg < grid; ++wg) {
             std::vector<uint8_t> blk(blk_bytes, 0);
             SeqWgHead h;
@@ -414,9 +483,9 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
                     h.n_seg++;
                 }
             }
-            for (int rb : fins[wg]) {
-                int op = ph[p].first;
-                while (op + 1 < ph[p].first + ph[p].count && rb >= rb_base[p][op + 1 - ph[p].first]) ++op;
+            for (int u : fins[wg]) {
+                const int rb = units[p][u].rb, rb2 = units[p][u].rb2;
+                const int op = op_of(p, rb);
                 const int rbl = rb - rb_base[p][op - ph[p].first];
                 const int64_t N = ops[op].N;
                 SeqFin f;
@@ -432,6 +501,11 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
                     0, std::min<int64_t>(f.rows, std::min<int64_t>(N, stats_cols[op]) - (int64_t)rbl * 64));
                 f.c0 = rb_c0[p][rb];
                 f.nc = rb_nc[p][rb];
+                if (rb2 >= 0) {   // its partials follow the gate block's
+                    f.out2 = reinterpret_cast<uint32_t *>(bufs[ops[pair_of[op]].out_buf]) + rbl * 32;
+                    f.nc_2 = rb_nc[p][rb2];
+                }
+                if (f.stats && stats_w[op]) f.norm_w = reinterpret_cast<const uint16_t *>(stats_w[op]) + rbl * 64;
                 memcpy(blk.data() + fin_off + h.n_fin * sizeof(SeqFin), &f, sizeof(f));
                 h.n_fin++;
             }

@@ -18,8 +18,13 @@ multi-token-prediction verify step):
 * group scales: fp32 U(0.005, 0.02) rounded to fp16, one per 128 weights
   along K.
 
+* RMSNorm weights (the "real" dataflow's weighted norms): fp32 U(0.5, 1.5)
+  rounded to bf16, one per input column.
+
 Seeds: matrix i of a weight set uses seed ``1 + i`` (codes drawn first, then
-scales); an activation block of M rows uses seed ``1_000_000 + M``.
+scales); an activation block of M rows uses seed ``1_000_000 + M``; the norm
+weights in front of the attention (mlp) projections of layer l use seed
+``2_000_000 + 2 * l`` (``+ 1``).
 """
 from __future__ import annotations
 
@@ -48,6 +53,11 @@ def activations(M: int, K: int, seed: int | None = None) -> np.ndarray:
     """bf16 bit patterns, shape [M][K], from fp32 N(0,1)."""
     rng = _rng(ACT_SEED_BASE + M if seed is None else seed)
     return f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+
+
+def norm_weights(K: int, seed: int) -> np.ndarray:
+    """bf16 bit patterns [K] of RMSNorm weights, from fp32 U(0.5, 1.5)."""
+    return f32_to_bf16_bits(_rng(seed).uniform(0.5, 1.5, K).astype(np.float32))
 
 
 def canon_row_bytes(bits: int, K: int) -> int:
@@ -130,21 +140,56 @@ def weight_bytes(bits: int, shapes) -> int:
 #   q[:, :K_o] --quant--> o
 #   o --quant--> gate, up              (up written, unread: SwiGLU partner stand-in)
 #   gate --quant--> down --> x of the next layer
+#
+# The "real" dataflow (dataflow="swiglu") puts the norms and gate of a decoder
+# layer in front of the quantisations instead:
+#   x --weighted RMSNorm+quant--> q, k, v
+#   q[:, :K_o] --quant--> o
+#   o --weighted RMSNorm+quant--> gate, up
+#   (gate, up) --SwiGLU+quant--> down --> x of the next layer
 BUF_NAMES = ["x", "q", "k", "v", "o", "gate", "up", "down"]
 PRO_QUANT = 0
 PRO_RMSNORM_QUANT = 1
+PRO_WRMSNORM_QUANT = 2
+PRO_SWIGLU_QUANT = 3
+NORM_SEED_BASE = 2_000_000
 
 
-def layer_program(shapes_fn, n_layers: int, distinct_buffers: bool = False):
+def layer_program(shapes_fn, n_layers: int, distinct_buffers: bool = False, dataflow: str = "plain"):
     """Op list of a decode-step walk.
 
     Returns (ops, buf_widths) where ops are dicts with keys
-    name, K, N, in_buf, out_buf, prologue, matrix (index into the weight set).
+    name, K, N, in_buf, out_buf, prologue, matrix (index into the weight set),
+    and for dataflow="swiglu" also in_buf2 (the down op's up buffer) and
+    norm_seed (the seed of the op's RMSNorm weights, see norm_weights).
     With distinct_buffers every op writes a buffer of its own so that every
     intermediate survives the walk (used by parity tests).  Otherwise the eight
     buffers of BUF_NAMES are reused by every layer: layer 0 reads buffer "x",
     and every later layer reads the "down" buffer written by the layer before.
     """
+    if dataflow not in ("plain", "swiglu"):
+        raise ValueError("dataflow must be 'plain' or 'swiglu'")
+    sw = dataflow == "swiglu"
+    # (name, input, prologue); the input None is the layer's x
+    plan = (("q", None, PRO_WRMSNORM_QUANT if sw else PRO_RMSNORM_QUANT),
+            ("k", None, PRO_WRMSNORM_QUANT if sw else PRO_RMSNORM_QUANT),
+            ("v", None, PRO_WRMSNORM_QUANT if sw else PRO_RMSNORM_QUANT),
+            ("o", "q", PRO_QUANT),
+            ("gate", "o", PRO_WRMSNORM_QUANT if sw else PRO_QUANT),
+            ("up", "o", PRO_WRMSNORM_QUANT if sw else PRO_QUANT),
+            ("down", "gate", PRO_SWIGLU_QUANT if sw else PRO_QUANT))
+
+    def extra(layer, nm, buf_of):
+        if not sw:
+            return {}
+        if nm == "down":
+            return {"in_buf2": buf_of("up")}
+        if nm in ("q", "k", "v"):
+            return {"norm_seed": NORM_SEED_BASE + 2 * layer}
+        if nm in ("gate", "up"):
+            return {"norm_seed": NORM_SEED_BASE + 2 * layer + 1}
+        return {}
+
     shapes = shapes_fn()
     widths = {}
     ops = []
@@ -158,19 +203,12 @@ def layer_program(shapes_fn, n_layers: int, distinct_buffers: bool = False):
             for nm, K, N in shapes:
                 bufw.append(N)
                 idx[nm] = len(bufw) - 1
-            def add(nm, src, pro):
-                nonlocal mi
+            for nm, in_name, pro in plan:
                 K, N = next((k, n) for (n_, k, n) in shapes if n_ == nm)
-                ops.append(dict(name=f"L{layer}.{nm}", K=K, N=N, in_buf=src,
-                                out_buf=idx[nm], prologue=pro, matrix=mi))
+                src = cur_x if in_name is None else idx[in_name]
+                ops.append(dict(name=f"L{layer}.{nm}", K=K, N=N, in_buf=src, out_buf=idx[nm],
+                                prologue=pro, matrix=mi, **extra(layer, nm, lambda b: idx[b])))
                 mi += 1
-            add("q", cur_x, PRO_RMSNORM_QUANT)
-            add("k", cur_x, PRO_RMSNORM_QUANT)
-            add("v", cur_x, PRO_RMSNORM_QUANT)
-            add("o", idx["q"], PRO_QUANT)
-            add("gate", idx["o"], PRO_QUANT)
-            add("up", idx["o"], PRO_QUANT)
-            add("down", idx["gate"], PRO_QUANT)
             cur_x = idx["down"]
         return ops, bufw
     sh = {nm: (K, N) for nm, K, N in shapes}
@@ -178,13 +216,10 @@ def layer_program(shapes_fn, n_layers: int, distinct_buffers: bool = False):
     B = {n: i for i, n in enumerate(BUF_NAMES)}
     for layer in range(n_layers):
         src = B["x"] if layer == 0 else B["down"]
-        for nm, in_name, pro in (("q", None, PRO_RMSNORM_QUANT), ("k", None, PRO_RMSNORM_QUANT),
-                                 ("v", None, PRO_RMSNORM_QUANT), ("o", "q", PRO_QUANT),
-                                 ("gate", "o", PRO_QUANT), ("up", "o", PRO_QUANT),
-                                 ("down", "gate", PRO_QUANT)):
+        for nm, in_name, pro in plan:
             K, N = sh[nm]
             ib = src if in_name is None else B[in_name]
             ops.append(dict(name=f"L{layer}.{nm}", K=K, N=N, in_buf=ib, out_buf=B[nm],
-                            prologue=pro, matrix=mi))
+                            prologue=pro, matrix=mi, **extra(layer, nm, lambda b: B[b])))
             mi += 1
     return ops, bufw

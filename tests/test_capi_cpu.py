@@ -137,10 +137,53 @@ def test_sequence_program_validation():
     assert L.mbq_sequence_prepare(good, 2, bufs_bad, W, 3, 1, A, need, None, ctypes.byref(info)) == -4
     assert L.mbq_sequence_prepare(good, 2, bufs, W, 3, 1, A, need, None, None) == -1
     assert L.mbq_sequence_prepare(good, 2, bufs, W, 3, 1, A + 64, need, None, ctypes.byref(info)) == -4
-    # mixed bit widths are accepted by the unfused walk only
+    # mixed bit widths are accepted by the unfused walk only: the workspace
+    # query sizes that, and the fused walk's set-up refuses the list
     mixed = _program([(4, 1, 512, 256, A, 0, 1), (6, 0, 256, 512, A, 1, 2)])
-    assert L.mbq_sequence_workspace_bytes(mixed, 2, W, 3, 1) == -6
+    assert L.mbq_sequence_workspace_bytes(mixed, 2, W, 3, 1) > 0
+    assert L.mbq_sequence_prepare(mixed, 2, bufs, W, 3, 1, A, need, None, ctypes.byref(info)) == -6
     # run refuses an info block that prepare did not fill
     assert L.mbq_sequence_run(ctypes.byref(info), A, None) == -6
     assert L.mbq_sequence_run(None, A, None) == -1
     assert L.mbq_sequence_check(None, None) == -1
+
+
+def _op(bits, pro, N, K, i, o, i2=0, w=None):
+    return (bits, pro, N, K, A, i, o, i2, 0, w)
+
+
+def test_sequence_fused_dataflow_rules():
+    """Which SwiGLU and weighted-RMSNorm dataflows the fused walk accepts.
+
+    Buffers: 0 x [256]; 1 gate [512]; 2 up [512]; 3 down [256]; 4 o [256];
+    5 up' [256].  An accepted list gets past the fused planner and stops at
+    the device check (no GPU here); a refused one returns MBQ_ERR_PROGRAM."""
+    L = mbq.lib()
+    W = (ctypes.c_int64 * 6)(256, 512, 512, 256, 256, 256)
+    bufs = (ctypes.c_void_p * 6)(*([A] * 6))
+    info = mbq.MbqSequenceInfo()
+    Wn, Wn2 = A + 4096, A + 8192      # two sets of norm weights
+    WR, SW = mbq.PRO_WRMSNORM_QUANT, mbq.PRO_SWIGLU_QUANT
+    gate_up = [_op(4, WR, 512, 256, 0, 1, w=Wn), _op(4, WR, 512, 256, 0, 2, w=Wn)]
+    down = _op(4, SW, 256, 512, 1, 3, i2=2)
+    cases = {
+        "pair in one phase": (gate_up + [down], True),
+        "both halves from before the walk": ([down], True),
+        "weighted consumers agreeing": (gate_up + [down, _op(4, WR, 256, 256, 3, 4, w=Wn),
+                                                  _op(4, WR, 256, 256, 3, 5, w=Wn)], True),
+        "weighted consumers disagreeing": (gate_up + [down, _op(4, WR, 256, 256, 3, 4, w=Wn),
+                                                     _op(4, WR, 256, 256, 3, 5, w=Wn2)], False),
+        "half from before the walk": ([gate_up[0], down], False),
+        "halves from two phases": ([gate_up[0], _op(4, WR, 512, 256, 0, 2, w=Wn2), down], False),
+        "up read by another op": (gate_up + [down, _op(4, 0, 256, 512, 2, 4)], False),
+        "gate read by another op first": (gate_up + [_op(4, 0, 256, 512, 1, 4), down], False),
+        "weighted and unweighted consumers": (gate_up + [down, _op(4, WR, 256, 256, 3, 4, w=Wn),
+                                                        _op(4, 0, 256, 256, 3, 5)], False),
+    }
+    for name, (ops, ok) in cases.items():
+        prog = _program(ops)
+        need = L.mbq_sequence_workspace_bytes(prog, len(ops), W, 6, 2)
+        assert need > 0, name          # the unfused walk takes every one of them
+        st = L.mbq_sequence_prepare(prog, len(ops), bufs, W, 6, 2, A, need, None, ctypes.byref(info))
+        assert (st != -6) == ok, f"{name}: status {st}"
+        assert st != 0, name

@@ -55,6 +55,40 @@ def test_quantize_bit_exact(M, K, rmsnorm):
     assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
 
 
+@pytest.mark.parametrize("K", [128, 4096, 17408])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_wrmsnorm_quantize_bit_exact(M, K):
+    x = synth.activations(M, K, seed=K + 7 * M)
+    w = synth.norm_weights(K, seed=K)
+    q, s = mbq.quantize_act(dev(x), norm_w=dev(w))
+    qo, so = oracle.prologue_quant(x, oracle.PRO_WRMSNORM_QUANT, norm_w=w)
+    assert np.array_equal(host(q), qo)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+
+
+@pytest.mark.parametrize("K", [128, 4096, 17408])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_swiglu_quantize(M, K):
+    """The gated values match the fp64 definition within one bf16 step, and the
+    codes and scales are exactly those of quantising the kernel's own gated values."""
+    import torch
+    g = synth.activations(M, K, seed=K + 11 * M)
+    rng = np.random.default_rng(K + M)
+    u = synth.f32_to_bf16_bits((rng.standard_normal((M, K)) * 2).astype(np.float32))
+    h = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+    q, s = mbq.quantize_act(dev(g), up=dev(u), h_out=h)
+    hg = host(h)
+    ho = oracle.swiglu_bf16(g, u)
+    def steps(b):   # bf16 patterns -> integers ordered like the values (+0 and -0 equal)
+        b = b.astype(np.int32)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+    d = np.abs(steps(hg) - steps(ho))
+    assert d.max() <= 1, f"{int((d > 0).sum())} differ, max {d.max()} bf16 steps"
+    qo, so = oracle.quantize_act(hg)
+    assert np.array_equal(host(q), qo)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+
+
 @pytest.mark.parametrize("rmsnorm", [False, True])
 @pytest.mark.parametrize("K", [128, 4096])
 def test_quantize_special_rows(K, rmsnorm):
@@ -204,17 +238,26 @@ def test_linear_workspace_reused_across_shapes():
 
 # ---------------------------------------------------------------- decode-step walk
 
-def _run_sequence(bits, shapes_fn, n_layers, M, distinct, seed_base=0, fused=True, runs=1):
+def _run_sequence(bits, shapes_fn, n_layers, M, distinct, seed_base=0, fused=True, runs=1, dataflow="plain"):
     import torch
-    ops, widths = synth.layer_program(shapes_fn, n_layers, distinct_buffers=distinct)
+    ops, widths = synth.layer_program(shapes_fn, n_layers, distinct_buffers=distinct, dataflow=dataflow)
     mats = {}
+    norms = {}   # one device copy per set of norm weights: ops sharing a norm share its pointer
     dev_ops = []
     for o in ops:
         canon, S = synth.weights(bits, o["N"], o["K"], seed=1 + o["matrix"] + seed_base)
         mats[o["matrix"]] = (canon, S)
-        dev_ops.append(dict(bits=bits, prologue=o["prologue"], N=o["N"], K=o["K"],
-                            packed=packed_on_device(bits, canon, S, o["N"], o["K"]),
-                            in_buf=o["in_buf"], out_buf=o["out_buf"]))
+        d = dict(bits=bits, prologue=o["prologue"], N=o["N"], K=o["K"],
+                 packed=packed_on_device(bits, canon, S, o["N"], o["K"]),
+                 in_buf=o["in_buf"], out_buf=o["out_buf"])
+        if "norm_seed" in o:
+            o["norm_w"] = synth.norm_weights(o["K"], o["norm_seed"])
+            if o["norm_seed"] not in norms:
+                norms[o["norm_seed"]] = dev(o["norm_w"])
+            d["norm_w"] = norms[o["norm_seed"]]
+        if "in_buf2" in o:
+            d["in_buf2"] = o["in_buf2"]
+        dev_ops.append(d)
     bufs = [torch.zeros((M, w), dtype=torch.bfloat16, device="cuda") for w in widths]
     x0 = synth.activations(M, widths[0])
     bufs[0].copy_(dev(x0))
@@ -247,6 +290,77 @@ def test_layer_sequence_teacher_forced_small(bits, M, fused):
         x = np.ascontiguousarray(bufs[o["in_buf"]][:, :o["K"]])
         ref = oracle.op(bits, x, o["prologue"], *mats[o["matrix"]])
         assert_close_bf16(bufs[o["out_buf"]], ref, o["name"])
+
+
+def _oracle_op_rows(bits, bufs, o, mats, rows=None):
+    """Oracle outputs of op o from the walk's own input buffers (teacher forced)."""
+    x = np.ascontiguousarray(bufs[o["in_buf"]][:, :o["K"]])
+    u = (np.ascontiguousarray(bufs[o["in_buf2"]][:, :o["K"]])
+         if o["prologue"] == oracle.PRO_SWIGLU_QUANT else None)
+    canon, S = mats[o["matrix"]]
+    if rows is not None:
+        canon, S = canon[rows], S[rows]
+    return oracle.op(bits, x, o["prologue"], canon, S, o.get("norm_w"), u)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("bits", [4, 6])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_layer_sequence_swiglu_dataflow_small(bits, M, fused):
+    """The walk with weighted RMSNorms and the SwiGLU gate in front of down."""
+    ops, mats, bufs, _ = _run_sequence(bits, _small_shapes, 3, M, distinct=True, fused=fused,
+                                       dataflow="swiglu")
+    for o in ops:
+        assert_close_bf16(bufs[o["out_buf"]], _oracle_op_rows(bits, bufs, o, mats), o["name"])
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("M", [1, 3])
+def test_layer_sequence_swiglu_dataflow_9b_layers(M, fused):
+    ops, mats, bufs, _ = _run_sequence(4, synth.layer_shapes_9b, 2, M, distinct=True, fused=fused,
+                                       dataflow="swiglu")
+    rng = np.random.default_rng(7)
+    for o in ops:
+        rows = sample_rows(rng, o["N"], 128)
+        assert_close_bf16(bufs[o["out_buf"]][:, rows], _oracle_op_rows(4, bufs, o, mats, rows), o["name"])
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("bits", [4, 6])
+@pytest.mark.parametrize("M", [1, 8])
+def test_sequence_gate_and_norm_inputs_from_before_the_walk(bits, M, fused):
+    """A SwiGLU op whose gate and up are written before the walk (the fused
+    walk gates them in its kernel-start pass), a weighted-RMSNorm op on its
+    output, and one on an input from before the walk."""
+    import torch
+    widths = [384, 384, 256, 256, 128, 256]
+    w1, w2 = synth.norm_weights(256, 11), synth.norm_weights(256, 12)
+    ops = [dict(name="down", K=384, N=256, in_buf=0, in_buf2=1, out_buf=2, prologue=oracle.PRO_SWIGLU_QUANT),
+           dict(name="a", K=256, N=128, in_buf=2, out_buf=4, prologue=oracle.PRO_WRMSNORM_QUANT, norm_w=w1),
+           dict(name="b", K=256, N=256, in_buf=3, out_buf=5, prologue=oracle.PRO_WRMSNORM_QUANT, norm_w=w2)]
+    mats, dev_ops = {}, []
+    for i, o in enumerate(ops):
+        o["matrix"] = i
+        mats[i] = synth.weights(bits, o["N"], o["K"], seed=300 + i)
+        d = dict(bits=bits, prologue=o["prologue"], N=o["N"], K=o["K"], in_buf=o["in_buf"], out_buf=o["out_buf"],
+                 packed=packed_on_device(bits, *mats[i], o["N"], o["K"]))
+        if "in_buf2" in o:
+            d["in_buf2"] = o["in_buf2"]
+        if "norm_w" in o:
+            d["norm_w"] = dev(o["norm_w"])
+        dev_ops.append(d)
+    bufs = [torch.zeros((M, w), dtype=torch.bfloat16, device="cuda") for w in widths]
+    for b, seed in ((0, 21), (1, 22), (3, 23)):
+        bufs[b].copy_(dev(synth.activations(M, widths[b], seed=seed)))
+    seq = mbq.LayerSequence(dev_ops, bufs, M, fused=fused)
+    for _ in range(2):   # the second run sees the first one's tags in the workspace
+        seq.run()
+        if fused:
+            seq.check()
+        torch.cuda.synchronize()
+        hb = [host(b) for b in bufs]
+        for o in ops:
+            assert_close_bf16(hb[o["out_buf"]], _oracle_op_rows(bits, hb, o, mats), o["name"])
 
 
 @pytest.mark.parametrize("bits", [4, 6])
