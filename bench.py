@@ -94,7 +94,7 @@ def time_sequence(mbq, dev_ops, widths, M, steps, warmup, fused=True):
                 event_ms_best=float(per.min()), event_ms_mean=float(per.mean()))
 
 
-KERNEL_SOURCES = ["seq_walk.h", "seq_plain.hip", "seqplan.hip", "mbq_seq.h", "mbq_internal.h"]
+KERNEL_SOURCES = ["seq_walk.h", "seq_plain.hip", "seq_full.hip", "seqplan.hip", "mbq_seq.h", "mbq_internal.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "seq_kernel_traffic.json")
 
 
