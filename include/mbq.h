@@ -106,6 +106,28 @@ int mbq_pack_weights(int bits, int64_t N, int64_t K, const void *w_canon,
 int mbq_unpack_weights(int bits, int64_t N, int64_t K, const void *packed,
                        void *w_canon, void *scales_f16, void *stream);
 
+/* The same re-layout done in place ("Optimizing the Linear Kernel": the
+ * kernel-order re-layout happens in VRAM, in place, once per load, with no
+ * extra RAM or VRAM).  buf (device, 256-byte aligned, buf_bytes >=
+ * mbq_packed_bytes(bits, N, K)) holds on entry the canonical codes of the N
+ * rows (row stride K * bits / 8 bytes, as mbq_pack_weights reads them)
+ * immediately followed by the fp16 scales [N][K/128]; bytes past those are
+ * ignored.  On return it holds exactly what mbq_pack_weights would write
+ * (padding rows zero).  No workspace: the bytes move inside buf (block
+ * rotations, then a grid-wide pass that stages whole row blocks in LDS).
+ * Waits for `stream`; a set-up call.  Calls on one device must not overlap
+ * (they share one grid-barrier word).  Returns MBQ_ERR_WORKSPACE if buf_bytes
+ * is too small, MBQ_ERR_SHAPE if K / 128 exceeds the tiles the device can
+ * stage at once (about 9000 groups at W4, 6000 at W6), MBQ_ERR_TIMEOUT if the
+ * grid barrier gave up (buf is then undefined). */
+int mbq_pack_weights_inplace(int bits, int64_t N, int64_t K, void *buf, int64_t buf_bytes, void *stream);
+
+/* Test helper, host only: the first two steps of the in-place re-layout
+ * (padding rows, then row blocks interleaved as [codes of rows 64b..64b+63]
+ * [their scales] for b = 0, 1, ..) on a host buffer of buf_bytes >=
+ * mbq_packed_bytes(bits, N, K) holding the canonical codes and scales. */
+int mbq_relayout_interleave_host(int bits, int64_t N, int64_t K, void *host_buf, int64_t buf_bytes);
+
 /* ---------------------------------------------------------------- activation quantisation
  * "Optimizing the Linear Kernel": quantise the activation to 8 bits before
  * the integer linear.  x_bf16: device bf16 [M][K] (row stride K);

@@ -22,7 +22,8 @@ STATUS = {0: "MBQ_OK", -1: "MBQ_ERR_NULL", -2: "MBQ_ERR_SHAPE", -3: "MBQ_ERR_BIT
           -7: "MBQ_ERR_HIP", -8: "MBQ_ERR_DEVICE", -9: "MBQ_ERR_TIMEOUT"}
 
 EXPORTS = ["mbq_status_string", "mbq_last_hip_error", "mbq_version", "mbq_packed_bytes",
-           "mbq_pack_weights", "mbq_unpack_weights", "mbq_quantize_act",
+           "mbq_pack_weights", "mbq_unpack_weights", "mbq_pack_weights_inplace",
+           "mbq_relayout_interleave_host", "mbq_quantize_act",
            "mbq_rmsnorm_quantize_act", "mbq_wrmsnorm_quantize_act", "mbq_swiglu_quantize_act",
            "mbq_linear_workspace_bytes", "mbq_w4a8_linear",
            "mbq_w6a8_linear", "mbq_linear_group_acc", "mbq_sequence_workspace_bytes",
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.mbq_packed_bytes.restype = I64
         L.mbq_pack_weights.argtypes = [ctypes.c_int, I64, I64, P, P, P, P]
         L.mbq_unpack_weights.argtypes = [ctypes.c_int, I64, I64, P, P, P, P]
+        L.mbq_pack_weights_inplace.argtypes = [ctypes.c_int, I64, I64, P, I64, P]
+        L.mbq_relayout_interleave_host.argtypes = [ctypes.c_int, I64, I64, P, I64]
         L.mbq_quantize_act.argtypes = [I64, I64, P, P, P, P]
         L.mbq_rmsnorm_quantize_act.argtypes = [I64, I64, P, P, P, P]
         L.mbq_wrmsnorm_quantize_act.argtypes = [I64, I64, P, P, P, P, P]
@@ -150,6 +153,27 @@ def pack_weights(bits: int, w_canon, scales_f16, N: int, K: int, out=None):
     _check("mbq_pack_weights", lib().mbq_pack_weights(bits, N, K, _ptr(w_canon), _ptr(scales_f16),
                                                       _ptr(out), _stream()))
     return out
+
+
+def pack_weights_inplace(bits: int, buf, N: int, K: int):
+    """Re-lay in place: buf (uint8 device tensor of at least packed_bytes(bits, N, K)
+    bytes) holds the canonical codes of the N rows followed by their fp16 scales;
+    afterwards it holds the packed tiles.  Waits for the stream."""
+    if buf.numel() * buf.element_size() < packed_bytes(bits, N, K):
+        raise ValueError("buffer smaller than packed_bytes(bits, N, K)")
+    _check("mbq_pack_weights_inplace", lib().mbq_pack_weights_inplace(
+        bits, N, K, _ptr(buf), buf.numel() * buf.element_size(), _stream()))
+    return buf
+
+
+def relayout_interleave_host(bits: int, buf, N: int, K: int):
+    """Test helper: the padding and row-block interleave steps of the in-place
+    re-layout on a host numpy uint8 array (modified in place)."""
+    import numpy as np
+    assert isinstance(buf, np.ndarray) and buf.dtype == np.uint8 and buf.flags.c_contiguous
+    _check("mbq_relayout_interleave_host", lib().mbq_relayout_interleave_host(
+        bits, N, K, buf.ctypes.data, buf.nbytes))
+    return buf
 
 
 def unpack_weights(bits: int, packed, N: int, K: int):

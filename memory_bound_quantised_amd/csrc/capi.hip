@@ -237,6 +237,30 @@ static int device_cus(int *n_cu) {
     return e == hipSuccess ? MBQ_OK : hip_fail(e);
 }
 
+int mbq_pack_weights_inplace(int bits, int64_t N, int64_t K, void *buf, int64_t buf_bytes, void *stream) {
+    if (!bits_ok(bits)) return MBQ_ERR_BITS;
+    if (!buf) return MBQ_ERR_NULL;
+    if (!n_ok(N) || !k_ok(K)) return MBQ_ERR_SHAPE;
+    if (!aligned(buf, 256)) return MBQ_ERR_ALIGN;
+    if (buf_bytes < mbq_packed_bytes(bits, N, K)) return MBQ_ERR_WORKSPACE;
+    int st = check_device();
+    if (st) return st;
+    int n_cu = 0;
+    st = device_cus(&n_cu);
+    if (st) return st;
+    hipError_t he = hipSuccess;
+    st = relayout_inplace(bits, N, K, buf, n_cu, (hipStream_t)stream, &he);
+    return st == MBQ_ERR_HIP ? hip_fail(he) : st;
+}
+
+int mbq_relayout_interleave_host(int bits, int64_t N, int64_t K, void *host_buf, int64_t buf_bytes) {
+    if (!bits_ok(bits)) return MBQ_ERR_BITS;
+    if (!host_buf) return MBQ_ERR_NULL;
+    if (!n_ok(N) || !k_ok(K)) return MBQ_ERR_SHAPE;
+    if (buf_bytes < mbq_packed_bytes(bits, N, K)) return MBQ_ERR_WORKSPACE;
+    return relayout_interleave_host(bits, N, K, (uint8_t *)host_buf);
+}
+
 int64_t mbq_sequence_workspace_bytes(const mbq_op *ops, int32_t n_ops, const int64_t *buf_widths,
                                      int32_t n_bufs, int64_t M) {
     const int64_t unfused = analyse_program(ops, n_ops, buf_widths, n_bufs, M, nullptr);

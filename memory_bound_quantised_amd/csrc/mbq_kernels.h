@@ -10,6 +10,46 @@ struct mbq_op;
 
 namespace mbq {
 
+// In-place re-layout (pack.hip).  Byte geometry of a matrix: canonical codes
+// (Cr bytes per row, pc per row and group), padded row count Np = 64 R, and
+// per row block C code bytes, S scale bytes, T = C + S (= G packed tiles).
+struct RelayoutGeom {
+    int64_t N, K, G, R, Np, Cr, pc, C, S, T, canon_bytes, packed_bytes;
+};
+__host__ __device__ inline RelayoutGeom relayout_geom(int bits, int64_t N, int64_t K) {
+    RelayoutGeom g;
+    g.N = N;
+    g.K = K;
+    g.G = K / 128;
+    g.R = (N + 63) / 64;
+    g.Np = 64 * g.R;
+    g.Cr = K * bits / 8;
+    g.pc = 128 * bits / 8;
+    g.C = 64 * g.Cr;
+    g.S = 64 * 2 * g.G;
+    g.T = g.C + g.S;
+    g.canon_bytes = N * (g.Cr + 2 * g.G);
+    g.packed_bytes = g.R * g.T;
+    return g;
+}
+// Interval [a, b) of row blocks at node i of recursion level `level` of step
+// A: the root is [0, R), and a node [a, b) splits at (a + b) / 2, the bits of
+// i choosing left or right from the top level down.
+__host__ __device__ inline void relayout_node(int64_t R, int level, int64_t i, int64_t &a, int64_t &b) {
+    a = 0;
+    b = R;
+    for (int d = level - 1; d >= 0; --d) {
+        const int64_t m = (a + b) / 2;
+        if ((i >> d) & 1) a = m;
+        else b = m;
+    }
+}
+// Steps P and A of the re-layout on a host buffer (tests of the schedule).
+int relayout_interleave_host(int bits, int64_t N, int64_t K, uint8_t *buf);
+// The whole re-layout on the device, in place; waits for the stream.  On
+// MBQ_ERR_HIP, *hip_err holds the failing call's error.
+int relayout_inplace(int bits, int64_t N, int64_t K, void *buf, int n_cu, hipStream_t s, hipError_t *hip_err);
+
 hipError_t launch_pack(int bits, int64_t N, int64_t K, const void *canon, const void *scales,
                        void *packed, hipStream_t s);
 hipError_t launch_unpack(int bits, int64_t N, int64_t K, const void *packed, void *canon,

@@ -187,3 +187,43 @@ def test_sequence_fused_dataflow_rules():
         st = L.mbq_sequence_prepare(prog, len(ops), bufs, W, 6, 2, A, need, None, ctypes.byref(info))
         assert (st != -6) == ok, f"{name}: status {st}"
         assert st != 0, name
+
+
+@pytest.mark.parametrize("bits,N,K", [(4, 64, 128), (4, 1, 128), (4, 128, 256), (4, 200, 384), (6, 130, 256),
+                                      (4, 1000, 1024), (6, 64 * 7 + 5, 640), (6, 64 * 9, 128), (4, 63, 17408)])
+def test_relayout_interleave_schedule(bits, N, K):
+    """The padding and row-block interleave steps of the in-place re-layout (block
+    rotations by reversal, on the host) turn [codes][scales] into [codes of a row
+    block][its scales] per row block, with the padding rows zero."""
+    import numpy as np
+    rng = np.random.default_rng(N * 7 + K + bits)
+    G, Cr = K // 128, K * bits // 8
+    R = (N + 63) // 64
+    codes = rng.integers(0, 256, (N, Cr), dtype=np.uint8)
+    scales = rng.integers(0, 1 << 16, (N, G), dtype=np.uint16)
+    total = mbq.lib().mbq_packed_bytes(bits, N, K)
+    buf = np.full(total, 0xAB, np.uint8)     # bytes past the canonical data are garbage
+    canon = np.concatenate([codes.reshape(-1), scales.reshape(-1).view(np.uint8)])
+    buf[:canon.size] = canon
+    mbq.relayout_interleave_host(bits, buf, N, K)
+    pc = np.zeros((R * 64, Cr), np.uint8)
+    pc[:N] = codes
+    ps = np.zeros((R * 64, G), np.uint16)
+    ps[:N] = scales
+    want = np.concatenate([np.concatenate([pc[64 * b:64 * b + 64].reshape(-1),
+                                           ps[64 * b:64 * b + 64].reshape(-1).view(np.uint8)])
+                           for b in range(R)])
+    assert want.size == total
+    assert np.array_equal(buf, want)
+
+
+def test_pack_inplace_validation():
+    L = mbq.lib()
+    need = L.mbq_packed_bytes(4, 64, 128)
+    assert L.mbq_pack_weights_inplace(5, 64, 128, A, need, None) == -3
+    assert L.mbq_pack_weights_inplace(4, 64, 128, None, need, None) == -1
+    assert L.mbq_pack_weights_inplace(4, 64, 100, A, need, None) == -2
+    assert L.mbq_pack_weights_inplace(4, 0, 128, A, need, None) == -2
+    assert L.mbq_pack_weights_inplace(4, 64, 128, A + 16, need, None) == -4
+    assert L.mbq_pack_weights_inplace(4, 64, 128, A, need - 1, None) == -5
+    assert L.mbq_relayout_interleave_host(4, 64, 128, None, need) == -1

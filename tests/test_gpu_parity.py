@@ -114,6 +114,22 @@ def test_pack_unpack_roundtrip(bits, N, K):
     assert np.array_equal(host(s2).view(np.uint16), S.view(np.uint16))
 
 
+@pytest.mark.parametrize("bits,N,K", [(4, 64, 128), (4, 1, 128), (4, 200, 384), (6, 130, 256), (6, 63, 1152),
+                                      (4, 4096, 4096), (6, 1000, 1024), (4, 17408, 5120), (4, 5120, 17408),
+                                      (6, 5120, 17408), (6, 17408, 5120)])
+def test_pack_inplace_matches_pack(bits, N, K):
+    """The in-place re-layout leaves exactly the bytes of the out-of-place pack."""
+    import torch
+    canon, S = synth.weights(bits, N, K, seed=N + 3 * K + bits)
+    ref = packed_on_device(bits, canon, S, N, K)
+    total = mbq.packed_bytes(bits, N, K)
+    blob = np.concatenate([canon.reshape(-1), S.reshape(-1).view(np.uint8)])
+    buf = torch.full((total,), 0x5A, dtype=torch.uint8, device="cuda")   # garbage past the canonical data
+    buf[:blob.size].copy_(dev(blob))
+    mbq.pack_weights_inplace(bits, buf, N, K)
+    assert torch.equal(buf, ref)
+
+
 @pytest.mark.parametrize("bits", [4, 6])
 def test_pack_pads_rows_with_zeros(bits):
     N, K = 70, 256
