@@ -49,6 +49,7 @@ def _load():
         lib.oracle_rmsnorm_bf16.argtypes = [I64, I64, P, P]
         lib.oracle_wrmsnorm_bf16.argtypes = [I64, I64, P, P, P]
         lib.oracle_swiglu_bf16.argtypes = [I64, P, P, P]
+        lib.oracle_decode_attention.argtypes = [I64, I64, I64, I64, I64, I64, P, P, P, P]
         lib.oracle_group_acc.argtypes = [ctypes.c_int, I64, I64, I64, P, P, P]
         lib.oracle_linear.argtypes = [ctypes.c_int, I64, I64, I64, P, P, P, P, P, P]
         lib.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
@@ -161,6 +162,24 @@ def swiglu_bf16(g_bf16: np.ndarray, u_bf16: np.ndarray) -> np.ndarray:
     h = np.empty(g.shape, np.uint16)
     _load().oracle_swiglu_bf16(g.size, _p(g), _p(u), _p(h))
     return h
+
+
+def decode_attention(q_bf16: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, P: int) -> np.ndarray:
+    """Split-prefix decode attention of the "Paying attention to the attention!"
+    section, by its definition (see oracle.c): q [M][n_q][D], caches
+    [n_kv][L][D] (bf16 bits) with the M new tokens' keys and values at
+    positions P .. P+M-1; token i attends to positions 0 .. P+i.  Returns bf16
+    bits [M][n_q][D]."""
+    q = _c(q_bf16, np.uint16)
+    k = _c(k_cache, np.uint16)
+    v = _c(v_cache, np.uint16)
+    M, n_q, D = q.shape
+    n_kv, L, D2 = k.shape
+    assert D2 == D and v.shape == k.shape and n_q % n_kv == 0 and P + M <= L
+    o = np.empty((M, n_q, D), np.uint16)
+    rc = _load().oracle_decode_attention(M, n_q, n_kv, D, P, L, _p(q), _p(k), _p(v), _p(o))
+    assert rc == 0
+    return o
 
 
 PRO_QUANT = 0

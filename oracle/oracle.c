@@ -41,6 +41,7 @@
  * Every loop below is the plain definition: no blocking, no reordering.
  */
 #include <math.h>
+#include <stdlib.h>
 #include <omp.h>
 #include <stdint.h>
 #include <string.h>
@@ -239,6 +240,53 @@ int oracle_linear(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q, co
             if (ypre) ypre[m * N + n] = v;
             if (y) y[m * N + n] = f64_to_bf16(v);
         }
+    }
+    return 0;
+}
+
+/* ---- split-prefix decode attention ---------------------------------------
+ *
+ * "Doubling LLM token rates in ComfyUI", section "Paying attention to the
+ * attention!": the decode attention of the grouped-query layers takes a short
+ * query -- one token, or the committed token and the MTP draft rows with their
+ * causal verification -- without a materialised mask.  What it computes is
+ * ordinary scaled dot-product attention; the readings used here:
+ *   - M new tokens sit at cache positions P .. P+M-1 (their keys and values
+ *     are already in the cache); token i attends to positions 0 .. P+i;
+ *   - query head h reads key/value head h / (n_q / n_kv);
+ *   - score = (q . k) / sqrt(D), softmax over the attended positions, output
+ *     = sum of softmax weight times v, rounded once to bf16 (nearest even);
+ *     everything here in fp64 from the bf16 inputs.
+ * Layouts: q and o [M][n_q][D]; k and v caches [n_kv][L][D] (L >= P+M). */
+int oracle_decode_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P, int64_t L,
+                            const uint16_t *q, const uint16_t *kc, const uint16_t *vc, uint16_t *o) {
+    if (n_kv < 1 || n_q % n_kv || P + M > L) return -1;
+    const int64_t qpg = n_q / n_kv;
+    const double scale = 1.0 / sqrt((double)D);
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t r = 0; r < M * n_q; ++r) {
+        const int64_t i = r / n_q, h = r % n_q, g = h / qpg;
+        const int64_t n = P + i + 1;                   /* attended positions */
+        const uint16_t *qr = q + r * D;
+        const uint16_t *kg = kc + g * L * D, *vg = vc + g * L * D;
+        double *s = (double *)malloc((size_t)n * sizeof(double));
+        double *acc = (double *)calloc((size_t)D, sizeof(double));
+        double mx = -INFINITY;
+        for (int64_t p = 0; p < n; ++p) {
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += (double)bf16_to_f32(qr[d]) * (double)bf16_to_f32(kg[p * D + d]);
+            s[p] = dot * scale;
+            if (s[p] > mx) mx = s[p];
+        }
+        double den = 0.0;
+        for (int64_t p = 0; p < n; ++p) {
+            const double w = exp(s[p] - mx);
+            den += w;
+            for (int64_t d = 0; d < D; ++d) acc[d] += w * (double)bf16_to_f32(vg[p * D + d]);
+        }
+        for (int64_t d = 0; d < D; ++d) o[r * D + d] = f64_to_bf16(acc[d] / den);
+        free(s);
+        free(acc);
     }
     return 0;
 }
