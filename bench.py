@@ -9,6 +9,10 @@ timed region.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--set 9b|27b] [--bits 4|6]
                   [--m 1] [--extra-m 3] [--dataflow plain|swiglu] [--no-cpu]
+
+With --workload attention it instead times the split-prefix decode attention of
+one 27B-shaped attention layer (32 query heads, 4 key/value heads of 256) over a
+--ctx-token bf16 KV cache, and reports the cache-read rate.
 """
 from __future__ import annotations
 
@@ -122,6 +126,79 @@ def measured_traffic(key):
     return e["fetch_bytes_per_launch"] + e["write_bytes_per_launch"]
 
 
+ATTN_SHAPE = dict(n_q=32, n_kv=4, D=256)
+
+
+def run_attention(args):
+    """One JSON line for the decode attention: KV-cache bytes per launch over the
+    event-timed launch, for M = args.m (and args.extra_m as extra fields)."""
+    import torch
+    import memory_bound_quantised_amd as mbq
+    n_q, n_kv, D, P = ATTN_SHAPE["n_q"], ATTN_SHAPE["n_kv"], ATTN_SHAPE["D"], args.ctx
+    Ms = [args.m] + [m for m in args.extra_m if m != args.m]
+    L = P + max(Ms)
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    k = torch.randn((n_kv, L, D), device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn((n_kv, L, D), device="cuda", generator=g).to(torch.bfloat16)
+    res = {}
+    for M in Ms:
+        q = torch.randn((M, n_q, D), device="cuda", generator=g).to(torch.bfloat16)
+        ws = torch.zeros(mbq.attention_workspace_bytes(M, n_q, n_kv, D, P), dtype=torch.uint8, device="cuda")
+        out = torch.empty((M, n_q, D), dtype=torch.bfloat16, device="cuda")
+        for _ in range(args.warmup):
+            mbq.decode_attention(q, k, v, P, out=out, ws=ws)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        for i in range(args.steps):
+            mbq.decode_attention(q, k, v, P, out=out, ws=ws)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+        assert torch.isfinite(out.float()).all()
+        kv_bytes = 2 * (P + M) * n_kv * D * 2
+        res[M] = dict(ms=float(np.median(per)), wall_ms=wall * 1e3 / args.steps, kv_bytes=kv_bytes)
+        log(f"attention M={M}: {res[M]}")
+    r = res[args.m]
+    gbs = r["kv_bytes"] / (r["ms"] / 1e3) / 1e9
+    out = {
+        "metric": "decode-attention KV-cache read GB/s (% of HBM peak), 27B-shaped layer",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(r["wall_ms"], 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"split-prefix decode attention, 32 query / 4 key-value heads of 256, "
+                               f"{P}-token bf16 cache, M={args.m}", "ctx": P, "M": args.m, **ATTN_SHAPE},
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_attention_kernel (1 launch per call)", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": r["kv_bytes"], "launch_ms": round(r["ms"], 4)},
+    }
+    for M, rm in res.items():
+        if M != args.m:
+            out[f"m{M}"] = {"GB/s": round(rm["kv_bytes"] / (rm["ms"] / 1e3) / 1e9, 2), "launch_ms": round(rm["ms"], 4)}
+    if not args.no_cpu:
+        import oracle
+        rng = np.random.default_rng(5)
+        heads_kv = 1   # a bounded sample: one key/value head group (8 query heads) at M=1
+        qh = synth.f32_to_bf16_bits(rng.standard_normal((1, n_q // n_kv * heads_kv, D), dtype=np.float32))
+        kh = synth.f32_to_bf16_bits(rng.standard_normal((heads_kv, P + 1, D), dtype=np.float32))
+        vh = synth.f32_to_bf16_bits(rng.standard_normal((heads_kv, P + 1, D), dtype=np.float32))
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 10.0 or reps == 0:
+            oracle.decode_attention(qh, kh, vh, P)
+            reps += 1
+        dt = time.perf_counter() - t0
+        b = reps * 2 * (P + 1) * heads_kv * D * 2
+        out["cpu_baseline"] = dict(value=round(b / dt / 1e9, 4), unit="GB/s", cores=oracle.num_threads(), kind="oracle",
+                                   sample=f"{reps} oracle calls of one key/value head group (8 query heads, M=1) over the "
+                                          f"{P}-token cache, {dt:.1f} s; KV bytes read per second")
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(set_name, bits, n_layers, dataflow="plain", budget_s=10.0):
     """The oracle on the host cores: the same M=1 walk, layer after layer (starting over after
     the last layer), until about budget_s seconds of oracle time have been spent."""
@@ -166,6 +243,9 @@ def main():
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--m", type=int, default=1)
     ap.add_argument("--extra-m", type=int, nargs="*", default=[3])
+    ap.add_argument("--workload", default="walk", choices=["walk", "attention"],
+                    help="attention: the split-prefix decode attention of one 27B-shaped layer instead of the walk")
+    ap.add_argument("--ctx", type=int, default=32768, help="attention: cached prefix length")
     ap.add_argument("--dataflow", default="plain", choices=["plain", "swiglu"],
                     help="swiglu: weighted RMSNorms before q/k/v and gate/up, silu(gate) * up before down")
     ap.add_argument("--no-cpu", action="store_true")
@@ -184,6 +264,10 @@ def main():
     mbq.lib()   # fails loudly if the HIP library is not built
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+
+    if args.workload == "attention":
+        run_attention(args)
+        return
 
     if args.calib_copy > 0:
         src = torch.ones(args.calib_copy << 18, dtype=torch.float32, device="cuda")

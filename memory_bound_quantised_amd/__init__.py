@@ -28,7 +28,7 @@ EXPORTS = ["mbq_status_string", "mbq_last_hip_error", "mbq_version", "mbq_packed
            "mbq_linear_workspace_bytes", "mbq_w4a8_linear",
            "mbq_w6a8_linear", "mbq_linear_group_acc", "mbq_sequence_workspace_bytes",
            "mbq_sequence_prepare", "mbq_sequence_run", "mbq_sequence_check", "mbq_layer_sequence",
-           "mbq_layer_sequence_unfused"]
+           "mbq_layer_sequence_unfused", "mbq_attention_workspace_bytes", "mbq_decode_attention"]
 
 
 class MbqError(RuntimeError):
@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.mbq_pack_weights.argtypes = [ctypes.c_int, I64, I64, P, P, P, P]
         L.mbq_unpack_weights.argtypes = [ctypes.c_int, I64, I64, P, P, P, P]
         L.mbq_pack_weights_inplace.argtypes = [ctypes.c_int, I64, I64, P, I64, P]
+        L.mbq_attention_workspace_bytes.argtypes = [I64, I64, I64, I64, I64]
+        L.mbq_attention_workspace_bytes.restype = I64
+        L.mbq_decode_attention.argtypes = [I64, I64, I64, I64, I64, I64, P, P, P, P, P, I64, P]
         L.mbq_relayout_interleave_host.argtypes = [ctypes.c_int, I64, I64, P, I64]
         L.mbq_quantize_act.argtypes = [I64, I64, P, P, P, P]
         L.mbq_rmsnorm_quantize_act.argtypes = [I64, I64, P, P, P, P]
@@ -97,7 +100,7 @@ def lib() -> ctypes.CDLL:
         for name in EXPORTS:
             if name not in ("mbq_status_string", "mbq_last_hip_error", "mbq_version",
                             "mbq_packed_bytes", "mbq_linear_workspace_bytes",
-                            "mbq_sequence_workspace_bytes"):
+                            "mbq_sequence_workspace_bytes", "mbq_attention_workspace_bytes"):
                 getattr(L, name).restype = ctypes.c_int
         _lib_handle = L
     return _lib_handle
@@ -174,6 +177,34 @@ def relayout_interleave_host(bits: int, buf, N: int, K: int):
     _check("mbq_relayout_interleave_host", lib().mbq_relayout_interleave_host(
         bits, N, K, buf.ctypes.data, buf.nbytes))
     return buf
+
+
+def attention_workspace_bytes(M: int, n_q: int, n_kv: int, D: int, P: int) -> int:
+    v = lib().mbq_attention_workspace_bytes(M, n_q, n_kv, D, P)
+    if v < 0:
+        raise MbqError("mbq_attention_workspace_bytes", v)
+    return v
+
+
+def decode_attention(q, k_cache, v_cache, P: int, out=None, ws=None):
+    """Split-prefix decode attention: q bf16 [M][n_q][D]; caches bf16 [n_kv][L][D]
+    holding the M new tokens' keys and values at positions P .. P+M-1.  Token i
+    attends to positions 0 .. P+i.  ws: a uint8 device tensor of at least
+    attention_workspace_bytes(...) bytes, zero-filled before its first use (each
+    call leaves it ready for the next); allocated here when omitted."""
+    import torch
+    M, n_q, D = q.shape
+    n_kv, L, D2 = k_cache.shape
+    assert D2 == D and v_cache.shape == k_cache.shape
+    if out is None:
+        out = torch.empty((M, n_q, D), dtype=torch.bfloat16, device=q.device)
+    need = attention_workspace_bytes(M, n_q, n_kv, D, P)
+    if ws is None:
+        ws = _zeros(need, q.device)
+    _check("mbq_decode_attention", lib().mbq_decode_attention(
+        M, n_q, n_kv, D, P, L, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream()))
+    return out
 
 
 def unpack_weights(bits: int, packed, N: int, K: int):

@@ -1,0 +1,483 @@
+// Split-prefix decode attention ("Paying attention to the attention!" on the
+// page "Doubling LLM token rates in ComfyUI"): a short query -- one token, or
+// the committed token and the MTP draft rows with their causal verification --
+// against a bf16 KV cache, with no materialised mask.  The cached prefix is
+// split across many workgroups so that the tiny query still fills the GPU,
+// and the last workgroup of each key/value head to finish combines the
+// partial results in the same launch.
+//
+// Workgroup (kv head g, split s): 256 threads, positions in blocks of 64,
+// staged in LDS (keys row-major, values transposed) while the next block is
+// loaded into registers.  The query rows of the head group (r = token * qpg +
+// head-in-group, at most 64) form up to four 16-row tiles, one per wave; a
+// wave's tile products run on the matrix cores (bf16, 16 x 16 x 32):
+//   scores   S = Q K^T, the query tile held in registers for the whole walk;
+//   softmax  online per row (running max m and sum l, base 2); the score and
+//            the output tiles put row 4 (lane / 16) + j of the tile in the
+//            same lane register, so rescaling needs no data movement;
+//   values   O += P V, with P as a bf16 high part plus a bf16 residual (two
+//            products, about 16 significant bits; bf16 alone loses a percent
+//            where values cancel), going through LDS to take the operand
+//            layout.
+// Each workgroup publishes (m, l, o) per row with agent-scope stores; the last
+// to count in for its head merges the splits: M = max m_s, L = sum l_s
+// 2^(m_s - M), O = sum o_s 2^(m_s - M) / L.
+#include <algorithm>
+
+#include "mbq.h"
+#include "mbq_internal.h"
+#include "mbq_kernels.h"
+
+namespace mbq {
+
+namespace {
+
+constexpr int kBlock = 64;        // positions per block
+constexpr int kGroupSplits = 8;   // splits merged together first
+constexpr int kMaxSplits = 128;
+constexpr int kMaxGroups = kMaxSplits / kGroupSplits;
+constexpr int kCounterWords = 64; // per key/value head: [0] groups done, [1 + k] splits of group k done
+constexpr int kAttnThreads = 256;
+
+struct AttnArgs {
+    const uint16_t *q;            // [M][n_q][D]
+    const uint16_t *k, *v;        // [n_kv][L][D]
+    uint16_t *o;                  // [M][n_q][D]
+    float *part_o;                // [n_kv][n_split][rows][D]
+    float *part_ml;               // [n_kv][n_split][rows][2]
+    float *gpart_o;               // [n_kv][kMaxGroups][rows][D]
+    float *gpart_ml;              // [n_kv][kMaxGroups][rows][2]
+    uint32_t *counters;           // [n_kv][kCounterWords]
+    int64_t L;                    // cache row stride (positions)
+    int32_t M, n_q, n_kv, qpg, rows, P, n_split, blocks_per_split, n_blocks;
+    float scale_log2;             // log2(e) / sqrt(D)
+};
+
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// Reductions over the 16 lanes of a DPP row, every lane ending with the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                                 CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_row<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_row<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_row<0x141>(v));   // row_half_mirror
+    return fmaxf(v, dpp_row<0x140>(v));   // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_row<0xB1>(v);
+    v += dpp_row<0x4E>(v);
+    v += dpp_row<0x141>(v);
+    return v + dpp_row<0x140>(v);
+}
+
+// WPR: waves per 16-row query tile (4, 2 or 1 for up to 16, 32 or 64 rows);
+// the waves of a tile split its score position tiles and output column tiles.
+template <int D, int WPR>
+__global__ __launch_bounds__(kAttnThreads) void decode_attention_kernel(AttnArgs a) {
+    constexpr int kKStride = D * 2 + 16;          // LDS bytes per key row
+    constexpr int kVtStride = kBlock * 2 + 16;    // LDS bytes per transposed value row (one column)
+    constexpr int kPStride = kBlock * 2 + 16;     // LDS bytes per probability row
+    constexpr int kChunks = D / 8;                // 16-byte pieces of a row
+    constexpr int kLoads = kBlock * kChunks / kAttnThreads;   // 16-byte loads per thread per tensor
+    constexpr int kKs = D / 32;                   // k steps of the score product
+    constexpr int kCt = D / 16;                   // column tiles of the output
+    constexpr int kPtW = 4 / WPR;                 // position tiles per wave
+    constexpr int kCtW = kCt / WPR;               // column tiles per wave
+    extern __shared__ __align__(16) uint8_t lds[];
+    uint8_t *k_lds = lds;                                  // [64][kKStride]
+    uint8_t *vt_lds = k_lds + kBlock * kKStride;           // [D][kVtStride]
+    uint8_t *p_lds = vt_lds + D * kVtStride;               // [4 row tiles][hi 16, lo 16][kPStride]
+    __shared__ float s_merge[64][2];
+    __shared__ float s_red[4][16];                         // per wave: its part of a row-tile reduction
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+    const int s = blockIdx.x, g = blockIdx.y;
+    const int rows = a.rows;
+    const int qpg = a.qpg;
+    const int lr = lane & 15, lq = lane >> 4;     // operand row / column, k group
+    const int rt = wave / WPR, sw = wave % WPR;   // the wave's row tile, and its part of it
+    const bool computes = rt * 16 < rows;
+
+    // the wave's query tile as score operands (rows past the group read zeros)
+    bf8 qa[kKs];
+    {
+        const int r = rt * 16 + lr;
+        const int i = r / qpg, j = r % qpg;
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) {
+            v4i v = v4i{0, 0, 0, 0};
+            if (r < rows) v = *gptr(reinterpret_cast<const v4i *>(a.q + ((int64_t)i * a.n_q + g * qpg + j) * D + 32 * ks + 8 * lq));
+            qa[ks] = __builtin_bit_cast(bf8, v);
+        }
+    }
+
+    const int b0 = s * a.blocks_per_split;
+    const int b1 = min(a.n_blocks, b0 + a.blocks_per_split);
+    const int64_t used = (int64_t)a.P + a.M;       // positions in the cache
+    const uint16_t *kg = a.k + (int64_t)g * a.L * D, *vg = a.v + (int64_t)g * a.L * D;
+
+    // Loads: wave w covers positions 16 w .. 16 w + 15 (lane & 15), and load u
+    // chunks 4 u .. 4 u + 3 (lane >> 4): 64 contiguous bytes of 16 rows.  The
+    // transposed value tile keeps a column's positions contiguous, rotated by
+    // 8 (d / 8 mod 8) positions, so the four lane groups of a write land on
+    // different banks while every 8-position operand run stays contiguous.
+    v4i kbuf[kLoads], vbuf[kLoads];
+    const int pp = 16 * wave + lr;
+    auto fetch = [&](int b) {
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            const int c = 4 * u + lq;
+            const int64_t pos = (int64_t)b * kBlock + pp;
+            kbuf[u] = v4i{0, 0, 0, 0};
+            vbuf[u] = v4i{0, 0, 0, 0};
+            if (pos < used) {
+                kbuf[u] = *gptr(reinterpret_cast<const v4i *>(kg + pos * D) + c);
+                vbuf[u] = *gptr(reinterpret_cast<const v4i *>(vg + pos * D) + c);
+            }
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            const int c = 4 * u + lq;
+            *reinterpret_cast<v4i *>(k_lds + pp * kKStride + c * 16) = kbuf[u];
+            const uint32_t w[4] = {(uint32_t)vbuf[u].x, (uint32_t)vbuf[u].y, (uint32_t)vbuf[u].z, (uint32_t)vbuf[u].w};
+            const int col = (pp + 8 * (c & 7)) & (kBlock - 1);   // rows 8c .. 8c+7: d / 8 = c
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                *reinterpret_cast<uint16_t *>(vt_lds + (8 * c + e) * kVtStride + col * 2) =
+                    (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
+    };
+
+    // m: the row's running max (the same in every wave of the tile); l: this
+    // wave's part of the running sum (its positions); o: its column tiles
+    float m[4], l[4];
+    f4 o[kCtW];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        m[j] = -INFINITY;
+        l[j] = 0.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < kCtW; ++c) o[c] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    uint8_t *pw = p_lds + rt * 32 * kPStride;     // rows 0-15: bf16 of p, rows 16-31: bf16 of the rest
+
+    if (b0 < b1) fetch(b0);
+    for (int b = b0; b < b1; ++b) {
+        __syncthreads();   // the previous block's LDS is consumed
+        stage();
+        __syncthreads();
+        if (b + 1 < b1) fetch(b + 1);
+        // scores of the wave's position tiles: sc[q][j] = S[row 4 lq + j][position 16 (sw + q WPR) + lr]
+        f4 sc[kPtW];
+        float x[kPtW][4];
+        if (computes) {
+#pragma unroll
+            for (int q = 0; q < kPtW; ++q) {
+                const int pt = sw + q * WPR;
+                f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int ks = 0; ks < kKs; ++ks) {
+                    const bf8 kb = *reinterpret_cast<const bf8 *>(k_lds + (16 * pt + lr) * kKStride + (32 * ks + 8 * lq) * 2);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, acc, 0, 0, 0);
+                }
+                sc[q] = acc;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = rt * 16 + 4 * lq + j;
+                const int64_t lim = r < rows ? (int64_t)a.P + r / qpg : -1;   // last attended position
+                float bm = -INFINITY;
+#pragma unroll
+                for (int q = 0; q < kPtW; ++q) {
+                    const int64_t pos = (int64_t)b * kBlock + 16 * (sw + q * WPR) + lr;
+                    x[q][j] = pos <= lim ? sc[q][j] * a.scale_log2 : -INFINITY;
+                    bm = fmaxf(bm, x[q][j]);
+                }
+                bm = row16_max(bm);
+                if (WPR > 1 && lr == 0) s_red[wave][4 * lq + j] = bm;
+            }
+        }
+        if (WPR > 1) __syncthreads();   // the row maxima of the tile's other waves
+        if (computes) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float bm = x[0][j];
+                if (WPR > 1) {
+                    bm = s_red[rt * WPR][4 * lq + j];
+#pragma unroll
+                    for (int k = 1; k < WPR; ++k) bm = fmaxf(bm, s_red[rt * WPR + k][4 * lq + j]);
+                } else {
+#pragma unroll
+                    for (int q = 1; q < kPtW; ++q) bm = fmaxf(bm, x[q][j]);
+                    bm = row16_max(bm);
+                }
+                const float mn = fmaxf(m[j], bm);
+                float alpha = 1.0f, ps = 0.0f;
+                uint32_t pb[kPtW], pr[kPtW];
+#pragma unroll
+                for (int q = 0; q < kPtW; ++q) pb[q] = pr[q] = 0;
+                if (mn != -INFINITY) {
+                    alpha = exp2f(m[j] - mn);                 // 0 when m was -inf
+#pragma unroll
+                    for (int q = 0; q < kPtW; ++q) {
+                        const float pv = exp2f(x[q][j] - mn);   // 0 at masked positions
+                        pb[q] = f32_to_bf16_bits(pv);
+                        pr[q] = f32_to_bf16_bits(pv - bf16_bits_to_f32(pb[q]));
+                        ps += pv;
+                    }
+                    m[j] = mn;
+                }
+                l[j] = l[j] * alpha + row16_sum(ps);
+#pragma unroll
+                for (int c = 0; c < kCtW; ++c) o[c][j] *= alpha;
+#pragma unroll
+                for (int q = 0; q < kPtW; ++q) {
+                    const int col = 16 * (sw + q * WPR) + lr;
+                    *reinterpret_cast<uint16_t *>(pw + (4 * lq + j) * kPStride + col * 2) = (uint16_t)pb[q];
+                    *reinterpret_cast<uint16_t *>(pw + (16 + 4 * lq + j) * kPStride + col * 2) = (uint16_t)pr[q];
+                }
+            }
+        }
+        if (WPR > 1) {
+            __syncthreads();   // the tile's probabilities from every wave
+        } else {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        if (!computes) continue;
+        // values: O += P V over the wave's column tiles
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const bf8 pa = *reinterpret_cast<const bf8 *>(pw + lr * kPStride + (32 * ks + 8 * lq) * 2);
+            const bf8 pl = *reinterpret_cast<const bf8 *>(pw + (16 + lr) * kPStride + (32 * ks + 8 * lq) * 2);
+#pragma unroll
+            for (int c = 0; c < kCtW; ++c) {
+                const int d = 16 * (sw + c * WPR) + lr;
+                const int col = (32 * ks + 8 * lq + 8 * ((d >> 3) & 7)) & (kBlock - 1);
+                const bf8 vb = *reinterpret_cast<const bf8 *>(vt_lds + d * kVtStride + col * 2);
+                o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[c], 0, 0, 0);
+                o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[c], 0, 0, 0);
+            }
+        }
+    }
+
+    // publish this split's (m, l, o) per row; l is the sum of the tile's waves' parts
+    const int64_t base = ((int64_t)g * a.n_split + s) * rows;
+    if (WPR > 1) {
+        __syncthreads();
+        if (computes && lr == 0)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s_red[wave][4 * lq + j] = l[j];
+        __syncthreads();
+        if (computes)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float t = s_red[rt * WPR][4 * lq + j];
+#pragma unroll
+                for (int k = 1; k < WPR; ++k) t += s_red[rt * WPR + k][4 * lq + j];
+                l[j] = t;
+            }
+    }
+    if (computes) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = rt * 16 + 4 * lq + j;
+            if (r >= rows) continue;
+#pragma unroll
+            for (int c = 0; c < kCtW; ++c) store_shared(a.part_o + (base + r) * D + 16 * (sw + c * WPR) + lr, o[c][j]);
+            if (lr == 0 && sw == 0) {
+                store_shared(a.part_ml + (base + r) * 2, m[j]);
+                store_shared(a.part_ml + (base + r) * 2 + 1, l[j]);
+            }
+        }
+    }
+    // Merge in two levels: the last split of each group of kGroupSplits to
+    // count in merges the group into an unnormalised group partial, and the
+    // last group of the head to count in merges the groups into the output.
+    // A merge stages the partials' (m, l) in LDS (over the staging area, free
+    // now), turns them into weights 2^(m_t - M) (over L for the output), and
+    // sums the o's with the loads of four outputs times eight partials in
+    // flight per thread.
+    auto merge = [&](const float *ml, const float *op, int n, bool final, float *dml, float *dop) {
+        float *wl = reinterpret_cast<float *>(k_lds);   // [n][rows]: m, then the weight
+        float *ll = wl + n * rows;                      // [n][rows]: l
+        for (int idx = tid; idx < n * rows; idx += kAttnThreads) {
+            wl[idx] = load_shared(ml + (int64_t)idx * 2);
+            ll[idx] = load_shared(ml + (int64_t)idx * 2 + 1);
+        }
+        __syncthreads();
+        for (int r = tid; r < rows; r += kAttnThreads) {
+            float mx = -INFINITY;
+            for (int t = 0; t < n; ++t) mx = fmaxf(mx, wl[t * rows + r]);
+            float den = 0.0f;
+            for (int t = 0; t < n; ++t) {
+                const float mt = wl[t * rows + r];
+                if (mt != -INFINITY) den += ll[t * rows + r] * exp2f(mt - mx);
+            }
+            s_merge[r][0] = mx;
+            s_merge[r][1] = den;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < n * rows; idx += kAttnThreads) {
+            const int r = idx % rows;
+            const float mt = wl[idx];
+            wl[idx] = mt == -INFINITY ? 0.0f : exp2f(mt - s_merge[r][0]) / (final ? s_merge[r][1] : 1.0f);
+        }
+        __syncthreads();
+        constexpr int kOut = 4;
+        for (int i0 = tid; i0 < rows * D; i0 += kOut * kAttnThreads) {
+            float acc[kOut];
+#pragma unroll
+            for (int q = 0; q < kOut; ++q) acc[q] = 0.0f;
+            for (int t0 = 0; t0 < n; t0 += 8) {
+                float pv[kOut][8];
+#pragma unroll
+                for (int q = 0; q < kOut; ++q) {
+                    const int idx = i0 + q * kAttnThreads;
+                    const int r = idx / D, d = idx % D;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        pv[q][u] = idx < rows * D && t0 + u < n ? load_shared(op + ((int64_t)(t0 + u) * rows + r) * D + d) : 0.0f;
+                }
+#pragma unroll
+                for (int q = 0; q < kOut; ++q) {
+                    const int idx = i0 + q * kAttnThreads;
+                    const int r = idx / D;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (idx < rows * D && t0 + u < n) acc[q] = fmaf(pv[q][u], wl[(t0 + u) * rows + r], acc[q]);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kOut; ++q) {
+                const int idx = i0 + q * kAttnThreads;
+                if (idx >= rows * D) continue;
+                const int r = idx / D, d = idx % D;
+                if (final) {
+                    const int i = r / qpg, j = r % qpg;
+                    a.o[((int64_t)i * a.n_q + g * qpg + j) * D + d] = (uint16_t)f32_to_bf16_bits(acc[q]);
+                } else {
+                    store_shared(dop + (int64_t)r * D + d, acc[q]);
+                }
+            }
+        }
+        if (!final)
+            for (int r = tid; r < rows; r += kAttnThreads) {
+                store_shared(dml + (int64_t)r * 2, s_merge[r][0]);
+                store_shared(dml + (int64_t)r * 2 + 1, s_merge[r][1]);
+            }
+        __syncthreads();
+    };
+
+    __shared__ uint32_t s_last;
+    uint32_t *cnt = a.counters + (int64_t)g * kCounterWords;
+    const int grp = s / kGroupSplits, n_groups = (a.n_split + kGroupSplits - 1) / kGroupSplits;
+    const int g0 = grp * kGroupSplits, gn = min(a.n_split - g0, kGroupSplits);
+    wait_memory();
+    __syncthreads();
+    if (tid == 0) s_last = counter_add(cnt + 1 + grp, 1u) == (uint32_t)(gn - 1) ? 1u : 0u;
+    __syncthreads();
+    if (!s_last) return;
+    if (tid == 0) store_shared(cnt + 1 + grp, 0u);   // ready for the next launch
+    if (n_groups == 1) {   // one group: its merge is the output
+        merge(a.part_ml + (int64_t)g * a.n_split * rows * 2, a.part_o + (int64_t)g * a.n_split * rows * D, gn, true,
+              nullptr, nullptr);
+        return;
+    }
+    const int64_t gb = (int64_t)g * kMaxGroups + grp;
+    merge(a.part_ml + ((int64_t)g * a.n_split + g0) * rows * 2, a.part_o + ((int64_t)g * a.n_split + g0) * rows * D, gn,
+          false, a.gpart_ml + gb * rows * 2, a.gpart_o + gb * rows * D);
+    wait_memory();
+    __syncthreads();
+    if (tid == 0) s_last = counter_add(cnt, 1u) == (uint32_t)(n_groups - 1) ? 1u : 0u;
+    __syncthreads();
+    if (!s_last) return;
+    if (tid == 0) store_shared(cnt, 0u);
+    merge(a.gpart_ml + (int64_t)g * kMaxGroups * rows * 2, a.gpart_o + (int64_t)g * kMaxGroups * rows * D, n_groups,
+          true, nullptr, nullptr);
+}
+
+}  // namespace
+
+AttnPlan plan_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P, int n_cu) {
+    AttnPlan pl;
+    const int64_t used = P + M;
+    pl.n_blocks = (used + kBlock - 1) / kBlock;
+    pl.rows = (n_q / n_kv) * M;
+    // keys, transposed values, the row tiles' probabilities; a merge reuses the
+    // area for two floats per merged partial and row
+    const int64_t row_tiles = (pl.rows + 15) / 16;
+    pl.lds_bytes = (int)std::max<int64_t>(kBlock * (D * 2 + 16) + D * (kBlock * 2 + 16) + row_tiles * 32 * (kBlock * 2 + 16),
+                                          std::max<int64_t>(kGroupSplits, kMaxGroups) * pl.rows * 8);
+    // a workgroup per CU, two where their LDS fits (one hides the other's
+    // load latency), and at least kMinBlocks blocks each (a split's fixed
+    // cost -- the query load, the first fetch, publishing -- is latency)
+    constexpr int64_t kMinBlocks = 4;
+    // (the one-tile form's registers also allow two waves per SIMD)
+    const int64_t per_cu = row_tiles == 1 && pl.lds_bytes <= 80 * 1024 ? 2 : 1;
+    const int64_t target = std::max<int64_t>(
+        1, std::min<int64_t>({kMaxSplits, per_cu * n_cu / n_kv, (pl.n_blocks + kMinBlocks - 1) / kMinBlocks}));
+    const int64_t want = std::min<int64_t>(pl.n_blocks, target);
+    pl.blocks_per_split = (pl.n_blocks + want - 1) / want;
+    pl.n_split = (pl.n_blocks + pl.blocks_per_split - 1) / pl.blocks_per_split;
+    // [counters][m, l per split and row][o per split and row]: the counters
+    // come first so that every call on one workspace finds them in one place
+    const int64_t part_o = n_kv * pl.n_split * pl.rows * D * 4;
+    const int64_t part_ml = n_kv * pl.n_split * pl.rows * 2 * 4;
+    const int64_t gpart_o = n_kv * kMaxGroups * pl.rows * D * 4;
+    const int64_t gpart_ml = n_kv * kMaxGroups * pl.rows * 2 * 4;
+    auto up = [](int64_t v) { return (v + 255) / 256 * 256; };
+    pl.off_cnt = 0;
+    pl.off_ml = up(n_kv * kCounterWords * 4);
+    pl.off_o = pl.off_ml + up(part_ml);
+    pl.off_gml = pl.off_o + up(part_o);
+    pl.off_go = pl.off_gml + up(gpart_ml);
+    pl.ws_bytes = pl.off_go + up(gpart_o);
+    return pl;
+}
+
+hipError_t launch_attention(const AttnPlan &pl, int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P,
+                            int64_t L, const void *q, const void *k, const void *v, void *o, void *ws,
+                            hipStream_t st) {
+    AttnArgs a;
+    a.q = (const uint16_t *)q;
+    a.k = (const uint16_t *)k;
+    a.v = (const uint16_t *)v;
+    a.o = (uint16_t *)o;
+    a.part_o = (float *)((char *)ws + pl.off_o);
+    a.part_ml = (float *)((char *)ws + pl.off_ml);
+    a.gpart_ml = (float *)((char *)ws + pl.off_gml);
+    a.gpart_o = (float *)((char *)ws + pl.off_go);
+    a.counters = (uint32_t *)((char *)ws + pl.off_cnt);
+    a.L = L;
+    a.M = (int32_t)M;
+    a.n_q = (int32_t)n_q;
+    a.n_kv = (int32_t)n_kv;
+    a.qpg = (int32_t)(n_q / n_kv);
+    a.rows = (int32_t)pl.rows;
+    a.P = (int32_t)P;
+    a.n_split = (int32_t)pl.n_split;
+    a.blocks_per_split = (int32_t)pl.blocks_per_split;
+    a.n_blocks = (int32_t)pl.n_blocks;
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    const int wpr = pl.rows <= 16 ? 4 : pl.rows <= 32 ? 2 : 1;
+#define MBQ_ATTN(DD) \
+    (wpr == 4 ? reinterpret_cast<const void *>(&decode_attention_kernel<DD, 4>)   \
+     : wpr == 2 ? reinterpret_cast<const void *>(&decode_attention_kernel<DD, 2>) \
+                : reinterpret_cast<const void *>(&decode_attention_kernel<DD, 1>))
+    const void *fn = D == 64 ? MBQ_ATTN(64) : D == 128 ? MBQ_ATTN(128) : MBQ_ATTN(256);
+#undef MBQ_ATTN
+    void *args[] = {(void *)&a};
+    return hipLaunchKernel(fn, dim3((unsigned)pl.n_split, (unsigned)n_kv), dim3(kAttnThreads), args,
+                           (size_t)pl.lds_bytes, st);
+}
+
+}  // namespace mbq

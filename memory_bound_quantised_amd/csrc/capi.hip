@@ -261,6 +261,44 @@ int mbq_relayout_interleave_host(int bits, int64_t N, int64_t K, void *host_buf,
     return relayout_interleave_host(bits, N, K, (uint8_t *)host_buf);
 }
 
+static bool attn_shape_ok(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P) {
+    return m_ok(M) && n_kv >= 1 && n_q >= n_kv && n_q % n_kv == 0 && n_q <= 4096 && (n_q / n_kv) * M <= 64 &&
+           (D == 64 || D == 128 || D == 256) && P >= 0 && P + M <= ((int64_t)1 << 30);
+}
+
+static int attn_cus(int *n_cu) {
+    int n = 0;
+    if (hipGetDeviceCount(&n) == hipSuccess && n > 0 && device_cus(n_cu) == MBQ_OK) return MBQ_OK;
+    *n_cu = 256;   // without a device: the MI355X's CU count
+    return MBQ_OK;
+}
+
+int64_t mbq_attention_workspace_bytes(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P) {
+    if (!attn_shape_ok(M, n_q, n_kv, D, P)) return MBQ_ERR_SHAPE;
+    int n_cu = 256;
+    attn_cus(&n_cu);
+    return plan_attention(M, n_q, n_kv, D, P, n_cu).ws_bytes;
+}
+
+int mbq_decode_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P, int64_t L, const void *q,
+                         const void *k_cache, const void *v_cache, void *o, void *ws, int64_t ws_bytes,
+                         void *stream) {
+    if (!q || !k_cache || !v_cache || !o) return MBQ_ERR_NULL;
+    if (!attn_shape_ok(M, n_q, n_kv, D, P) || L < P + M) return MBQ_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 2)) return MBQ_ERR_ALIGN;
+    if (!ws) return MBQ_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return MBQ_ERR_ALIGN;
+    int st = check_device();
+    if (st) return st;
+    int n_cu = 0;
+    st = device_cus(&n_cu);
+    if (st) return st;
+    const AttnPlan pl = plan_attention(M, n_q, n_kv, D, P, n_cu);
+    if (ws_bytes < pl.ws_bytes) return MBQ_ERR_WORKSPACE;
+    hipError_t e = launch_attention(pl, M, n_q, n_kv, D, P, L, q, k_cache, v_cache, o, ws, (hipStream_t)stream);
+    return e == hipSuccess ? MBQ_OK : hip_fail(e);
+}
+
 int64_t mbq_sequence_workspace_bytes(const mbq_op *ops, int32_t n_ops, const int64_t *buf_widths,
                                      int32_t n_bufs, int64_t M) {
     const int64_t unfused = analyse_program(ops, n_ops, buf_widths, n_bufs, M, nullptr);

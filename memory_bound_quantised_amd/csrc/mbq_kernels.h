@@ -50,6 +50,17 @@ int relayout_interleave_host(int bits, int64_t N, int64_t K, uint8_t *buf);
 // MBQ_ERR_HIP, *hip_err holds the failing call's error.
 int relayout_inplace(int bits, int64_t N, int64_t K, void *buf, int n_cu, hipStream_t s, hipError_t *hip_err);
 
+// Split-prefix decode attention (attn.hip).
+struct AttnPlan {
+    int64_t n_blocks = 0, blocks_per_split = 0, n_split = 0, rows = 0;
+    int64_t off_cnt = 0, off_ml = 0, off_o = 0, off_gml = 0, off_go = 0, ws_bytes = 0;
+    int lds_bytes = 0;
+};
+AttnPlan plan_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P, int n_cu);
+hipError_t launch_attention(const AttnPlan &pl, int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P,
+                            int64_t L, const void *q, const void *k, const void *v, void *o, void *ws,
+                            hipStream_t st);
+
 hipError_t launch_pack(int bits, int64_t N, int64_t K, const void *canon, const void *scales,
                        void *packed, hipStream_t s);
 hipError_t launch_unpack(int bits, int64_t N, int64_t K, const void *packed, void *canon,
