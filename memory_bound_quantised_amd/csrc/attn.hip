@@ -126,6 +126,10 @@ __global__ __launch_bounds__(kAttnThreads) void decode_attention_kernel(AttnArgs
     // transposed value tile keeps a column's positions contiguous, rotated by
     // 8 (d / 8 mod 8) positions, so the four lane groups of a write land on
     // different banks while every 8-position operand run stays contiguous.
+    // With one position tile per wave (WPR = 4) the keys are not staged:
+    // load u of a wave is exactly its score operand for k step u (position
+    // 16 w + lr, k 32 u + 8 lq .. +7), kept in registers until the block's
+    // scores.
     v4i kbuf[kLoads], vbuf[kLoads];
     const int pp = 16 * wave + lr;
     auto fetch = [&](int b) {
@@ -141,11 +145,14 @@ __global__ __launch_bounds__(kAttnThreads) void decode_attention_kernel(AttnArgs
             }
         }
     };
+    static_assert(WPR != 4 || kLoads == kKs, "one key load per k step");
+    v4i kop[WPR == 4 ? kKs : 1];
     auto stage = [&]() {
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) {
             const int c = 4 * u + lq;
-            *reinterpret_cast<v4i *>(k_lds + pp * kKStride + c * 16) = kbuf[u];
+            if constexpr (WPR == 4) kop[u] = kbuf[u];
+            else *reinterpret_cast<v4i *>(k_lds + pp * kKStride + c * 16) = kbuf[u];
             const uint32_t w[4] = {(uint32_t)vbuf[u].x, (uint32_t)vbuf[u].y, (uint32_t)vbuf[u].z, (uint32_t)vbuf[u].w};
             const int col = (pp + 8 * (c & 7)) & (kBlock - 1);   // rows 8c .. 8c+7: d / 8 = c
 #pragma unroll
@@ -184,7 +191,9 @@ __global__ __launch_bounds__(kAttnThreads) void decode_attention_kernel(AttnArgs
                 f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int ks = 0; ks < kKs; ++ks) {
-                    const bf8 kb = *reinterpret_cast<const bf8 *>(k_lds + (16 * pt + lr) * kKStride + (32 * ks + 8 * lq) * 2);
+                    bf8 kb;
+                    if constexpr (WPR == 4) kb = __builtin_bit_cast(bf8, kop[ks < (WPR == 4 ? kKs : 1) ? ks : 0]);
+                    else kb = *reinterpret_cast<const bf8 *>(k_lds + (16 * pt + lr) * kKStride + (32 * ks + 8 * lq) * 2);
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, acc, 0, 0, 0);
                 }
                 sc[q] = acc;

@@ -253,7 +253,7 @@ __device__ __forceinline__ void quant_cols(const SeqPlan *P, const Lay &L, const
                 for (int u = 0; u < x_batch<M>(); ++u)
 #pragma unroll
                     for (int m = 0; m < M; ++m)
-                        stale |= j0 + threadIdx.x + u * kSeqThreads < words && tag_of(xw[u][m]) != want;
+                        stale |= j0 + (int)threadIdx.x + u * kSeqThreads < words && tag_of(xw[u][m]) != want;
                 if (!wave_any(stale) || gave_up(P, spins)) break;
 #pragma unroll
                 for (int u = 0; u < x_batch<M>(); ++u) {
@@ -313,7 +313,6 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
     const bool weighted = ph.norm_w != nullptr;
     const uint32_t want = make_tag(gen, ph.in_phase);
     const int words = (h.k_hi - h.k_lo) >> 1;          // bf16 pairs per activation row
-    const bool tagged_in = ph.in_xt != nullptr;
     const bool has = h.k_hi > h.k_lo;
     const bool need_scale = has || h.n_fin > 0;   // finalising rescales by the input scale
 
