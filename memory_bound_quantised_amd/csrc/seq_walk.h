@@ -413,24 +413,24 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
 
 // ---------------------------------------------------------------- hand-over of a phase
 
-// Gather a row block's contributions (lane l's M tagged words of contribution
-// c at area + (c * 64 + l) * M) in their fixed order, write its bf16 outputs,
-// their tagged copy and its stats record (the caller counts it as done).
-template <int BITS, int M>
-__device__ __forceinline__ void finalize_rb(const SeqPlan *P, const uint64_t *area, uint32_t tag, const SeqFin &f,
-                                            const float *s_act, int64_t stat_stride, int64_t stat_rep, int lane) {
-    using Lt = Layout<BITS>;
-    float tot[M];
+// Sum contributions [c_begin, c_end) of the partial area (lane l's M tagged
+// words of contribution c at area + (c * 64 + l) * M) in their fixed order
+// into tot, re-polling stale words.  PAIR: contributions from index split on
+// (a gate block's up partner) go to a fresh sum: the sums before it end up in
+// tot2.
+template <int M, bool PAIR>
+__device__ __forceinline__ void gather_sum(const SeqPlan *P, const uint64_t *area, uint32_t tag, int c_begin,
+                                           int c_end, int split, float (&tot)[M], float (&tot2)[M], int lane) {
 #pragma unroll
-    for (int m = 0; m < M; ++m) tot[m] = 0.0f;
+    for (int m = 0; m < M; ++m) tot[m] = tot2[m] = 0.0f;
     constexpr int B = 32 / M;   // contributions per round trip (within the vector-memory counter)
-    for (int c0 = 0; c0 < f.nc; c0 += B) {
+    for (int c0 = c_begin; c0 < c_end; c0 += B) {
         uint64_t v[B][M];
 #pragma unroll
         for (int u = 0; u < B; ++u) {
-            const uint64_t *src = area + ((int64_t)(f.c0 + c0 + u) * 64 + lane) * M;
+            const uint64_t *src = area + ((int64_t)(c0 + u) * 64 + lane) * M;
 #pragma unroll
-            for (int m = 0; m < M; ++m) v[u][m] = c0 + u < f.nc ? load_shared(src + m) : 0;
+            for (int m = 0; m < M; ++m) v[u][m] = c0 + u < c_end ? load_shared(src + m) : 0;
         }
         // re-poll every stale word together: one round trip per round
         int64_t spins = 0;
@@ -439,24 +439,51 @@ __device__ __forceinline__ void finalize_rb(const SeqPlan *P, const uint64_t *ar
 #pragma unroll
             for (int u = 0; u < B; ++u)
 #pragma unroll
-                for (int m = 0; m < M; ++m) stale |= c0 + u < f.nc && tag_of(v[u][m]) != tag;
+                for (int m = 0; m < M; ++m) stale |= c0 + u < c_end && tag_of(v[u][m]) != tag;
             if (!wave_any(stale) || gave_up(P, spins)) break;
 #pragma unroll
             for (int u = 0; u < B; ++u) {
-                const uint64_t *src = area + ((int64_t)(f.c0 + c0 + u) * 64 + lane) * M;
+                const uint64_t *src = area + ((int64_t)(c0 + u) * 64 + lane) * M;
 #pragma unroll
                 for (int m = 0; m < M; ++m)
-                    if (c0 + u < f.nc && tag_of(v[u][m]) != tag) v[u][m] = load_shared(src + m);
+                    if (c0 + u < c_end && tag_of(v[u][m]) != tag) v[u][m] = load_shared(src + m);
             }
         }
 #pragma unroll
         for (int u = 0; u < B; ++u) {
-            if (c0 + u < f.nc) {
+            if constexpr (PAIR) {
+                if (uniform(c0 + u == split)) {   // wave-uniform: plain blocks pay nothing
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        tot2[m] = tot[m];
+                        tot[m] = 0.0f;
+                    }
+                }
+            }
+            if (c0 + u < c_end) {
 #pragma unroll
                 for (int m = 0; m < M; ++m) tot[m] += __uint_as_float((uint32_t)v[u][m]);
             }
         }
     }
+    // a range wholly before the split holds gate sums only
+    if constexpr (PAIR) {
+        if (uniform(split >= c_end ? 1 : 0)) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                tot2[m] = tot[m];
+                tot[m] = 0.0f;
+            }
+        }
+    }
+}
+
+// A row block's outputs from its contribution sums: the bf16 outputs, their
+// tagged copy and its stats record (the caller counts it as done).
+template <int BITS, int M>
+__device__ __forceinline__ void emit_rb(const SeqFin &f, uint32_t tag, const float (&tot)[M], const float *s_act,
+                                        int64_t stat_stride, int64_t stat_rep, int lane) {
+    using Lt = Layout<BITS>;
     const float unscale = 1.0f / (float)(1 << Lt::kAccShift);
     float yv[M];
 #pragma unroll
@@ -475,63 +502,16 @@ __device__ __forceinline__ void finalize_rb(const SeqPlan *P, const uint64_t *ar
 }
 
 // The same for walks with weighted RMSNorms or SwiGLU pairs: a gate block
-// paired with its up block gathers both in one pass, writes both outputs and
-// hands over silu(gate) * up; a consumer's norm weights scale the maxima.
+// paired with its up block (tot2: gate sums, tot: up sums) writes both outputs
+// and hands over silu(gate) * up; a consumer's norm weights scale the maxima.
 template <int BITS, int M>
-__device__ __forceinline__ void finalize_rb_full(const SeqPlan *P, const uint64_t *area, uint32_t tag, const SeqFin &f,
-                                            const float *s_act, int64_t stat_stride, int64_t stat_rep, int lane) {
+__device__ __forceinline__ void emit_rb_full(const SeqFin &f, uint32_t tag, const float (&tot)[M],
+                                             const float (&tot2)[M], const float *s_act, int64_t stat_stride,
+                                             int64_t stat_rep, int lane) {
     using Lt = Layout<BITS>;
-    float tot[M], tot2[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) tot[m] = tot2[m] = 0.0f;
-    // a pair's up contributions follow the gate's: at that boundary the gate
-    // sums move to tot2 (a wave-uniform test, so plain blocks pay nothing)
-    const int n_all = f.nc + f.nc_2;
-    const int split = f.nc_2 > 0 ? f.nc : -1;
-    constexpr int B = 32 / M;   // contributions per round trip (within the vector-memory counter)
-    for (int c0 = 0; c0 < n_all; c0 += B) {
-        uint64_t v[B][M];
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-            const uint64_t *src = area + ((int64_t)(f.c0 + c0 + u) * 64 + lane) * M;
-#pragma unroll
-            for (int m = 0; m < M; ++m) v[u][m] = c0 + u < n_all ? load_shared(src + m) : 0;
-        }
-        // re-poll every stale word together: one round trip per round
-        int64_t spins = 0;
-        for (;;) {
-            bool stale = false;
-#pragma unroll
-            for (int u = 0; u < B; ++u)
-#pragma unroll
-                for (int m = 0; m < M; ++m) stale |= c0 + u < n_all && tag_of(v[u][m]) != tag;
-            if (!wave_any(stale) || gave_up(P, spins)) break;
-#pragma unroll
-            for (int u = 0; u < B; ++u) {
-                const uint64_t *src = area + ((int64_t)(f.c0 + c0 + u) * 64 + lane) * M;
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-                    if (c0 + u < n_all && tag_of(v[u][m]) != tag) v[u][m] = load_shared(src + m);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-            if (uniform(c0 + u == split)) {
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    tot2[m] = tot[m];
-                    tot[m] = 0.0f;
-                }
-            }
-            if (c0 + u < n_all) {
-#pragma unroll
-                for (int m = 0; m < M; ++m) tot[m] += __uint_as_float((uint32_t)v[u][m]);
-            }
-        }
-    }
     const float unscale = 1.0f / (float)(1 << Lt::kAccShift);
     float yv[M], ya[M];
-    if (uniform(f.out2 != nullptr ? 1 : 0)) {   // a gate/up pair: tot2 holds the gate, tot the up sums
+    if (uniform(f.out2 != nullptr ? 1 : 0)) {
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             const int64_t idx = (int64_t)m * f.row_words + (lane >> 1);
@@ -602,10 +582,15 @@ __device__ __forceinline__ void leave_phase(const SeqPlan *P, const Lay &L, int 
 }
 
 // A finalising workgroup's row blocks of phase p, spread over its waves.
+// With one or two blocks and more contributions than one round trip gathers,
+// 4 / n_fin waves share each block: each sums a contiguous quarter (or half)
+// of its contributions, and the block's first wave adds those sums in wave
+// order (a fixed order, so results stay reproducible) and emits the block.
+// c_sh: kSeqWaves x (X ? 2 : 1) x M x 64 floats of LDS.
 // Inline: a call would wait for every outstanding store on entry and exit.
 template <int BITS, int M, bool X>
 __device__ __forceinline__ void finalize_phase(const SeqPlan *P, const Lay &L, int p, uint32_t gen,
-                                            const float *s_act) {
+                                            const float *s_act, float *c_sh) {
     const SeqWgHead h = *meta_head(L, p);
     const int lane = threadIdx.x & 63;
     const int j = uniform(threadIdx.x >> 6);
@@ -613,14 +598,53 @@ __device__ __forceinline__ void finalize_phase(const SeqPlan *P, const Lay &L, i
     const uint64_t *area = cload(&P->partials) + (int64_t)(p & 1) * L.part_stride * 64 * M;
     uint32_t *fin_count = meta_phase(L, p)->fin_count;
     const int64_t stat_stride = cload(&P->stat_stride), stat_rep = cload(&P->stat_rep);
+    constexpr int B = 32 / M;
+    bool share = false;
+    // at M = 1 one round trip holds 32 contributions: the shared form stays out
+    if (M > 1 && h.n_fin >= 1 && h.n_fin <= 2)
+        for (int i = 0; i < h.n_fin; ++i) {
+            const SeqFin &f = meta_fin(L, p)[i];
+            share |= f.nc + f.nc_2 > B;
+        }
+    share = M > 1 && uniform(share ? 1 : 0) != 0;
+    // shared: wave j takes part j % g of block j / g (one pass); else wave j
+    // takes blocks j, j + 4, ... whole
+    const int g = share ? kSeqWaves / h.n_fin : 1;
+    const int part = share ? j % g : 0;
     uint32_t done = 0;
-    for (int i = j; i < h.n_fin; i += kSeqWaves) {
+    for (int i = share ? j / g : j; i < h.n_fin; i += kSeqWaves) {
         const SeqFin f = meta_fin(L, p)[i];
+        const int n_all = f.nc + f.nc_2;
+        const int a = f.c0 + n_all * part / g, b = f.c0 + n_all * (part + 1) / g;
+        float tot[M], tot2[M];
+        if constexpr (X)
+            gather_sum<M, true>(P, area, tag, a, b, f.nc_2 > 0 ? f.c0 + f.nc : -1, tot, tot2, lane);
+        else
+            gather_sum<M, false>(P, area, tag, a, b, -1, tot, tot2, lane);
+        if (share) {
+            constexpr int NS = X ? 2 : 1;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                c_sh[((j * NS + 0) * M + m) * 64 + lane] = tot[m];
+                if constexpr (X) c_sh[((j * NS + 1) * M + m) * 64 + lane] = tot2[m];
+            }
+            __syncthreads();   // every wave passes here exactly once
+            if (part != 0) break;
+#pragma unroll
+            for (int m = 0; m < M; ++m) tot[m] = tot2[m] = 0.0f;
+            for (int w = j; w < j + g; ++w) {
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    tot[m] += c_sh[((w * NS + 0) * M + m) * 64 + lane];
+                    if constexpr (X) tot2[m] += c_sh[((w * NS + 1) * M + m) * 64 + lane];
+                }
+            }
+        }
         if constexpr (X) {
-            finalize_rb_full<BITS, M>(P, area, tag, f, s_act, stat_stride, stat_rep, lane);
+            emit_rb_full<BITS, M>(f, tag, tot, tot2, s_act, stat_stride, stat_rep, lane);
             done += f.out2 ? 2u : 1u;
         } else {
-            finalize_rb<BITS, M>(P, area, tag, f, s_act, stat_stride, stat_rep, lane);
+            emit_rb<BITS, M>(f, tag, tot, s_act, stat_stride, stat_rep, lane);
             ++done;
         }
     }
@@ -832,6 +856,7 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const SeqPlan *__restr
                                                           uint32_t gen) {
     __shared__ float s_sh[2][kMaxM];
     __shared__ float r_sh[2][kMaxM];
+    __shared__ float c_sh[kSeqWaves * (X ? 2 : 1) * M * 64];   // shared gathers of a finaliser
     // the workspace must hold a prepared plan, made for this form of the kernel
     if (cload(&P->magic) != kPlanMagic || cload(&P->full) != (X ? 1 : 0)) {
         if (threadIdx.x == 0 && blockIdx.x == 0) store_shared(err, 2u);
@@ -882,7 +907,7 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const SeqPlan *__restr
         // the others start the next phase's weight stream (wave 0 at once,
         // the rest paced), after a barrier that keeps any wave's loads from
         // queueing ahead of another wave's partials.
-        if (finaliser) finalize_phase<BITS, M, X>(P, L, p, gen, s_sh[p & 1]);
+        if (finaliser) finalize_phase<BITS, M, X>(P, L, p, gen, s_sh[p & 1], c_sh);
         else __syncthreads();
         if (p + 1 == L.n_phases) break;
         prime<BITS, D, 0, D>(is, lane, uniform(meta_head(L, p + 1)->tiles[wi]), ring, wi != 0);

@@ -54,14 +54,22 @@ struct PhaseGeom {
 };
 
 // Share of a phase's tiles given to a wave of a non-finalising workgroup,
-// relative to a finalising one.
-double other_weight() {
-    static const double w = [] {
+// relative to a finalising one.  A finaliser's hand-over work grows with M (it
+// gathers M words per contribution, 32 / M contributions per round trip), so
+// from M = 3 on the finalisers take a third of the tiles (2.0 cut 9B- and
+// 27B-shaped W4 walks by 4-11 % at M = 3..8; it costs 1-4 % at M = 1..2).
+// It also decides where the ranges end: at 2.0 most of those walks' ranges
+// are whole numbers of tiles per wave, which keeps a row block's
+// contributions (and the finaliser's round trips) few.  MBQ_SPLIT_WEIGHT
+// overrides it.
+double other_weight(int64_t M) {
+    static const double env = [] {
         const char *e = getenv("MBQ_SPLIT_WEIGHT");
-        const double v = e ? atof(e) : 1.0;
-        return v > 0.05 && v < 20.0 ? v : 1.0;
+        const double v = e ? atof(e) : 0.0;
+        return v > 0.05 && v < 20.0 ? v : 0.0;
     }();
-    return w;
+    if (env > 0.0) return env;
+    return M >= 3 ? 2.0 : 1.0;
 }
 
 }  // namespace
@@ -205,7 +213,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
         const int64_t T = R * g.G;
         if (T >= ((int64_t)1 << 31)) return MBQ_ERR_SHAPE;
         g.T = (int)T;
-        g.cut(waves, grid, other_weight());
+        g.cut(waves, grid, other_weight(M));
         for (int w = 0; w < g.W; ++w) {
             const int t0 = g.start(w), t1 = g.start(w + 1) - 1;
             const int sc = g.segment(t1) - g.segment(t0) + 1;
@@ -332,7 +340,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     const int q_stride = (int)up(q_span, 16);
     const int64_t meta_bytes = up(sizeof(SeqPhase) + blk_bytes, 16);
     const int64_t lds = M * q_stride + (int64_t)kSeqWaves * slots * M * 64 * 4 + 2 * meta_bytes;
-    if (lds > 150 * 1024) return MBQ_ERR_SHAPE;
+    if (lds > 132 * 1024) return MBQ_ERR_SHAPE;   // plus the kernel's static LDS (up to 17 KB)
 
     // ---- workspace layout
     const int64_t off_err = 0;
