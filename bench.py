@@ -172,7 +172,8 @@ def run_attention(args):
         "config": {"workload": f"split-prefix decode attention, 32 query / 4 key-value heads of 256, "
                                f"{P}-token bf16 cache, M={args.m}", "ctx": P, "M": args.m, **ATTN_SHAPE},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "decode_attention_kernel (1 launch per call)", "achieved": round(gbs, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_attention_kernel, then attn_merge_kernel when the prefix has "
+                               "several splits (timed together per call)", "achieved": round(gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": r["kv_bytes"], "launch_ms": round(r["ms"], 4)},
     }

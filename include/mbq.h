@@ -179,8 +179,8 @@ int mbq_linear_group_acc(int bits, int64_t M, int64_t N, int64_t K, const int8_t
  * "Paying attention to the attention!": the grouped-query attention of a decode
  * step for a short query -- the committed token, or it and the MTP draft rows
  * with their causal verification -- without a materialised mask.  The cached
- * prefix is split across many workgroups, and the last of each key/value head
- * to finish combines the partial softmax results in the same launch.
+ * prefix is split across many workgroups; a second kernel on the same stream
+ * combines their partial softmax results (none when one split covers it).
  *
  * q: device bf16 [M][n_q][D]; k_cache, v_cache: device bf16 [n_kv][L][D]
  * (row stride D, head stride L * D) holding the M new tokens' keys and values
@@ -189,11 +189,9 @@ int mbq_linear_group_acc(int bits, int64_t M, int64_t N, int64_t K, const int8_t
  * scores are scaled by 1/sqrt(D); softmax and sums in fp32.
  * Shapes: M in 1..8, D in {64, 128, 256}, n_q a multiple of n_kv with
  * (n_q / n_kv) * M <= 64, L >= P + M.  q and the caches 16-byte aligned.
- * ws: device, 256-byte aligned, >= mbq_attention_workspace_bytes(...) bytes,
- * zero-filled before its first use; every call leaves it ready for the next,
- * whatever its shape (calls sharing a workspace must not overlap).  Its first
- * 256 bytes per key/value head count the finished splits and groups of
- * splits; the last of each clears its count.  Enqueued on `stream`. */
+ * ws: device, 256-byte aligned, >= mbq_attention_workspace_bytes(...) bytes
+ * of scratch for the partial results (any contents; calls sharing a workspace
+ * must not overlap).  Enqueued on `stream`. */
 int64_t mbq_attention_workspace_bytes(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P);
 int mbq_decode_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P, int64_t L, const void *q,
                          const void *k_cache, const void *v_cache, void *o, void *ws, int64_t ws_bytes,

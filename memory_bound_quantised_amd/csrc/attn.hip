@@ -19,9 +19,12 @@
 //            products, about 16 significant bits; bf16 alone loses a percent
 //            where values cancel), going through LDS to take the operand
 //            layout.
-// Each workgroup publishes (m, l, o) per row with agent-scope stores; the last
-// to count in for its head merges the splits: M = max m_s, L = sum l_s
-// 2^(m_s - M), O = sum o_s 2^(m_s - M) / L.
+// Each workgroup publishes (m, l, o) per row (the only split of a head writes
+// the output itself), and a second kernel, wide over (head, output columns),
+// merges the splits: M = max m_s, L = sum l_s 2^(m_s - M), O = sum o_s
+// 2^(m_s - M) / L.  Merging in the split kernel itself -- the last split of a
+// head to finish -- leaves the whole merge to one workgroup, whose round trips
+// at 64 rows x 256 columns cost more than the second launch.
 #include <algorithm>
 
 #include "mbq.h"
@@ -33,11 +36,11 @@ namespace mbq {
 namespace {
 
 constexpr int kBlock = 64;        // positions per block
-constexpr int kGroupSplits = 8;   // splits merged together first
 constexpr int kMaxSplits = 128;
-constexpr int kMaxGroups = kMaxSplits / kGroupSplits;
-constexpr int kCounterWords = 64; // per key/value head: [0] groups done, [1 + k] splits of group k done
 constexpr int kAttnThreads = 256;
+#ifndef MBQ_ATTN_MIN_BLOCKS
+#define MBQ_ATTN_MIN_BLOCKS 2
+#endif
 
 struct AttnArgs {
     const uint16_t *q;            // [M][n_q][D]
@@ -45,9 +48,6 @@ struct AttnArgs {
     uint16_t *o;                  // [M][n_q][D]
     float *part_o;                // [n_kv][n_split][rows][D]
     float *part_ml;               // [n_kv][n_split][rows][2]
-    float *gpart_o;               // [n_kv][kMaxGroups][rows][D]
-    float *gpart_ml;              // [n_kv][kMaxGroups][rows][2]
-    uint32_t *counters;           // [n_kv][kCounterWords]
     int64_t L;                    // cache row stride (positions)
     int32_t M, n_q, n_kv, qpg, rows, P, n_split, blocks_per_split, n_blocks;
     float scale_log2;             // log2(e) / sqrt(D)
@@ -92,7 +92,6 @@ __global__ __launch_bounds__(kAttnThreads) void decode_attention_kernel(AttnArgs
     uint8_t *k_lds = lds;                                  // [64][kKStride]
     uint8_t *vt_lds = k_lds + kBlock * kKStride;           // [D][kVtStride]
     uint8_t *p_lds = vt_lds + D * kVtStride;               // [4 row tiles][hi 16, lo 16][kPStride]
-    __shared__ float s_merge[64][2];
     __shared__ float s_red[4][16];                         // per wave: its part of a row-tile reduction
 
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
@@ -300,118 +299,111 @@ __global__ __launch_bounds__(kAttnThreads) void decode_attention_kernel(AttnArgs
         for (int j = 0; j < 4; ++j) {
             const int r = rt * 16 + 4 * lq + j;
             if (r >= rows) continue;
+            if (a.n_split == 1) {   // the head's only split: its result is the output
+                const float inv = 1.0f / l[j];
+                const int i = r / qpg, jj = r % qpg;
+                uint16_t *dst = a.o + ((int64_t)i * a.n_q + g * qpg + jj) * D;
 #pragma unroll
-            for (int c = 0; c < kCtW; ++c) store_shared(a.part_o + (base + r) * D + 16 * (sw + c * WPR) + lr, o[c][j]);
+                for (int c = 0; c < kCtW; ++c) dst[16 * (sw + c * WPR) + lr] = (uint16_t)f32_to_bf16_bits(o[c][j] * inv);
+                continue;
+            }
+#pragma unroll
+            for (int c = 0; c < kCtW; ++c) a.part_o[(base + r) * D + 16 * (sw + c * WPR) + lr] = o[c][j];
             if (lr == 0 && sw == 0) {
-                store_shared(a.part_ml + (base + r) * 2, m[j]);
-                store_shared(a.part_ml + (base + r) * 2 + 1, l[j]);
+                a.part_ml[(base + r) * 2] = m[j];
+                a.part_ml[(base + r) * 2 + 1] = l[j];
             }
         }
     }
-    // Merge in two levels: the last split of each group of kGroupSplits to
-    // count in merges the group into an unnormalised group partial, and the
-    // last group of the head to count in merges the groups into the output.
-    // A merge stages the partials' (m, l) in LDS (over the staging area, free
-    // now), turns them into weights 2^(m_t - M) (over L for the output), and
-    // sums the o's with the loads of four outputs times eight partials in
-    // flight per thread.
-    auto merge = [&](const float *ml, const float *op, int n, bool final, float *dml, float *dop) {
-        float *wl = reinterpret_cast<float *>(k_lds);   // [n][rows]: m, then the weight
-        float *ll = wl + n * rows;                      // [n][rows]: l
-        for (int idx = tid; idx < n * rows; idx += kAttnThreads) {
-            wl[idx] = load_shared(ml + (int64_t)idx * 2);
-            ll[idx] = load_shared(ml + (int64_t)idx * 2 + 1);
-        }
-        __syncthreads();
-        for (int r = tid; r < rows; r += kAttnThreads) {
-            float mx = -INFINITY;
-            for (int t = 0; t < n; ++t) mx = fmaxf(mx, wl[t * rows + r]);
-            float den = 0.0f;
-            for (int t = 0; t < n; ++t) {
-                const float mt = wl[t * rows + r];
-                if (mt != -INFINITY) den += ll[t * rows + r] * exp2f(mt - mx);
-            }
-            s_merge[r][0] = mx;
-            s_merge[r][1] = den;
-        }
-        __syncthreads();
-        for (int idx = tid; idx < n * rows; idx += kAttnThreads) {
-            const int r = idx % rows;
-            const float mt = wl[idx];
-            wl[idx] = mt == -INFINITY ? 0.0f : exp2f(mt - s_merge[r][0]) / (final ? s_merge[r][1] : 1.0f);
-        }
-        __syncthreads();
-        constexpr int kOut = 4;
-        for (int i0 = tid; i0 < rows * D; i0 += kOut * kAttnThreads) {
-            float acc[kOut];
-#pragma unroll
-            for (int q = 0; q < kOut; ++q) acc[q] = 0.0f;
-            for (int t0 = 0; t0 < n; t0 += 8) {
-                float pv[kOut][8];
-#pragma unroll
-                for (int q = 0; q < kOut; ++q) {
-                    const int idx = i0 + q * kAttnThreads;
-                    const int r = idx / D, d = idx % D;
-#pragma unroll
-                    for (int u = 0; u < 8; ++u)
-                        pv[q][u] = idx < rows * D && t0 + u < n ? load_shared(op + ((int64_t)(t0 + u) * rows + r) * D + d) : 0.0f;
-                }
-#pragma unroll
-                for (int q = 0; q < kOut; ++q) {
-                    const int idx = i0 + q * kAttnThreads;
-                    const int r = idx / D;
-#pragma unroll
-                    for (int u = 0; u < 8; ++u)
-                        if (idx < rows * D && t0 + u < n) acc[q] = fmaf(pv[q][u], wl[(t0 + u) * rows + r], acc[q]);
-                }
-            }
-#pragma unroll
-            for (int q = 0; q < kOut; ++q) {
-                const int idx = i0 + q * kAttnThreads;
-                if (idx >= rows * D) continue;
-                const int r = idx / D, d = idx % D;
-                if (final) {
-                    const int i = r / qpg, j = r % qpg;
-                    a.o[((int64_t)i * a.n_q + g * qpg + j) * D + d] = (uint16_t)f32_to_bf16_bits(acc[q]);
-                } else {
-                    store_shared(dop + (int64_t)r * D + d, acc[q]);
-                }
-            }
-        }
-        if (!final)
-            for (int r = tid; r < rows; r += kAttnThreads) {
-                store_shared(dml + (int64_t)r * 2, s_merge[r][0]);
-                store_shared(dml + (int64_t)r * 2 + 1, s_merge[r][1]);
-            }
-        __syncthreads();
-    };
+}
 
-    __shared__ uint32_t s_last;
-    uint32_t *cnt = a.counters + (int64_t)g * kCounterWords;
-    const int grp = s / kGroupSplits, n_groups = (a.n_split + kGroupSplits - 1) / kGroupSplits;
-    const int g0 = grp * kGroupSplits, gn = min(a.n_split - g0, kGroupSplits);
-    wait_memory();
-    __syncthreads();
-    if (tid == 0) s_last = counter_add(cnt + 1 + grp, 1u) == (uint32_t)(gn - 1) ? 1u : 0u;
-    __syncthreads();
-    if (!s_last) return;
-    if (tid == 0) store_shared(cnt + 1 + grp, 0u);   // ready for the next launch
-    if (n_groups == 1) {   // one group: its merge is the output
-        merge(a.part_ml + (int64_t)g * a.n_split * rows * 2, a.part_o + (int64_t)g * a.n_split * rows * D, gn, true,
-              nullptr, nullptr);
-        return;
+struct MergeArgs {
+    const float *part_o, *part_ml;   // as in AttnArgs
+    uint16_t *o;
+    int32_t n_split, rows, qpg, n_q, tpq;
+};
+
+// Merge of the splits of one head, wide: lanes t of a group of tpq
+// consecutive lanes sum splits t, t + tpq, ... (at most 8, so tpq * 8 >= the
+// split count) for four adjacent outputs (one 16-byte load each), and the
+// group adds its lanes' sums.  A workgroup covers
+// 256 / tpq such groups; it stages the weights 2^(m_s - M) / L of the rows
+// it touches (at most 16) in LDS first.
+template <int D>
+__global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(MergeArgs a) {
+    constexpr int kMaxRowsWg = kAttnThreads * 4 / 64;   // rows a workgroup touches, at most
+    __shared__ float w_s[kMaxSplits][kMaxRowsWg];
+    __shared__ float l_s[kMaxSplits][kMaxRowsWg];
+    __shared__ float red[kMaxRowsWg][2];
+    const int tid = threadIdx.x, g = blockIdx.y;
+    const int n = a.n_split, rows = a.rows, tpq = a.tpq;
+    const int groups = kAttnThreads / tpq;
+    const int64_t e_lo = (int64_t)blockIdx.x * groups * 4;
+    const int r_lo = (int)(e_lo / D);
+    const int r_hi = min(rows, (int)((e_lo + groups * 4 - 1) / D) + 1);
+    const int nr = r_hi - r_lo;
+    // the lane's partials (at most 8 splits: tpq * 8 >= n) go out first, so
+    // that their round trip overlaps the weights' one
+    const int64_t e0 = e_lo + (int64_t)(tid / tpq) * 4;   // the group's first output
+    const int t = tid % tpq;
+    const int r = (int)(e0 / D), d = (int)(e0 % D);
+    const bool real = r < rows;
+    f4 v[8];
+    {
+        const float *op = a.part_o + ((int64_t)g * n * rows + (real ? r : 0)) * D + d;
+        const int64_t stride = (int64_t)rows * D;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int s = t + u * tpq;
+            v[u] = real && s < n ? *reinterpret_cast<const f4 *>(op + s * stride) : f4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
     }
-    const int64_t gb = (int64_t)g * kMaxGroups + grp;
-    merge(a.part_ml + ((int64_t)g * a.n_split + g0) * rows * 2, a.part_o + ((int64_t)g * a.n_split + g0) * rows * D, gn,
-          false, a.gpart_ml + gb * rows * 2, a.gpart_o + gb * rows * D);
-    wait_memory();
+    const float *ml = a.part_ml + (int64_t)g * n * rows * 2;
+    for (int idx = tid; idx < n * nr; idx += kAttnThreads) {
+        const int s = idx / nr, rr = idx % nr;
+        w_s[s][rr] = ml[((int64_t)s * rows + r_lo + rr) * 2];
+        l_s[s][rr] = ml[((int64_t)s * rows + r_lo + rr) * 2 + 1];
+    }
     __syncthreads();
-    if (tid == 0) s_last = counter_add(cnt, 1u) == (uint32_t)(n_groups - 1) ? 1u : 0u;
+    {   // a wave per row: its lanes stride over the splits
+        const int lane = tid & 63, wave = tid >> 6;
+        for (int rr = wave; rr < nr; rr += kAttnThreads / 64) {
+            float mx = -INFINITY;
+            for (int s = lane; s < n; s += 64) mx = fmaxf(mx, w_s[s][rr]);
+            for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            float den = 0.0f;
+            for (int s = lane; s < n; s += 64)
+                if (w_s[s][rr] != -INFINITY) den += l_s[s][rr] * exp2f(w_s[s][rr] - mx);
+            for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+            if (lane == 0) {
+                red[rr][0] = mx;
+                red[rr][1] = den;
+            }
+        }
+    }
     __syncthreads();
-    if (!s_last) return;
-    if (tid == 0) store_shared(cnt, 0u);
-    merge(a.gpart_ml + (int64_t)g * kMaxGroups * rows * 2, a.gpart_o + (int64_t)g * kMaxGroups * rows * D, n_groups,
-          true, nullptr, nullptr);
+    for (int idx = tid; idx < n * nr; idx += kAttnThreads) {
+        const int s = idx / nr, rr = idx % nr;
+        const float mt = w_s[s][rr];
+        w_s[s][rr] = mt == -INFINITY ? 0.0f : exp2f(mt - red[rr][0]) / red[rr][1];
+    }
+    __syncthreads();
+    f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (real) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int s = t + u * tpq;
+            if (s < n) acc += w_s[s][r - r_lo] * v[u];
+        }
+    }
+    for (int off = 1; off < tpq; off <<= 1)   // the group's lanes are consecutive
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
+    if (!real || t != 0) return;
+    const int i = r / a.qpg, j = r % a.qpg;
+    uint32_t *dst = reinterpret_cast<uint32_t *>(a.o + ((int64_t)i * a.n_q + g * a.qpg + j) * D + d);
+    dst[0] = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+    dst[1] = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
 }
 
 }  // namespace
@@ -421,15 +413,13 @@ AttnPlan plan_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t
     const int64_t used = P + M;
     pl.n_blocks = (used + kBlock - 1) / kBlock;
     pl.rows = (n_q / n_kv) * M;
-    // keys, transposed values, the row tiles' probabilities; a merge reuses the
-    // area for two floats per merged partial and row
+    // keys, transposed values, the row tiles' probabilities
     const int64_t row_tiles = (pl.rows + 15) / 16;
-    pl.lds_bytes = (int)std::max<int64_t>(kBlock * (D * 2 + 16) + D * (kBlock * 2 + 16) + row_tiles * 32 * (kBlock * 2 + 16),
-                                          std::max<int64_t>(kGroupSplits, kMaxGroups) * pl.rows * 8);
+    pl.lds_bytes = (int)(kBlock * (D * 2 + 16) + D * (kBlock * 2 + 16) + row_tiles * 32 * (kBlock * 2 + 16));
     // a workgroup per CU, two where their LDS fits (one hides the other's
     // load latency), and at least kMinBlocks blocks each (a split's fixed
     // cost -- the query load, the first fetch, publishing -- is latency)
-    constexpr int64_t kMinBlocks = 4;
+    constexpr int64_t kMinBlocks = MBQ_ATTN_MIN_BLOCKS;
     // (the one-tile form's registers also allow two waves per SIMD)
     const int64_t per_cu = row_tiles == 1 && pl.lds_bytes <= 80 * 1024 ? 2 : 1;
     const int64_t target = std::max<int64_t>(
@@ -437,19 +427,16 @@ AttnPlan plan_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t
     const int64_t want = std::min<int64_t>(pl.n_blocks, target);
     pl.blocks_per_split = (pl.n_blocks + want - 1) / want;
     pl.n_split = (pl.n_blocks + pl.blocks_per_split - 1) / pl.blocks_per_split;
-    // [counters][m, l per split and row][o per split and row]: the counters
-    // come first so that every call on one workspace finds them in one place
-    const int64_t part_o = n_kv * pl.n_split * pl.rows * D * 4;
+    // merge: lanes per group of four outputs, so that a lane sums at most 8 splits
+    pl.merge_tpq = 1;
+    while (pl.merge_tpq < 16 && pl.merge_tpq * 8 < pl.n_split) pl.merge_tpq *= 2;
+    // [m, l per split and row][o per split and row]
     const int64_t part_ml = n_kv * pl.n_split * pl.rows * 2 * 4;
-    const int64_t gpart_o = n_kv * kMaxGroups * pl.rows * D * 4;
-    const int64_t gpart_ml = n_kv * kMaxGroups * pl.rows * 2 * 4;
+    const int64_t part_o = n_kv * pl.n_split * pl.rows * D * 4;
     auto up = [](int64_t v) { return (v + 255) / 256 * 256; };
-    pl.off_cnt = 0;
-    pl.off_ml = up(n_kv * kCounterWords * 4);
-    pl.off_o = pl.off_ml + up(part_ml);
-    pl.off_gml = pl.off_o + up(part_o);
-    pl.off_go = pl.off_gml + up(gpart_ml);
-    pl.ws_bytes = pl.off_go + up(gpart_o);
+    pl.off_ml = 0;
+    pl.off_o = up(part_ml);
+    pl.ws_bytes = pl.off_o + up(part_o);
     return pl;
 }
 
@@ -463,9 +450,6 @@ hipError_t launch_attention(const AttnPlan &pl, int64_t M, int64_t n_q, int64_t 
     a.o = (uint16_t *)o;
     a.part_o = (float *)((char *)ws + pl.off_o);
     a.part_ml = (float *)((char *)ws + pl.off_ml);
-    a.gpart_ml = (float *)((char *)ws + pl.off_gml);
-    a.gpart_o = (float *)((char *)ws + pl.off_go);
-    a.counters = (uint32_t *)((char *)ws + pl.off_cnt);
     a.L = L;
     a.M = (int32_t)M;
     a.n_q = (int32_t)n_q;
@@ -485,8 +469,25 @@ hipError_t launch_attention(const AttnPlan &pl, int64_t M, int64_t n_q, int64_t 
     const void *fn = D == 64 ? MBQ_ATTN(64) : D == 128 ? MBQ_ATTN(128) : MBQ_ATTN(256);
 #undef MBQ_ATTN
     void *args[] = {(void *)&a};
-    return hipLaunchKernel(fn, dim3((unsigned)pl.n_split, (unsigned)n_kv), dim3(kAttnThreads), args,
-                           (size_t)pl.lds_bytes, st);
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)pl.n_split, (unsigned)n_kv), dim3(kAttnThreads), args,
+                                   (size_t)pl.lds_bytes, st);
+    if (e != hipSuccess || pl.n_split == 1) return e;
+    MergeArgs ma;
+    ma.part_o = a.part_o;
+    ma.part_ml = a.part_ml;
+    ma.o = a.o;
+    ma.n_split = a.n_split;
+    ma.rows = a.rows;
+    ma.qpg = a.qpg;
+    ma.n_q = a.n_q;
+    ma.tpq = (int32_t)pl.merge_tpq;
+    const int64_t per_wg = kAttnThreads / pl.merge_tpq * 4;   // outputs per workgroup
+    const unsigned gx = (unsigned)((pl.rows * D + per_wg - 1) / per_wg);
+    const void *mf = D == 64 ? reinterpret_cast<const void *>(&attn_merge_kernel<64>)
+                     : D == 128 ? reinterpret_cast<const void *>(&attn_merge_kernel<128>)
+                                : reinterpret_cast<const void *>(&attn_merge_kernel<256>);
+    void *margs[] = {(void *)&ma};
+    return hipLaunchKernel(mf, dim3(gx, (unsigned)n_kv), dim3(kAttnThreads), margs, 0, st);
 }
 
 }  // namespace mbq

@@ -53,7 +53,8 @@ int relayout_inplace(int bits, int64_t N, int64_t K, void *buf, int n_cu, hipStr
 // Split-prefix decode attention (attn.hip).
 struct AttnPlan {
     int64_t n_blocks = 0, blocks_per_split = 0, n_split = 0, rows = 0;
-    int64_t off_cnt = 0, off_ml = 0, off_o = 0, off_gml = 0, off_go = 0, ws_bytes = 0;
+    int64_t merge_tpq = 1;   // merge lanes per four outputs
+    int64_t off_ml = 0, off_o = 0, ws_bytes = 0;
     int lds_bytes = 0;
 };
 AttnPlan plan_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P, int n_cu);

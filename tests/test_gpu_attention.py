@@ -56,11 +56,11 @@ def test_decode_attention_causal_rows_and_heads_exactly():
 
 
 def test_decode_attention_workspace_reused():
-    """Two calls on one workspace (the counters reset themselves), different P."""
+    """Calls of different P on one workspace, which starts out as garbage."""
     import torch
     M, n_q, n_kv, D = 4, 8, 2, 128
     need = max(mbq.attention_workspace_bytes(M, n_q, n_kv, D, P) for P in (3000, 10))
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
     for P in (3000, 10, 3000):
         L = P + M
         q, k, v = _inputs(M, n_q, n_kv, D, L, seed=P)
