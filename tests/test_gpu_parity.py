@@ -418,6 +418,17 @@ def test_layer_sequence_fused_deterministic_and_rerunnable(bits):
         assert_close_bf16(outs[0][o["out_buf"]], unf[o["out_buf"]], o["name"])
 
 
+@pytest.mark.parametrize("shapes,M,dataflow", [("27b", 8, "plain"), ("27b", 3, "plain"), ("9b", 4, "swiglu")])
+def test_layer_sequence_shared_gathers_reproducible(shapes, M, dataflow):
+    """Where a finalising workgroup's waves share a row block's gather (the o
+    and down blocks of these layers, gate/up pairs in the SwiGLU walk), the
+    parts are added in a fixed order: two runs agree bitwise."""
+    fn = synth.layer_shapes_27b if shapes == "27b" else synth.layer_shapes_9b
+    _, _, outs, _ = _run_sequence(4, fn, 1, M, distinct=True, runs=2, dataflow=dataflow)
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("M", [1, 3])
 def test_layer_sequence_bench_configuration(M):
     """The 36-layer 9B-shaped walk with reused buffers, as the benchmark runs it.
