@@ -6,7 +6,8 @@
 // a stream over the packed weights.
 //
 // Work split: each wave owns one row block (64 rows, one per lane) and a
-// contiguous range of its k groups (a "split").  For every 64x128 tile the
+// contiguous range of its k groups (a "split"), the next tile loading while
+// the current one is summed.  For every 64x128 tile the
 // lane unpacks its 128 codes to int8, takes int8 dot products against the
 // activation (wave-uniform, so it is read through the scalar unit and shared
 // by all 64 rows), sums them exactly in int32, and adds the group's
@@ -25,6 +26,8 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kTargetWaves = 2048;   // about 8 waves per CU on 256 CUs
+constexpr int kTilesPerWave = 4;     // a split's tiles, at least (when the matrix has enough)
+constexpr int kMaxSplits = 16;       // a row block's partials, at most
 
 template <int BITS, int M>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void linear_kernel(
@@ -111,16 +114,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void linear_kernel(
 #pragma unroll
     for (int m = 0; m < M; ++m) tot[m] = 0.0f;
     const float *rbp = partials + ((int64_t)rb * splits * M) * 64;
-    // issue eight partial loads at a time, then add them in split order
-    for (int p0 = 0; p0 < splits; p0 += 8) {
-        float v[8][M];
+    // issue 32 / M partial loads at a time, then add them in split order
+    constexpr int B = 32 / M;
+    for (int p0 = 0; p0 < splits; p0 += B) {
+        float v[B][M];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < B; ++u)
 #pragma unroll
             for (int m = 0; m < M; ++m)
                 v[u][m] = p0 + u < splits ? load_shared(rbp + ((p0 + u) * M + m) * 64 + r) : 0.0f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < B; ++u)
 #pragma unroll
             for (int m = 0; m < M; ++m) tot[m] += v[u][m];
     }
@@ -217,7 +221,16 @@ LinearPlan plan_linear(int bits, int64_t M, int64_t N, int64_t K) {
     LinearPlan p;
     p.n_rb = row_blocks(N);
     p.groups = K / kGroup;
-    int64_t sp = (kTargetWaves + p.n_rb - 1) / p.n_rb;
+    // enough waves to fill the chip, but kTilesPerWave tiles each where the
+    // matrix has them and at most kMaxSplits splits per row block: a split
+    // pays the load latency once, and the last arriver gathers every partial
+    // of its row block, so a one-tile split (4096 x 4096 at 2048 waves) or a
+    // 26-way split (5120 x 17408) costs more than it spreads.
+    int64_t waves = p.n_rb * p.groups / kTilesPerWave;
+    if (waves > kTargetWaves) waves = kTargetWaves;
+    if (waves < p.n_rb) waves = p.n_rb;
+    int64_t sp = (waves + p.n_rb - 1) / p.n_rb;
+    if (sp > kMaxSplits) sp = kMaxSplits;
     if (sp > p.groups) sp = p.groups;
     if (sp < 1) sp = 1;
     p.splits = sp;
