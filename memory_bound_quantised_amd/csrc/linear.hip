@@ -28,6 +28,9 @@ constexpr int kWavesPerBlock = 4;
 constexpr int kTargetWaves = 2048;   // about 8 waves per CU on 256 CUs
 constexpr int kTilesPerWave = 4;     // a split's tiles, at least (when the matrix has enough)
 constexpr int kMaxSplits = 16;       // a row block's partials, at most
+#ifndef MBQ_LIN_MFMA_MIN_M
+#define MBQ_LIN_MFMA_MIN_M 1
+#endif
 
 template <int BITS, int M>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void linear_kernel(
@@ -46,64 +49,122 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void linear_kernel(
     const int g1 = (int)(((int64_t)(sp + 1) * G) / splits);
 
     const uint8_t *tiles = packed + (int64_t)rb * G * L::kTileBytes;
-    const int *qa = reinterpret_cast<const int *>(q);
-    const int kdw = K >> 2;  // dwords per activation row
 
-    float facc[4][M];
+    // Matrix cores from MBQ_LIN_MFMA_MIN_M rows on: lane l then holds the sums
+    // of weight rows 4 (l & 15) + i for activation rows 4 (l >> 4) + j (rows
+    // past M are computed from row 0 and dropped); with v_dot4 every lane
+    // holds all M activation rows of its k slice.
+    constexpr bool kMfma = M >= MBQ_LIN_MFMA_MIN_M;
+    constexpr int AR = kMfma ? (M > 4 ? 4 : M) : M;
+    float facc[4][AR];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int m = 0; m < M; ++m) facc[i][m] = 0.0f;
+        for (int m = 0; m < AR; ++m) facc[i][m] = 0.0f;
     const int slice = lane >> 4;   // this lane's k slice
-
     v4i wc[L::kSlabs];
     v2u sc = {0u, 0u};
-    if (g0 < g1) load_tile<BITS>(tiles + (int64_t)g0 * L::kTileBytes, lane, wc, sc);
-    for (int g = g0; g < g1; ++g) {
-        v4i wn[L::kSlabs];
-        v2u sn = {0u, 0u};
-        if (g + 1 < g1) load_tile<BITS>(tiles + (int64_t)(g + 1) * L::kTileBytes, lane, wn, sn);
-        int acc[4][M];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int m = 0; m < M; ++m) acc[i][m] = 0;
-        const int *qg = qa + g * 32 + slice * 8;
-        dot_tile<BITS, M>(wc, [&](int m, int d) { return qg[m * kdw + d]; }, acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float S = row_scale(sc, i);
-#pragma unroll
-            for (int m = 0; m < M; ++m) facc[i][m] = fmaf((float)acc[i][m], S, facc[i][m]);
+    if constexpr (kMfma) {
+        const int am = (lane & 15) < M ? (lane & 15) : 0;
+        const v4i *qrow = reinterpret_cast<const v4i *>(q + (int64_t)am * K + slice * 32);   // 8 v4i per group
+        v4i ac0 = v4i{0, 0, 0, 0}, ac1 = v4i{0, 0, 0, 0};
+        if (g0 < g1) {
+            load_tile<BITS>(tiles + (int64_t)g0 * L::kTileBytes, lane, wc, sc);
+            ac0 = *gptr(qrow + g0 * 8);
+            ac1 = *gptr(qrow + g0 * 8 + 1);
         }
+        for (int g = g0; g < g1; ++g) {
+            v4i wn[L::kSlabs];
+            v2u sn = {0u, 0u};
+            v4i an0 = v4i{0, 0, 0, 0}, an1 = v4i{0, 0, 0, 0};
+            if (g + 1 < g1) {
+                load_tile<BITS>(tiles + (int64_t)(g + 1) * L::kTileBytes, lane, wn, sn);
+                an0 = *gptr(qrow + (g + 1) * 8);
+                an1 = *gptr(qrow + (g + 1) * 8 + 1);
+            }
+            v4i acc[4];
+            mfma_tile_regs<BITS>(wc, ac0, ac1, acc);
 #pragma unroll
-        for (int j = 0; j < L::kSlabs; ++j) wc[j] = wn[j];
-        sc = sn;
+            for (int i = 0; i < 4; ++i) {
+                const float S = row_scale(sc, i);
+#pragma unroll
+                for (int j = 0; j < AR; ++j) facc[i][j] = fmaf((float)acc[i][j], S, facc[i][j]);
+            }
+#pragma unroll
+            for (int j = 0; j < L::kSlabs; ++j) wc[j] = wn[j];
+            sc = sn;
+            ac0 = an0;
+            ac1 = an1;
+        }
+    } else {
+        const int *qa = reinterpret_cast<const int *>(q);
+        const int kdw = K >> 2;  // dwords per activation row
+        if (g0 < g1) load_tile<BITS>(tiles + (int64_t)g0 * L::kTileBytes, lane, wc, sc);
+        for (int g = g0; g < g1; ++g) {
+            v4i wn[L::kSlabs];
+            v2u sn = {0u, 0u};
+            if (g + 1 < g1) load_tile<BITS>(tiles + (int64_t)(g + 1) * L::kTileBytes, lane, wn, sn);
+            int acc[4][M];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int m = 0; m < M; ++m) acc[i][m] = 0;
+            const int *qg = qa + g * 32 + slice * 8;
+            dot_tile<BITS, M>(wc, [&](int m, int d) { return qg[m * kdw + d]; }, acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float S = row_scale(sc, i);
+#pragma unroll
+                for (int m = 0; m < M; ++m) facc[i][m] = fmaf((float)acc[i][m], S, facc[i][m]);
+            }
+#pragma unroll
+            for (int j = 0; j < L::kSlabs; ++j) wc[j] = wn[j];
+            sc = sn;
+        }
     }
-    // sum the four k slices: lane l ends with row r = slice_row(l)
-    float frow[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        float f[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = facc[i][m];
-        frow[m] = slice_reduce(f);
-    }
-
     const float unscale = 1.0f / (float)(1 << L::kAccShift);   // exact power of two
+    // the combine below works in the dot form: lane l gathers row slice_row(l), every m
     const int r = slice_row(lane);
     const int n = rb * 64 + r;
-    if (splits == 1) {
-        if (n < N) {
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-                y[m * y_stride + n] = (uint16_t)f32_to_bf16_bits(s[m] * (frow[m] * unscale));
-        }
-        return;
-    }
     float *part = partials + ((int64_t)item * M) * 64;
+    if constexpr (kMfma) {
 #pragma unroll
-    for (int m = 0; m < M; ++m) store_shared(part + m * 64 + r, frow[m]);
+        for (int j = 0; j < AR; ++j) {
+            const int m = 4 * (lane >> 4) + j;
+            if (m >= M) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 4 * (lane & 15) + i;
+                if (splits == 1) {
+                    if (rb * 64 + rr < N)
+                        y[m * y_stride + rb * 64 + rr] = (uint16_t)f32_to_bf16_bits(s[m] * (facc[i][j] * unscale));
+                } else {
+                    store_shared(part + m * 64 + rr, facc[i][j]);
+                }
+            }
+        }
+        if (splits == 1) return;
+    } else {
+        // sum the four k slices: lane l ends with row r = slice_row(l)
+        float frow[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float f[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f[i] = facc[i][m];
+            frow[m] = slice_reduce(f);
+        }
+        if (splits == 1) {
+            if (n < N) {
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    y[m * y_stride + n] = (uint16_t)f32_to_bf16_bits(s[m] * (frow[m] * unscale));
+            }
+            return;
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) store_shared(part + m * 64 + r, frow[m]);
+    }
     wait_memory();
     unsigned prev = 0;
     if (lane == 0) prev = counter_add(&counters[rb], 1u);

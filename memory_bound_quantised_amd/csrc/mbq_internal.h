@@ -269,6 +269,17 @@ __device__ __forceinline__ void dot_tile(const v4i (&w)[Layout<BITS>::kSlabs], A
 }
 
 // The lane's slabs and its four rows' fp16 scales (packed in two dwords).
+// The same product with the lane's activation slice already in registers.
+template <int BITS>
+__device__ __forceinline__ void mfma_tile_regs(const v4i (&w)[Layout<BITS>::kSlabs], v4i a0, v4i a1,
+                                               v4i (&acc)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const v4i z = {0, 0, 0, 0};
+        acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, unpack_half<BITS>(w, i, 0), z, 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, unpack_half<BITS>(w, i, 1), acc[i], 0, 0, 0);
+    }
+}
 template <int BITS>
 __device__ __forceinline__ void load_tile(const uint8_t *tile, int lane, v4i (&w)[Layout<BITS>::kSlabs],
                                           v2u &scales) {
