@@ -78,7 +78,7 @@ __device__ __forceinline__ float row16_sum(float v) {
 // WPR: waves per 16-row query tile (4, 2 or 1 for up to 16, 32 or 64 rows);
 // the waves of a tile split its score position tiles and output column tiles.
 template <int D, int WPR>
-__global__ __launch_bounds__(kAttnThreads) void decode_attention_kernel(AttnArgs a) {
+__device__ __forceinline__ void attention_split(const AttnArgs &a) {
     constexpr int kKStride = D * 2 + 16;          // LDS bytes per key row
     constexpr int kVtStride = kBlock * 2 + 16;    // LDS bytes per transposed value row (one column)
     constexpr int kPStride = kBlock * 2 + 16;     // LDS bytes per probability row
@@ -317,6 +317,18 @@ __global__ __launch_bounds__(kAttnThreads) void decode_attention_kernel(AttnArgs
     }
 }
 
+template <int D, int WPR>
+__global__ __launch_bounds__(kAttnThreads) void decode_attention_kernel(AttnArgs a) {
+    attention_split<D, WPR>(a);
+}
+// The same with at most 256 registers, so that two workgroups fit on a CU
+// (two waves per SIMD): the form for two row tiles, whose LDS allows two.
+template <int D, int WPR>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_attention_kernel_x2(
+    AttnArgs a) {
+    attention_split<D, WPR>(a);
+}
+
 struct MergeArgs {
     const float *part_o, *part_ml;   // as in AttnArgs
     uint16_t *o;
@@ -420,8 +432,10 @@ AttnPlan plan_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t
     // load latency), and at least kMinBlocks blocks each (a split's fixed
     // cost -- the query load, the first fetch, publishing -- is latency)
     constexpr int64_t kMinBlocks = MBQ_ATTN_MIN_BLOCKS;
-    // (the one-tile form's registers also allow two waves per SIMD)
-    const int64_t per_cu = row_tiles == 1 && pl.lds_bytes <= 80 * 1024 ? 2 : 1;
+    // (the one-tile form's registers allow two waves per SIMD; the two-tile
+    // form is compiled for it)
+    const int64_t per_cu = row_tiles <= 2 && pl.lds_bytes <= 80 * 1024 ? 2 : 1;
+    pl.two_per_cu = per_cu == 2;
     const int64_t target = std::max<int64_t>(
         1, std::min<int64_t>({kMaxSplits, per_cu * n_cu / n_kv, (pl.n_blocks + kMinBlocks - 1) / kMinBlocks}));
     const int64_t want = std::min<int64_t>(pl.n_blocks, target);
@@ -462,9 +476,10 @@ hipError_t launch_attention(const AttnPlan &pl, int64_t M, int64_t n_q, int64_t 
     a.n_blocks = (int32_t)pl.n_blocks;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const int wpr = pl.rows <= 16 ? 4 : pl.rows <= 32 ? 2 : 1;
-#define MBQ_ATTN(DD) \
-    (wpr == 4 ? reinterpret_cast<const void *>(&decode_attention_kernel<DD, 4>)   \
-     : wpr == 2 ? reinterpret_cast<const void *>(&decode_attention_kernel<DD, 2>) \
+#define MBQ_ATTN(DD)                                                                              \
+    (wpr == 4   ? reinterpret_cast<const void *>(&decode_attention_kernel<DD, 4>)                  \
+     : wpr == 2 ? (pl.two_per_cu ? reinterpret_cast<const void *>(&decode_attention_kernel_x2<DD, 2>) \
+                                 : reinterpret_cast<const void *>(&decode_attention_kernel<DD, 2>))  \
                 : reinterpret_cast<const void *>(&decode_attention_kernel<DD, 1>))
     const void *fn = D == 64 ? MBQ_ATTN(64) : D == 128 ? MBQ_ATTN(128) : MBQ_ATTN(256);
 #undef MBQ_ATTN
