@@ -67,10 +67,10 @@ def test_decode_attention_workspace_reused():
         assert_close_bf16(_run(q, k, v, P, ws=ws), oracle.decode_attention(q, k, v, P), f"P={P}")
 
 
-@pytest.mark.parametrize("M", [1, 8])
+@pytest.mark.parametrize("M", [1, 4, 8])
 def test_decode_attention_27b_shape(M):
     """The 27B-shaped attention layer: 32 query heads, 4 key/value heads of 256,
-    a 32768-token prefix."""
+    a 32768-token prefix (M = 4: two row tiles, two workgroups per CU)."""
     n_q, n_kv, D, P = 32, 4, 256, 32768
     L = P + M
     q, k, v = _inputs(M, n_q, n_kv, D, L, seed=77 + M)
