@@ -341,6 +341,8 @@ struct MergeArgs {
 // group adds its lanes' sums.  A workgroup covers
 // 256 / tpq such groups; it stages the weights 2^(m_s - M) / L of the rows
 // it touches (at most 16) in LDS first.
+// a lane sums at most 8 splits and a group has at most 16 lanes
+static_assert(kMaxSplits <= 16 * 8, "the merge covers every split");
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(MergeArgs a) {
     constexpr int kMaxRowsWg = kAttnThreads * 4 / 64;   // rows a workgroup touches, at most
