@@ -14,7 +14,16 @@ constexpr int kSeqThreads = 64 * kSeqWaves;
 // and publish their outputs; the others, once their partials are out, start
 // loading the next phase's weights at once, which keeps the memory busy while
 // the finalisers (whose memory queues are then empty) run the phase hand-over.
-__host__ __device__ inline bool is_final_wg(int wg, int grid) { return grid == 1 || (wg & 1) != 0; }
+// The dispatcher deals workgroups to the 8 XCDs in turn, so the odd
+// workgroups fill XCDs 1, 3, 5 and 7, and workgroups 3 mod 4 fill XCDs 3 and
+// 7: the hand-over's requests then cross XCDs with no weight loads queued.
+// Up to M = 3 a quarter of the workgroups finalise (their gathers are short),
+// from M = 4 on half of them, and always half in walks with SwiGLU pairs
+// (a pair is two row blocks: a quarter of the grid would take some in turn).
+__host__ __device__ inline bool is_final_wg(int wg, int grid, int M, bool full) {
+    if (grid == 1) return true;
+    return M <= 3 && !full && grid >= 8 ? (wg & 3) == 3 : (wg & 1) != 0;
+}
 constexpr int kChunkGroups = 8;                // k groups per k chunk (1024 k)
 constexpr int kCounterStride = 32;             // u32 words between phase counters (one 128-B line each)
 constexpr int kStatReplicas = 8;               // copies of the stats records, one per XCD

@@ -875,7 +875,7 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const SeqPlan *__restr
     L.part_stride = cload(&P->part_stride);
     L.meta_off = M * L.qs + kSeqWaves * L.slots * M * 64 * 4;
     L.meta_bytes = ((int)sizeof(SeqPhase) + L.blk_bytes + 15) & ~15;
-    const bool finaliser = is_final_wg(wg, L.grid);
+    const bool finaliser = is_final_wg(wg, L.grid, M, X);
 
     {   // metadata of the first phase
         uint32_t pre[kMetaIters];

@@ -38,10 +38,10 @@ struct PhaseGeom {
     }
     // Cut the T tiles into W = min(T, waves) contiguous ranges, the waves of
     // non-finalising workgroups weighted by w_other, every range non-empty.
-    void cut(int waves, int grid, double w_other) {
+    void cut(int waves, int grid, int M, bool full, double w_other) {
         W = T < waves ? T : waves;
         std::vector<double> cum(W + 1, 0.0);
-        for (int w = 0; w < W; ++w) cum[w + 1] = cum[w] + (is_final_wg(w / kSeqWaves, grid) ? 1.0 : w_other);
+        for (int w = 0; w < W; ++w) cum[w + 1] = cum[w] + (is_final_wg(w / kSeqWaves, grid, M, full) ? 1.0 : w_other);
         st.assign(W + 1, 0);
         for (int w = 1; w < W; ++w) {
             int v = (int)((double)T * cum[w] / cum[W] + 0.5);
@@ -213,7 +213,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
         const int64_t T = R * g.G;
         if (T >= ((int64_t)1 << 31)) return MBQ_ERR_SHAPE;
         g.T = (int)T;
-        g.cut(waves, grid, other_weight(M));
+        g.cut(waves, grid, (int)M, full, other_weight(M));
         for (int w = 0; w < g.W; ++w) {
             const int t0 = g.start(w), t1 = g.start(w + 1) - 1;
             const int sc = g.segment(t1) - g.segment(t0) + 1;
@@ -321,7 +321,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
         {
             std::vector<int> fwg;
             for (int wg = 0; wg < grid; ++wg)
-                if (is_final_wg(wg, grid)) fwg.push_back(wg);
+                if (is_final_wg(wg, grid, (int)M, full)) fwg.push_back(wg);
             unit_fin[p].assign(units[p].size(), 0);
             for (size_t u = 0; u < units[p].size(); ++u) unit_fin[p][u] = fwg[u % fwg.size()];
         }
