@@ -20,9 +20,10 @@ constexpr int kSeqThreads = 64 * kSeqWaves;
 // Up to M = 3 a quarter of the workgroups finalise (their gathers are short),
 // from M = 4 on half of them, and always half in walks with SwiGLU pairs
 // (a pair is two row blocks: a quarter of the grid would take some in turn).
+__host__ __device__ inline bool quarter_finalise(int grid, int M, bool full) { return M <= 3 && !full && grid >= 8; }
 __host__ __device__ inline bool is_final_wg(int wg, int grid, int M, bool full) {
     if (grid == 1) return true;
-    return M <= 3 && !full && grid >= 8 ? (wg & 3) == 3 : (wg & 1) != 0;
+    return quarter_finalise(grid, M, full) ? (wg & 3) == 3 : (wg & 1) != 0;
 }
 constexpr int kChunkGroups = 8;                // k groups per k chunk (1024 k)
 constexpr int kCounterStride = 32;             // u32 words between phase counters (one 128-B line each)

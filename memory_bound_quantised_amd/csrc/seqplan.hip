@@ -54,21 +54,24 @@ struct PhaseGeom {
 };
 
 // Share of a phase's tiles given to a wave of a non-finalising workgroup,
-// relative to a finalising one.  A finaliser's hand-over work grows with M (it
-// gathers M words per contribution, 32 / M contributions per round trip), so
-// from M = 3 on the finalisers take a third of the tiles (2.0 cut 9B- and
-// 27B-shaped W4 walks by 4-11 % at M = 3..8; it costs 1-4 % at M = 1..2).
-// It also decides where the ranges end: at 2.0 most of those walks' ranges
-// are whole numbers of tiles per wave, which keeps a row block's
-// contributions (and the finaliser's round trips) few.  MBQ_SPLIT_WEIGHT
-// overrides it.
-double other_weight(int64_t M) {
+// relative to a finalising one.  It also decides where the ranges end, and so
+// how many contributions a row block gets (whole tiles per wave keep them
+// few); the values were measured on 9B- and 27B-shaped W4 walks.
+//   - A quarter of the grid finalising (plain walks up to M = 3): 3.0, so the
+//     finalisers stream a tenth of the tiles (2.6-3.8 % faster than 2.0 at
+//     M = 1..2; 2.5-3.5 are within 1 % of each other).
+//   - Half of the grid finalising: 1.0 below M = 3, 2.0 from M = 3 on, where
+//     a finaliser gathers M words per contribution (2.0 cut 4-11 % at M =
+//     3..8; 1.75 was worse than both 1.5 and 2.0).
+// MBQ_SPLIT_WEIGHT overrides it.
+double other_weight(int64_t M, bool quarter) {
     static const double env = [] {
         const char *e = getenv("MBQ_SPLIT_WEIGHT");
         const double v = e ? atof(e) : 0.0;
         return v > 0.05 && v < 20.0 ? v : 0.0;
     }();
     if (env > 0.0) return env;
+    if (quarter) return 3.0;
     return M >= 3 ? 2.0 : 1.0;
 }
 
@@ -213,7 +216,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
         const int64_t T = R * g.G;
         if (T >= ((int64_t)1 << 31)) return MBQ_ERR_SHAPE;
         g.T = (int)T;
-        g.cut(waves, grid, (int)M, full, other_weight(M));
+        g.cut(waves, grid, (int)M, full, other_weight(M, quarter_finalise(grid, (int)M, full)));
         for (int w = 0; w < g.W; ++w) {
             const int t0 = g.start(w), t1 = g.start(w + 1) - 1;
             const int sc = g.segment(t1) - g.segment(t0) + 1;
