@@ -35,7 +35,7 @@ namespace mbq {
 
 namespace {
 
-constexpr int kBlock = 64;        // positions per block
+constexpr int kBlock = 64;        // positions per block (32 for four row tiles)
 constexpr int kMaxSplits = 128;
 constexpr int kAttnThreads = 256;
 #ifndef MBQ_ATTN_MIN_BLOCKS
@@ -77,20 +77,25 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 // WPR: waves per 16-row query tile (4, 2 or 1 for up to 16, 32 or 64 rows);
 // the waves of a tile split its score position tiles and output column tiles.
-template <int D, int WPR>
+// BLK: positions per block, 64 or 32 (32 halves the staging LDS and the
+// load registers, so the one-wave-per-tile form fits two workgroups per CU).
+template <int D, int WPR, int BLK>
 __device__ __forceinline__ void attention_split(const AttnArgs &a) {
+    static_assert(BLK == 64 || BLK == 32, "block of 64 or 32 positions");
+    constexpr int kPt = BLK / 16;                 // position tiles per block
+    static_assert(WPR <= kPt, "a wave takes whole position tiles");
     constexpr int kKStride = D * 2 + 16;          // LDS bytes per key row
-    constexpr int kVtStride = kBlock * 2 + 16;    // LDS bytes per transposed value row (one column)
-    constexpr int kPStride = kBlock * 2 + 16;     // LDS bytes per probability row
+    constexpr int kVtStride = BLK * 2 + 16;       // LDS bytes per transposed value row (one column)
+    constexpr int kPStride = BLK * 2 + 16;        // LDS bytes per probability row
     constexpr int kChunks = D / 8;                // 16-byte pieces of a row
-    constexpr int kLoads = kBlock * kChunks / kAttnThreads;   // 16-byte loads per thread per tensor
+    constexpr int kLoads = BLK * kChunks / kAttnThreads;   // 16-byte loads per thread per tensor
     constexpr int kKs = D / 32;                   // k steps of the score product
     constexpr int kCt = D / 16;                   // column tiles of the output
-    constexpr int kPtW = 4 / WPR;                 // position tiles per wave
+    constexpr int kPtW = kPt / WPR;               // position tiles per wave
     constexpr int kCtW = kCt / WPR;               // column tiles per wave
     extern __shared__ __align__(16) uint8_t lds[];
-    uint8_t *k_lds = lds;                                  // [64][kKStride]
-    uint8_t *vt_lds = k_lds + kBlock * kKStride;           // [D][kVtStride]
+    uint8_t *k_lds = lds;                                  // [BLK][kKStride]
+    uint8_t *vt_lds = k_lds + BLK * kKStride;              // [D][kVtStride]
     uint8_t *p_lds = vt_lds + D * kVtStride;               // [4 row tiles][hi 16, lo 16][kPStride]
     __shared__ float s_red[4][16];                         // per wave: its part of a row-tile reduction
 
@@ -129,13 +134,16 @@ __device__ __forceinline__ void attention_split(const AttnArgs &a) {
     // load u of a wave is exactly its score operand for k step u (position
     // 16 w + lr, k 32 u + 8 lq .. +7), kept in registers until the block's
     // scores.
+    // With 32-position blocks two waves share a 16-position group, each
+    // loading half of the row's 16-byte chunks.
     v4i kbuf[kLoads], vbuf[kLoads];
-    const int pp = 16 * wave + lr;
+    const int pp = 16 * (wave % kPt) + lr;
+    const int cbase = (wave / kPt) * (kChunks * kPt / 4);
     auto fetch = [&](int b) {
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) {
-            const int c = 4 * u + lq;
-            const int64_t pos = (int64_t)b * kBlock + pp;
+            const int c = cbase + 4 * u + lq;
+            const int64_t pos = (int64_t)b * BLK + pp;
             kbuf[u] = v4i{0, 0, 0, 0};
             vbuf[u] = v4i{0, 0, 0, 0};
             if (pos < used) {
@@ -144,16 +152,16 @@ __device__ __forceinline__ void attention_split(const AttnArgs &a) {
             }
         }
     };
-    static_assert(WPR != 4 || kLoads == kKs, "one key load per k step");
+    static_assert(WPR != 4 || (BLK == 64 && kLoads == kKs), "one key load per k step");
     v4i kop[WPR == 4 ? kKs : 1];
     auto stage = [&]() {
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) {
-            const int c = 4 * u + lq;
+            const int c = cbase + 4 * u + lq;
             if constexpr (WPR == 4) kop[u] = kbuf[u];
             else *reinterpret_cast<v4i *>(k_lds + pp * kKStride + c * 16) = kbuf[u];
             const uint32_t w[4] = {(uint32_t)vbuf[u].x, (uint32_t)vbuf[u].y, (uint32_t)vbuf[u].z, (uint32_t)vbuf[u].w};
-            const int col = (pp + 8 * (c & 7)) & (kBlock - 1);   // rows 8c .. 8c+7: d / 8 = c
+            const int col = (pp + 8 * (c & 7)) & (BLK - 1);   // rows 8c .. 8c+7: d / 8 = c
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 *reinterpret_cast<uint16_t *>(vt_lds + (8 * c + e) * kVtStride + col * 2) =
@@ -204,7 +212,7 @@ __device__ __forceinline__ void attention_split(const AttnArgs &a) {
                 float bm = -INFINITY;
 #pragma unroll
                 for (int q = 0; q < kPtW; ++q) {
-                    const int64_t pos = (int64_t)b * kBlock + 16 * (sw + q * WPR) + lr;
+                    const int64_t pos = (int64_t)b * BLK + 16 * (sw + q * WPR) + lr;
                     x[q][j] = pos <= lim ? sc[q][j] * a.scale_log2 : -INFINITY;
                     bm = fmaxf(bm, x[q][j]);
                 }
@@ -263,13 +271,13 @@ __device__ __forceinline__ void attention_split(const AttnArgs &a) {
         if (!computes) continue;
         // values: O += P V over the wave's column tiles
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < BLK / 32; ++ks) {
             const bf8 pa = *reinterpret_cast<const bf8 *>(pw + lr * kPStride + (32 * ks + 8 * lq) * 2);
             const bf8 pl = *reinterpret_cast<const bf8 *>(pw + (16 + lr) * kPStride + (32 * ks + 8 * lq) * 2);
 #pragma unroll
             for (int c = 0; c < kCtW; ++c) {
                 const int d = 16 * (sw + c * WPR) + lr;
-                const int col = (32 * ks + 8 * lq + 8 * ((d >> 3) & 7)) & (kBlock - 1);
+                const int col = (32 * ks + 8 * lq + 8 * ((d >> 3) & 7)) & (BLK - 1);
                 const bf8 vb = *reinterpret_cast<const bf8 *>(vt_lds + d * kVtStride + col * 2);
                 o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[c], 0, 0, 0);
                 o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[c], 0, 0, 0);
@@ -317,16 +325,17 @@ __device__ __forceinline__ void attention_split(const AttnArgs &a) {
     }
 }
 
-template <int D, int WPR>
+template <int D, int WPR, int BLK>
 __global__ __launch_bounds__(kAttnThreads) void decode_attention_kernel(AttnArgs a) {
-    attention_split<D, WPR>(a);
+    attention_split<D, WPR, BLK>(a);
 }
 // The same with at most 256 registers, so that two workgroups fit on a CU
-// (two waves per SIMD): the form for two row tiles, whose LDS allows two.
-template <int D, int WPR>
+// (two waves per SIMD): the forms for two row tiles, and for four with
+// 32-position blocks, whose LDS allows two.
+template <int D, int WPR, int BLK>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_attention_kernel_x2(
     AttnArgs a) {
-    attention_split<D, WPR>(a);
+    attention_split<D, WPR, BLK>(a);
 }
 
 struct MergeArgs {
@@ -425,18 +434,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(MergeArgs a) {
 AttnPlan plan_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P, int n_cu) {
     AttnPlan pl;
     const int64_t used = P + M;
-    pl.n_blocks = (used + kBlock - 1) / kBlock;
     pl.rows = (n_q / n_kv) * M;
-    // keys, transposed values, the row tiles' probabilities
     const int64_t row_tiles = (pl.rows + 15) / 16;
-    pl.lds_bytes = (int)(kBlock * (D * 2 + 16) + D * (kBlock * 2 + 16) + row_tiles * 32 * (kBlock * 2 + 16));
+    pl.block = row_tiles > 2 ? kBlock / 2 : kBlock;
+    pl.n_blocks = (used + pl.block - 1) / pl.block;
+    // keys, transposed values, the row tiles' probabilities
+    pl.lds_bytes = (int)(pl.block * (D * 2 + 16) + D * (pl.block * 2 + 16) + row_tiles * 32 * (pl.block * 2 + 16));
     // a workgroup per CU, two where their LDS fits (one hides the other's
-    // load latency), and at least kMinBlocks blocks each (a split's fixed
-    // cost -- the query load, the first fetch, publishing -- is latency)
-    constexpr int64_t kMinBlocks = MBQ_ATTN_MIN_BLOCKS;
-    // (the one-tile form's registers allow two waves per SIMD; the two-tile
-    // form is compiled for it)
-    const int64_t per_cu = row_tiles <= 2 && pl.lds_bytes <= 80 * 1024 ? 2 : 1;
+    // load latency; the one-tile form's registers allow it, and the others
+    // have a form capped at 256 registers), and at least MBQ_ATTN_MIN_BLOCKS
+    // 64-position blocks' worth of positions each (a split's fixed cost --
+    // the query load, the first fetch, publishing -- is latency)
+    const int64_t kMinBlocks = MBQ_ATTN_MIN_BLOCKS * kBlock / pl.block;
+    const int64_t per_cu = pl.lds_bytes <= 80 * 1024 ? 2 : 1;
     pl.two_per_cu = per_cu == 2;
     const int64_t target = std::max<int64_t>(
         1, std::min<int64_t>({kMaxSplits, per_cu * n_cu / n_kv, (pl.n_blocks + kMinBlocks - 1) / kMinBlocks}));
@@ -478,11 +488,12 @@ hipError_t launch_attention(const AttnPlan &pl, int64_t M, int64_t n_q, int64_t 
     a.n_blocks = (int32_t)pl.n_blocks;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const int wpr = pl.rows <= 16 ? 4 : pl.rows <= 32 ? 2 : 1;
-#define MBQ_ATTN(DD)                                                                              \
-    (wpr == 4   ? reinterpret_cast<const void *>(&decode_attention_kernel<DD, 4>)                  \
-     : wpr == 2 ? (pl.two_per_cu ? reinterpret_cast<const void *>(&decode_attention_kernel_x2<DD, 2>) \
-                                 : reinterpret_cast<const void *>(&decode_attention_kernel<DD, 2>))  \
-                : reinterpret_cast<const void *>(&decode_attention_kernel<DD, 1>))
+#define MBQ_ATTN(DD)                                                                                   \
+    (wpr == 4   ? reinterpret_cast<const void *>(&decode_attention_kernel<DD, 4, 64>)                   \
+     : wpr == 2 ? (pl.two_per_cu ? reinterpret_cast<const void *>(&decode_attention_kernel_x2<DD, 2, 64>) \
+                                 : reinterpret_cast<const void *>(&decode_attention_kernel<DD, 2, 64>))  \
+                : (pl.two_per_cu ? reinterpret_cast<const void *>(&decode_attention_kernel_x2<DD, 1, 32>) \
+                                 : reinterpret_cast<const void *>(&decode_attention_kernel<DD, 1, 32>)))
     const void *fn = D == 64 ? MBQ_ATTN(64) : D == 128 ? MBQ_ATTN(128) : MBQ_ATTN(256);
 #undef MBQ_ATTN
     void *args[] = {(void *)&a};

@@ -53,8 +53,9 @@ int relayout_inplace(int bits, int64_t N, int64_t K, void *buf, int n_cu, hipStr
 // Split-prefix decode attention (attn.hip).
 struct AttnPlan {
     int64_t n_blocks = 0, blocks_per_split = 0, n_split = 0, rows = 0;
+    int64_t block = 64;      // positions per block
     int64_t merge_tpq = 1;   // merge lanes per four outputs
-    bool two_per_cu = false; // two workgroups per CU (the split kernel's register-capped form for two row tiles)
+    bool two_per_cu = false; // two workgroups per CU (the split kernel's register-capped form)
     int64_t off_ml = 0, off_o = 0, ws_bytes = 0;
     int lds_bytes = 0;
 };
