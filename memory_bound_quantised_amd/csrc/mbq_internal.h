@@ -290,23 +290,6 @@ __device__ __forceinline__ void load_tile(const uint8_t *tile, int lane, v4i (&w
         gptr(reinterpret_cast<const v2u *>(tile + Layout<BITS>::kWeightBytes) + (lane & 15)));
 }
 
-// The same through a buffer resource: with real == false the resource has no
-// bytes, so every load returns zeros without touching memory (a placeholder
-// that keeps a fixed count of outstanding loads).  Slabs 4 and 5 (W6) reach
-// past the 12-bit instruction offset through the scalar offset.
-template <int BITS>
-__device__ __forceinline__ void load_tile_buf(const uint8_t *tile, bool real, int lane,
-                                              v4i (&w)[Layout<BITS>::kSlabs], v2u &scales) {
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(tile), 0, real ? Layout<BITS>::kTileBytes : 0, 0x00020000);
-    constexpr int kNt = 2;   // non-temporal: the weights are read once
-#pragma unroll
-    for (int j = 0; j < Layout<BITS>::kSlabs; ++j)
-        w[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16 + (j & 3) * kSlab,
-                                                                              (j >> 2) * 4 * kSlab, kNt));
-    scales = __builtin_amdgcn_raw_buffer_load_b64(r, Layout<BITS>::kWeightBytes + (lane & 15) * 8, 0, kNt);
-}
-
 // fp32 scale of row i (0..3) of the lane from its packed scales.
 __device__ __forceinline__ float row_scale(v2u s, int i) {
     const uint32_t word = i < 2 ? s.x : s.y;
