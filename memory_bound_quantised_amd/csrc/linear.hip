@@ -26,7 +26,10 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kTargetWaves = 2048;   // about 8 waves per CU on 256 CUs
-constexpr int kTilesPerWave = 4;     // a split's tiles, at least (when the matrix has enough)
+#ifndef MBQ_LIN_TILES
+#define MBQ_LIN_TILES 4
+#endif
+constexpr int kTilesPerWave = MBQ_LIN_TILES;   // a split's tiles, at least (when the matrix has enough)
 constexpr int kMaxSplits = 16;       // a row block's partials, at most
 #ifndef MBQ_LIN_MFMA_MIN_M
 #define MBQ_LIN_MFMA_MIN_M 1
