@@ -30,7 +30,7 @@ def _run(q, k, v, P, ws=None):
 
 @pytest.mark.parametrize("P", [0, 1, 63, 64, 65, 200, 1000])
 @pytest.mark.parametrize("M,n_q,n_kv,D", [(1, 1, 1, 64), (1, 8, 1, 128), (2, 4, 2, 256), (3, 6, 3, 64),
-                                          (8, 8, 1, 256), (5, 16, 4, 128), (8, 16, 2, 64)])
+                                          (8, 8, 1, 256), (5, 16, 4, 128), (8, 16, 2, 64), (5, 8, 1, 256)])
 def test_decode_attention_matches_oracle(M, n_q, n_kv, D, P):
     L = P + M + 5
     q, k, v = _inputs(M, n_q, n_kv, D, L, seed=P * 31 + M * 7 + D)
