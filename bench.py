@@ -1,18 +1,24 @@
 """Benchmark: decode-step weight-read bandwidth of the skinny W4A8/W6A8 linears.
 
-One step is one mbq_layer_sequence call: the whole decode-step walk (per layer:
-RMSNorm+quant -> q/k/v, quant -> o, quant -> gate/up, quant -> down; with
---dataflow swiglu the norms carry weights and down reads silu(gate) * up) over
-a synthetic 9B-shaped (default) or 27B-shaped weight set, every weight matrix
-read once.  Weights, buffers and the workspace are resident in HBM before the
-timed region.  Prints one JSON line.
+One step is one launch of the fused decode-step walk (per layer: RMSNorm+quant
+-> q/k/v, quant -> o, quant -> gate/up, quant -> down; with --dataflow swiglu
+the norms carry weights and down reads silu(gate) * up) over a synthetic
+27B-shaped (default) or 9B-shaped weight set, every weight matrix read once.
+Weights, buffers and the workspace are resident in HBM before the timed
+region.  Prints one JSON line: the walk at --m (default 1) as the headline,
+the other row counts (--extra-m, default 2 3 4) as fields, the HBM
+stream-read ceiling measured in the same process, the single 4096 x 4096
+W4A8 linear at M = 1 over 128 rotated copies (alone and with its
+quantisation), and the CPU oracle on all host cores and on one.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--set 9b|27b] [--bits 4|6]
-                  [--m 1] [--extra-m 3] [--dataflow plain|swiglu] [--no-cpu]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--set 27b|9b] [--bits 4|6]
+                  [--m 1] [--extra-m 2 3 4] [--dataflow plain|swiglu] [--no-cpu]
+                  [--no-linear] [--no-ceiling]
 
-With --workload attention it instead times the split-prefix decode attention of
-one 27B-shaped attention layer (32 query heads, 4 key/value heads of 256) over a
---ctx-token bf16 KV cache, and reports the cache-read rate.
+--workload linear prints the single-linear measurement as the headline instead;
+--workload attention times the split-prefix decode attention of one
+27B-shaped attention layer (32 query heads, 4 key/value heads of 256) over a
+--ctx-token bf16 KV cache and reports the cache-read rate.
 """
 from __future__ import annotations
 
@@ -200,38 +206,180 @@ def run_attention(args):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(set_name, bits, n_layers, dataflow="plain", budget_s=10.0):
-    """The oracle on the host cores: the same M=1 walk, layer after layer (starting over after
-    the last layer), until about budget_s seconds of oracle time have been spent."""
+CEILING_BYTES = 4 << 30
+
+
+def measure_ceiling(mbq, reps=10):
+    """HBM stream-read ceiling: one pass of mbq_stream_read over 4 GiB, best and
+    median of `reps` event-timed passes after 3 warm-up passes."""
+    import torch
+    buf = torch.ones(CEILING_BYTES, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        mbq.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        mbq.stream_read(buf, sink)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]) / 1e3
+    del buf
+    torch.cuda.empty_cache()
+    return {"GB/s_best": round(CEILING_BYTES / per.min() / 1e9, 1),
+            "GB/s_median": round(CEILING_BYTES / float(np.median(per)) / 1e9, 1),
+            "bytes": CEILING_BYTES, "kernel": "stream_read_kernel (mbq_stream_read): dwordx4 nt loads, "
+                                             "8 waves per CU, one pass over 4 GiB"}
+
+
+def _graph_time(fn, n_calls, reps):
+    """Per-call milliseconds of fn(i) for i in range(n_calls), captured once in a
+    HIP graph and replayed `reps` times (event-timed), so that back-to-back
+    launches run without host gaps.  Falls back to eager launches if capture fails."""
+    import torch
+    torch.cuda.synchronize()
+    mode = "graph"
+    try:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(n_calls):       # warm-up outside the capture
+                fn(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(n_calls):
+                fn(i)
+        run = g.replay
+    except Exception as e:   # pragma: no cover - depends on the runtime
+        log(f"graph capture failed ({e}); timing eager launches")
+        mode = "eager"
+
+        def run():
+            for i in range(n_calls):
+                fn(i)
+    run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for r in range(reps):
+        run()
+        ev[r + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]) / n_calls
+    return float(np.median(per)), float(per.min()), mode
+
+
+def run_linear_config(mbq, copies=128, reps=8):
+    """The single 4096 x 4096 W4A8 linear at M = 1 (activations N(0,1) bf16, int4
+    codes uniform, fp16 group-128 scales U(0.005, 0.02)) over `copies` distinct
+    packed matrices used in turn (8.65 MB each, together over 1 GB, so no copy is
+    still cached when it comes round again): the linear alone, and the per-row
+    quantisation followed by the linear."""
+    import torch
+    N = K = 4096
+    bits = 4
+    packed = []
+    for i in range(copies):
+        canon, S = synth.weights(bits, N, K, seed=10_000 + i)
+        packed.append(mbq.pack_weights(bits, to_dev(canon), to_dev(S), N, K))
+    x = to_dev(synth.activations(1, K))
+    q, s = mbq.quantize_act(x)
+    ws = torch.zeros(mbq.linear_workspace_bytes(bits, 1, N, K), dtype=torch.uint8, device="cuda")
+    y = torch.empty((1, N), dtype=torch.bfloat16, device="cuda")
+    qb = torch.empty_like(q)
+    sb = torch.empty_like(s)
+    L = mbq.lib()
+    st = lambda: mbq._stream()
+
+    def lin(i):
+        mbq._check("mbq_w4a8_linear", L.mbq_w4a8_linear(1, N, K, q.data_ptr(), s.data_ptr(),
+                                                        packed[i].data_ptr(), y.data_ptr(), ws.data_ptr(),
+                                                        ws.numel(), st()))
+
+    def quant_lin(i):
+        mbq._check("mbq_quantize_act", L.mbq_quantize_act(1, K, x.data_ptr(), qb.data_ptr(), sb.data_ptr(), st()))
+        mbq._check("mbq_w4a8_linear", L.mbq_w4a8_linear(1, N, K, qb.data_ptr(), sb.data_ptr(),
+                                                        packed[i].data_ptr(), y.data_ptr(), ws.data_ptr(),
+                                                        ws.numel(), st()))
+    wb = synth.weight_bytes(bits, [("w", K, N)])
+    lin_ms, lin_best, mode = _graph_time(lin, copies, reps)
+    ql_ms, ql_best, _ = _graph_time(quant_lin, copies, reps)
+    assert torch.isfinite(y.float()).all()
+    del packed
+    torch.cuda.empty_cache()
+    return {"workload": "single 4096x4096 W4A8 linear, M=1, 128 rotated copies", "weight_bytes_per_call": wb,
+            "timing": f"{mode} of {copies} back-to-back calls, median of {reps} replays",
+            "linear_us": round(lin_ms * 1e3, 3), "linear_GB/s": round(wb / (lin_ms / 1e3) / 1e9, 1),
+            "linear_pct_hbm_peak": round(100 * wb / (lin_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
+            "linear_us_best": round(lin_best * 1e3, 3),
+            "quant_plus_linear_us": round(ql_ms * 1e3, 3),
+            "quant_plus_linear_GB/s": round(wb / (ql_ms / 1e3) / 1e9, 1)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(set_name, bits, n_layers, dataflow="plain", budget_s=10.0, sample_layers=8):
+    """The oracle on the host cores: the M=1 walk of the first `sample_layers`
+    layers of the set, layer after layer (starting over after the last of
+    them), until about budget_s seconds of oracle time have been spent; once on
+    every host core and once on one thread."""
     import oracle
     shapes_fn, _ = synth.WEIGHT_SETS[set_name]
-    ops, widths = synth.layer_program(shapes_fn, n_layers, dataflow=dataflow)
+    L = min(n_layers, sample_layers)
+    ops, widths = synth.layer_program(shapes_fn, L, dataflow=dataflow)
     for o in ops:
         if "norm_seed" in o:
             o["norm_w"] = synth.norm_weights(o["K"], o["norm_seed"])
-    M = 1
-    bufs = {i: np.zeros((M, w), np.uint16) for i, w in enumerate(widths)}
-    bufs[0] = synth.activations(M, widths[0])
     per_layer = len(shapes_fn())
-    spent, done_bytes, layers = 0.0, 0, 0
     mats = {}
-    while spent < budget_s:
-        layer = layers % n_layers
-        lops = ops[layer * per_layer:(layer + 1) * per_layer]
-        for o in lops:
-            if o["matrix"] not in mats:
-                mats[o["matrix"]] = synth.weights(bits, o["N"], o["K"], seed=1 + o["matrix"])
-        t0 = time.perf_counter()
-        oracle.layer_sequence(bits, lops, bufs, lambda i: mats[i])
-        spent += time.perf_counter() - t0
-        done_bytes += synth.weight_bytes(bits, [(o["name"], o["K"], o["N"]) for o in lops])
-        layers += 1
-    gbs = done_bytes / spent / 1e9
-    step_bytes = synth.weight_bytes(bits, [(o["name"], o["K"], o["N"]) for o in ops])
-    return dict(value=round(gbs, 4), unit="GB/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"{layers} layers of the {n_layers}-layer walk at M=1 ({layers / n_layers:.1f} passes, "
-                       f"{done_bytes / 1e9:.3f} GB of weights, {spent:.1f} s of oracle time), scaled to GB/s; "
-                       f"equivalent {gbs * 1e9 / step_bytes:.4f} steps/s")
+    step_bytes = synth.weight_bytes(bits, [(o["name"], o["K"], o["N"]) for o in ops]) * n_layers // L
+
+    def timed(threads):
+        oracle.set_threads(threads)
+        used = oracle.num_threads()
+        M = 1
+        bufs = {i: np.zeros((M, w), np.uint16) for i, w in enumerate(widths)}
+        bufs[0] = synth.activations(M, widths[0])
+        spent, done_bytes, layers = 0.0, 0, 0
+        while spent < budget_s:
+            layer = layers % L
+            lops = ops[layer * per_layer:(layer + 1) * per_layer]
+            for o in lops:
+                if o["matrix"] not in mats:
+                    mats[o["matrix"]] = synth.weights(bits, o["N"], o["K"], seed=1 + o["matrix"])
+            t0 = time.perf_counter()
+            oracle.layer_sequence(bits, lops, bufs, lambda i: mats[i])
+            spent += time.perf_counter() - t0
+            done_bytes += synth.weight_bytes(bits, [(o["name"], o["K"], o["N"]) for o in lops])
+            layers += 1
+        return used, done_bytes / spent / 1e9, layers, done_bytes, spent
+
+    all_threads = os.cpu_count() or 1
+    used, gbs, layers, done, spent = timed(all_threads)
+    used1, gbs1, layers1, done1, spent1 = timed(1)
+    oracle.set_threads(all_threads)
+    return dict(value=round(gbs, 4), unit="GB/s", cores=used, kind="oracle",
+                sample=f"{layers} layer walks (cycling over the first {L} layers of the {n_layers}-layer set) at M=1, "
+                       f"{done / 1e9:.3f} GB of weights in {spent:.1f} s of oracle time on {used} threads, "
+                       f"scaled to GB/s; equivalent {gbs * 1e9 / step_bytes:.4f} steps/s",
+                cpu_model=cpu_model(),
+                one_thread={"value": round(gbs1, 4), "unit": "GB/s", "cores": used1,
+                            "sample": f"{layers1} layer walks, {done1 / 1e9:.3f} GB in {spent1:.1f} s"})
 
 
 def main():
@@ -239,13 +387,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--set", default="9b", choices=sorted(synth.WEIGHT_SETS))
+    ap.add_argument("--set", default="27b", choices=sorted(synth.WEIGHT_SETS))
     ap.add_argument("--bits", type=int, default=4, choices=[4, 6])
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--m", type=int, default=1)
-    ap.add_argument("--extra-m", type=int, nargs="*", default=[3])
-    ap.add_argument("--workload", default="walk", choices=["walk", "attention"],
-                    help="attention: the split-prefix decode attention of one 27B-shaped layer instead of the walk")
+    ap.add_argument("--extra-m", type=int, nargs="*", default=[2, 3, 4])
+    ap.add_argument("--workload", default="walk", choices=["walk", "linear", "attention"],
+                    help="linear: the single 4096x4096 W4A8 linear as the headline; attention: the "
+                         "split-prefix decode attention of one 27B-shaped layer instead of the walk")
+    ap.add_argument("--no-linear", action="store_true", help="skip the single-linear measurement")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the stream-read ceiling")
     ap.add_argument("--ctx", type=int, default=32768, help="attention: cached prefix length")
     ap.add_argument("--dataflow", default="plain", choices=["plain", "swiglu"],
                     help="swiglu: weighted RMSNorms before q/k/v and gate/up, silu(gate) * up before down")
@@ -268,6 +419,26 @@ def main():
 
     if args.workload == "attention":
         run_attention(args)
+        return
+
+    ceiling = None
+    if not args.no_ceiling:
+        log("measuring the HBM stream-read ceiling (4 GiB)")
+        ceiling = measure_ceiling(mbq)
+        log(f"ceiling: {ceiling}")
+
+    if args.workload == "linear":
+        r = run_linear_config(mbq)
+        gbs = r["linear_GB/s"]
+        out = {"metric": "single-linear weight-read GB/s (% of HBM peak), 4096x4096 W4A8, M=1", "value": gbs,
+               "unit": "GB/s", "n_gpus": 1, "steps": 8, "warmup": 1, "ms_per_step": r["linear_us"] / 1e3,
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+               "data": "synthetic", "config": {"workload": r["workload"]}, "linear": r,
+               "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+        if ceiling:
+            out["ceiling"] = ceiling
+            out["pct_of_ceiling"] = round(100 * gbs / ceiling["GB/s_best"], 2)
+        print(json.dumps(out), flush=True)
         return
 
     if args.calib_copy > 0:
@@ -339,8 +510,15 @@ def main():
                        "traffic": measured_traffic(f"{args.set}/w{args.bits}/m{args.m}/l{n_layers}"
                                                    + ("/swiglu" if args.dataflow == "swiglu" else "")),
                        "bytes_per_launch": wbytes, "launch_ms": round(main_r["event_ms_median"], 4)}
+    if ceiling:
+        out["ceiling"] = ceiling
+        out["pct_of_ceiling"] = round(100 * gbs / ceiling["GB/s_best"], 2)
+    if not args.no_linear:
+        log("timing the single 4096x4096 W4A8 linear over 128 rotated copies")
+        out["linear_4096"] = run_linear_config(mbq)
+        log(f"linear: {out['linear_4096']}")
     if not args.no_cpu:
-        log("timing the CPU oracle on a bounded sample")
+        log("timing the CPU oracle on a bounded sample (all host cores, then one thread)")
         out["cpu_baseline"] = cpu_baseline(args.set, args.bits, n_layers, args.dataflow)
     print(json.dumps(out), flush=True)
 

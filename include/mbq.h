@@ -46,10 +46,14 @@
  *   - Alignment: packed weights 256-byte aligned; activation, q and y
  *     pointers 16-byte aligned; workspaces 256-byte aligned.
  *   - Workspaces: caller-owned device memory of at least the queried size,
- *     zero-filled before its first use (e.g. allocated with zeros).  A call
- *     that runs to completion leaves the workspace's counters zero again, so
- *     the same workspace serves any later call.  Calls that share a workspace
- *     must not overlap in time (same stream, or synchronised).
+ *     zero-filled before its first use (e.g. allocated with zeros).  A linear
+ *     that runs to completion leaves its workspace's counters zero again, so
+ *     the same workspace serves any later linear of any shape.  A walk's
+ *     workspace (mbq_sequence_workspace_bytes) holds two disjoint regions, the
+ *     fused walk's and the unfused form's, so both forms may share it; the
+ *     fused region keeps the prepared plan and tagged data between steps and
+ *     must not be handed to other calls while the plan is in use.  Calls that
+ *     share a workspace must not overlap in time (same stream, or synchronised).
  */
 #ifndef MBQ_H
 #define MBQ_H
@@ -171,8 +175,16 @@ int mbq_w6a8_linear(int64_t M, int64_t N, int64_t K, const int8_t *q, const floa
                     void *stream);
 
 /* The exact int32 group sums acc[m][n][g] (device int32 [M][N][K/128]) that the
- * linear rescales, computed by the same unpack and dot-product code.  For tests. */
-int mbq_linear_group_acc(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q,
+ * linears rescale, for tests.  `form` picks the tile code that produces them,
+ * each being the very function the product runs:
+ *   MBQ_FORM_MFMA  the matrix-core tile (v_mfma_i32_16x16x64_i8, activation rows
+ *                  padded to 16): mbq_w4a8_linear / mbq_w6a8_linear at every M,
+ *                  and the fused walk from M = 2 on;
+ *   MBQ_FORM_DOT4  the v_dot4 tile with its four 32-k slice sums added in int32:
+ *                  the fused walk at M = 1.
+ * Returns MBQ_ERR_SHAPE for any other form. */
+enum { MBQ_FORM_DOT4 = 0, MBQ_FORM_MFMA = 1 };
+int mbq_linear_group_acc(int bits, int form, int64_t M, int64_t N, int64_t K, const int8_t *q,
                          const void *packed, int32_t *acc, void *stream);
 
 /* ---------------------------------------------------------------- decode attention
@@ -196,6 +208,17 @@ int64_t mbq_attention_workspace_bytes(int64_t M, int64_t n_q, int64_t n_kv, int6
 int mbq_decode_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P, int64_t L, const void *q,
                          const void *k_cache, const void *v_cache, void *o, void *ws, int64_t ws_bytes,
                          void *stream);
+
+/* ---------------------------------------------------------------- measurement
+ * HBM stream-read ceiling ("What is the bottleneck?": token generation is
+ * bound by how fast the GPU reads the model from VRAM): one pass over `bytes`
+ * bytes of device memory at buf (256-byte aligned; bytes a positive multiple
+ * of 1024) with the same 16-byte non-temporal loads the weight stream uses,
+ * spread over every CU.  The bytes read are folded into a digest; *sink
+ * (device uint32, 4-byte aligned) is written only for one particular digest
+ * value, so the call leaves it untouched in practice.  The achieved rate of
+ * this call is the measured ceiling the weight stream is judged against. */
+int mbq_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
 
 /* ---------------------------------------------------------------- decode-step walk
  * "What is the bottleneck?": one decode step reads every weight matrix of the
@@ -224,10 +247,10 @@ typedef struct mbq_op {
                             16-byte aligned; otherwise ignored */
 } mbq_op;
 
-/* Workspace bytes for the walk (fused and unfused forms; only the unfused
- * form's when the fused walk rejects the list, see mbq_sequence_prepare), or a
- * negative mbq_status (MBQ_ERR_PROGRAM for a malformed op list).  ops,
- * buf_widths: host. */
+/* Workspace bytes for the walk: the fused walk's region (none when the fused
+ * walk rejects the list, see mbq_sequence_prepare) followed by the unfused
+ * form's, or a negative mbq_status (MBQ_ERR_PROGRAM for a malformed op list).
+ * ops, buf_widths: host. */
 int64_t mbq_sequence_workspace_bytes(const mbq_op *ops, int32_t n_ops,
                                      const int64_t *buf_widths, int32_t n_bufs, int64_t M);
 
@@ -254,8 +277,12 @@ typedef struct mbq_sequence_info {
  * weights, or use a weighted RMSNorm and no weights, or when a SwiGLU op's
  * gate and up buffers are not either both written before the walk or both
  * written by ops of one phase with equal N whose outputs nothing else in the
- * walk reads.  The plan stays valid while ws, bufs, the packed weights and
- * the norm weights stay where they are. */
+ * walk reads; when an op overwrites a buffer that an earlier phase read as
+ * an input written before the walk; and when one buffer is written by several
+ * ops whose row blocks are finalised by different workgroups (the walk
+ * orders neither case; the same op layout repeated layer after layer is
+ * fine).  The plan stays valid while ws, bufs, the packed weights and the
+ * norm weights stay where they are. */
 int mbq_sequence_prepare(const mbq_op *ops, int32_t n_ops, void *const *bufs,
                          const int64_t *buf_widths, int32_t n_bufs, int64_t M, void *ws,
                          int64_t ws_bytes, void *stream, mbq_sequence_info *info);

@@ -28,7 +28,8 @@ EXPORTS = ["mbq_status_string", "mbq_last_hip_error", "mbq_version", "mbq_packed
            "mbq_linear_workspace_bytes", "mbq_w4a8_linear",
            "mbq_w6a8_linear", "mbq_linear_group_acc", "mbq_sequence_workspace_bytes",
            "mbq_sequence_prepare", "mbq_sequence_run", "mbq_sequence_check", "mbq_layer_sequence",
-           "mbq_layer_sequence_unfused", "mbq_attention_workspace_bytes", "mbq_decode_attention"]
+           "mbq_layer_sequence_unfused", "mbq_attention_workspace_bytes", "mbq_decode_attention",
+           "mbq_stream_read"]
 
 
 class MbqError(RuntimeError):
@@ -89,7 +90,7 @@ def lib() -> ctypes.CDLL:
         L.mbq_linear_workspace_bytes.restype = I64
         for fn in (L.mbq_w4a8_linear, L.mbq_w6a8_linear):
             fn.argtypes = [I64, I64, I64, P, P, P, P, P, I64, P]
-        L.mbq_linear_group_acc.argtypes = [ctypes.c_int, I64, I64, I64, P, P, P, P]
+        L.mbq_linear_group_acc.argtypes = [ctypes.c_int, ctypes.c_int, I64, I64, I64, P, P, P, P]
         L.mbq_sequence_workspace_bytes.argtypes = [P, I32, P, I32, I64]
         L.mbq_sequence_workspace_bytes.restype = I64
         L.mbq_layer_sequence.argtypes = [P, I32, P, P, I32, I64, P, I64, P]
@@ -97,6 +98,7 @@ def lib() -> ctypes.CDLL:
         L.mbq_sequence_prepare.argtypes = [P, I32, P, P, I32, I64, P, I64, P, P]
         L.mbq_sequence_run.argtypes = [P, P, P]
         L.mbq_sequence_check.argtypes = [P, P]
+        L.mbq_stream_read.argtypes = [P, I64, P, P]
         for name in EXPORTS:
             if name not in ("mbq_status_string", "mbq_last_hip_error", "mbq_version",
                             "mbq_packed_bytes", "mbq_linear_workspace_bytes",
@@ -261,13 +263,29 @@ def w6a8_linear(q, s, packed, N, ws=None, out=None):
     return linear(6, q, s, packed, N, ws, out)
 
 
-def linear_group_acc(bits: int, q, packed, N: int):
+FORM_DOT4, FORM_MFMA = 0, 1
+
+
+def linear_group_acc(bits: int, q, packed, N: int, form: int = FORM_MFMA):
+    """Exact int32 group sums [M][N][K/128] through the product's tile code:
+    form=FORM_MFMA (the linears, the walk from M=2) or FORM_DOT4 (the walk at M=1)."""
     import torch
     M, K = q.shape
     acc = torch.empty((M, N, K // 128), dtype=torch.int32, device=q.device)
-    _check("mbq_linear_group_acc", lib().mbq_linear_group_acc(bits, M, N, K, _ptr(q), _ptr(packed),
+    _check("mbq_linear_group_acc", lib().mbq_linear_group_acc(bits, form, M, N, K, _ptr(q), _ptr(packed),
                                                               _ptr(acc), _stream()))
     return acc
+
+
+def stream_read(buf, sink=None):
+    """One pass of the HBM stream-read ceiling kernel over the uint8 device tensor
+    buf (a multiple of 1 KiB); sink: a uint32/int32 device scalar (made if None)."""
+    import torch
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check("mbq_stream_read", lib().mbq_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                                    _stream()))
+    return sink
 
 
 class LayerSequence:
@@ -276,13 +294,14 @@ class LayerSequence:
     ops: iterable of dicts with bits, prologue, N, K, packed (uint8 tensor),
     in_buf, out_buf, and in_buf2 (SwiGLU's up buffer) or norm_w (bf16 tensor
     [K], weighted RMSNorm) where the prologue needs them.  bufs: list of bf16
-    tensors [M][width].  The workspace is
-    allocated (zero-filled) once here.  fused=True prepares the persistent
+    tensors [M][width].  The workspace is allocated (zero-filled) once here
+    unless ws (a zero-filled uint8 device tensor, possibly shared with another
+    LayerSequence over the same op list) is given.  fused=True prepares the persistent
     kernel's plan once (mbq_sequence_prepare) and run() is one launch
     (mbq_sequence_run); fused=False runs mbq_layer_sequence_unfused.
     """
 
-    def __init__(self, ops, bufs, M: int, fused: bool = True):
+    def __init__(self, ops, bufs, M: int, fused: bool = True, ws=None):
         self.M = M
         self.fused = fused
         self.bufs = list(bufs)
@@ -300,7 +319,9 @@ class LayerSequence:
         need = lib().mbq_sequence_workspace_bytes(arr, self._n_ops, self._widths, len(bufs), M)
         if need < 0:
             raise MbqError("mbq_sequence_workspace_bytes", need)
-        self.ws = _zeros(need, bufs[0].device)
+        if ws is not None and ws.numel() * ws.element_size() < need:
+            raise ValueError(f"workspace of {ws.numel()} bytes, {need} needed")
+        self.ws = _zeros(need, bufs[0].device) if ws is None else ws
         self.info = MbqSequenceInfo()
         if fused:
             _check("mbq_sequence_prepare",

@@ -218,15 +218,16 @@ int mbq_w6a8_linear(int64_t M, int64_t N, int64_t K, const int8_t *q, const floa
     return linear_common(6, M, N, K, q, s, packed, y_bf16, ws, ws_bytes, stream);
 }
 
-int mbq_linear_group_acc(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q,
+int mbq_linear_group_acc(int bits, int form, int64_t M, int64_t N, int64_t K, const int8_t *q,
                          const void *packed, int32_t *acc, void *stream) {
     if (!bits_ok(bits)) return MBQ_ERR_BITS;
+    if (form != MBQ_FORM_DOT4 && form != MBQ_FORM_MFMA) return MBQ_ERR_SHAPE;
     if (!q || !packed || !acc) return MBQ_ERR_NULL;
     if (!m_ok(M) || !n_ok(N) || !k_ok(K)) return MBQ_ERR_SHAPE;
     if (!aligned(packed, 256) || !aligned(q, 16) || !aligned(acc, 4)) return MBQ_ERR_ALIGN;
     int st = check_device();
     if (st) return st;
-    hipError_t e = launch_group_acc(bits, M, N, K, q, packed, acc, (hipStream_t)stream);
+    hipError_t e = launch_group_acc(bits, form == MBQ_FORM_MFMA, M, N, K, q, packed, acc, (hipStream_t)stream);
     return e == hipSuccess ? MBQ_OK : hip_fail(e);
 }
 
@@ -234,6 +235,19 @@ static int device_cus(int *n_cu) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    return e == hipSuccess ? MBQ_OK : hip_fail(e);
+}
+
+int mbq_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream) {
+    if (!buf || !sink) return MBQ_ERR_NULL;
+    if (bytes < kSlab || bytes % kSlab) return MBQ_ERR_SHAPE;
+    if (!aligned(buf, 256) || !aligned(sink, 4)) return MBQ_ERR_ALIGN;
+    int st = check_device();
+    if (st) return st;
+    int n_cu = 0;
+    st = device_cus(&n_cu);
+    if (st) return st;
+    hipError_t e = launch_stream_read(buf, bytes, sink, n_cu, (hipStream_t)stream);
     return e == hipSuccess ? MBQ_OK : hip_fail(e);
 }
 
@@ -299,19 +313,31 @@ int mbq_decode_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_
     return e == hipSuccess ? MBQ_OK : hip_fail(e);
 }
 
+// CUs the fused walk's plan is sized for: the current device's, or the
+// MI355X's 256 when no device is visible (sizing queries work without one).
+static int plan_cus() {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return 256;
+    int n_cu = 0;
+    return device_cus(&n_cu) == MBQ_OK && n_cu > 0 ? n_cu : 256;
+}
+
+// The sequence workspace holds two disjoint regions: the fused walk's (plan,
+// statistics, tagged copies, partials; none when the fused walk rejects the
+// list) and after it the unfused form's (quantised activations, scales and
+// the linears' self-clearing counters).  Either form can therefore run on a
+// workspace the other has used.
+static int64_t fused_region_bytes(const mbq_op *ops, int32_t n_ops, const int64_t *widths, int32_t n_bufs,
+                                  int64_t M) {
+    const int64_t f = build_sequence_plan(ops, n_ops, nullptr, widths, n_bufs, M, plan_cus(), nullptr, nullptr);
+    return f > 0 ? align256(f) : 0;
+}
+
 int64_t mbq_sequence_workspace_bytes(const mbq_op *ops, int32_t n_ops, const int64_t *buf_widths,
                                      int32_t n_bufs, int64_t M) {
     const int64_t unfused = analyse_program(ops, n_ops, buf_widths, n_bufs, M, nullptr);
     if (unfused < 0) return unfused;
-    int n_cu = 256;                                  // without a device: the MI355X's CU count
-    if (hipGetDeviceCount(&n_cu) == hipSuccess && n_cu > 0) {
-        if (device_cus(&n_cu) != MBQ_OK) n_cu = 256;
-    } else {
-        n_cu = 256;
-    }
-    // a list the fused walk rejects still runs unfused
-    const int64_t fused = build_sequence_plan(ops, n_ops, nullptr, buf_widths, n_bufs, M, n_cu, nullptr, nullptr);
-    return fused > unfused ? fused : unfused;
+    return fused_region_bytes(ops, n_ops, buf_widths, n_bufs, M) + unfused;
 }
 
 static std::atomic<uint32_t> g_generation{0};
@@ -333,9 +359,7 @@ int mbq_sequence_prepare(const mbq_op *ops, int32_t n_ops, void *const *bufs, co
     if (pre < 0) return (int)pre;
     int st = check_device();
     if (st) return st;
-    int n_cu = 0;
-    st = device_cus(&n_cu);
-    if (st) return st;
+    const int n_cu = plan_cus();
     SeqBuild b;
     const int64_t need = build_sequence_plan(ops, n_ops, bufs, buf_widths, n_bufs, M, n_cu, (uint8_t *)ws, &b);
     if (need < 0) return (int)need;
@@ -398,8 +422,10 @@ int mbq_layer_sequence_unfused(const mbq_op *ops, int32_t n_ops, void *const *bu
                                int64_t ws_bytes, void *stream) {
     if (!bufs) return MBQ_ERR_NULL;
     std::vector<Phase> phases;
-    const int64_t need = analyse_program(ops, n_ops, buf_widths, n_bufs, M, &phases);
-    if (need < 0) return (int)need;
+    const int64_t unfused = analyse_program(ops, n_ops, buf_widths, n_bufs, M, &phases);
+    if (unfused < 0) return (int)unfused;
+    const int64_t base = fused_region_bytes(ops, n_ops, buf_widths, n_bufs, M);
+    const int64_t need = base + unfused;
     for (int32_t b = 0; b < n_bufs; ++b) {
         if (!bufs[b]) return MBQ_ERR_NULL;
         if (!aligned(bufs[b], 16)) return MBQ_ERR_ALIGN;
@@ -411,9 +437,10 @@ int mbq_layer_sequence_unfused(const mbq_op *ops, int32_t n_ops, void *const *bu
     hipStream_t hs = (hipStream_t)stream;
     int64_t k_max = 0;
     for (int32_t i = 0; i < n_ops; ++i) k_max = ops[i].K > k_max ? ops[i].K : k_max;
-    int8_t *q = (int8_t *)ws;
-    float *s = (float *)((char *)ws + align256(M * k_max));
-    void *lin_ws = (char *)ws + align256(M * k_max) + 256;
+    char *region = (char *)ws + base;
+    int8_t *q = (int8_t *)region;
+    float *s = (float *)(region + align256(M * k_max));
+    void *lin_ws = region + align256(M * k_max) + 256;
     for (const Phase &p : phases) {
         const mbq_op &o0 = ops[p.first];
         const bool swiglu = o0.prologue == MBQ_PRO_SWIGLU_QUANT;

@@ -200,8 +200,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void linear_kernel(
     if (lane == 0) store_shared(&counters[rb], 0u);
 }
 
-// Exact int32 group sums for the tests: one wave per tile.
-template <int BITS, int M>
+// Exact int32 group sums for the tests: one wave per tile, through the same
+// tile functions the product runs.  MFMA = true: mfma_tile_regs, the form of
+// the per-op linear (every M) and of the fused walk from two rows on, with
+// the activation halves loaded exactly as the linear loads them; false:
+// group_sums_dot, the v_dot4 form of the fused walk at one row.
+template <int BITS, int M, bool MFMA>
 __global__ __launch_bounds__(64) void group_acc_kernel(const uint8_t *__restrict__ packed,
                                                        const int8_t *__restrict__ q,
                                                        int32_t *__restrict__ acc_out, int N, int K) {
@@ -213,22 +217,30 @@ __global__ __launch_bounds__(64) void group_acc_kernel(const uint8_t *__restrict
     v4i w[L::kSlabs];
     v2u sb;
     load_tile<BITS>(packed + (int64_t)tile * L::kTileBytes, lane, w, sb);
-    int acc[4][M];
+    if constexpr (MFMA) {
+        const int am = (lane & 15) < M ? (lane & 15) : 0;
+        const v4i *qrow = reinterpret_cast<const v4i *>(q + (int64_t)am * K + (lane >> 4) * 32);
+        v4i acc[4];
+        mfma_tile_regs<BITS>(w, *gptr(qrow + g * 8), *gptr(qrow + g * 8 + 1), acc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) {
+            const int m = 4 * (lane >> 4) + j;
+            if (m >= M) continue;
 #pragma unroll
-        for (int m = 0; m < M; ++m) acc[i][m] = 0;
-    const int *qg = reinterpret_cast<const int *>(q) + g * 32 + (lane >> 4) * 8;
-    const int kdw = K >> 2;
-    dot_tile<BITS, M>(w, [&](int m, int d) { return qg[m * kdw + d]; }, acc);
-    const int n = rb * 64 + slice_row(lane);
+            for (int i = 0; i < 4; ++i) {
+                const int n = rb * 64 + 4 * (lane & 15) + i;
+                if (n < N) acc_out[((int64_t)m * N + n) * G + g] = acc[i][j] >> L::kAccShift;
+            }
+        }
+    } else {
+        const int *qg = reinterpret_cast<const int *>(q) + g * 32 + (lane >> 4) * 8;
+        const int kdw = K >> 2;
+        int gs[M];
+        group_sums_dot<BITS, M>(w, [&](int m, int d) { return qg[m * kdw + d]; }, gs);
+        const int n = rb * 64 + slice_row(lane);
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-        int f[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = acc[i][m];
-        const int v = slice_reduce(f);
-        if (n < N) acc_out[((int64_t)m * N + n) * G + g] = v >> L::kAccShift;
+        for (int m = 0; m < M; ++m)
+            if (n < N) acc_out[((int64_t)m * N + n) * G + g] = gs[m] >> L::kAccShift;
     }
 }
 
@@ -260,21 +272,23 @@ hipError_t launch_linear_bits(int64_t M, int64_t N, int64_t K, const int8_t *q, 
     return hipGetLastError();
 }
 
-template <int BITS>
-hipError_t launch_group_acc_bits(int64_t M, int64_t N, int64_t K, const int8_t *q, const void *packed,
+template <int BITS, bool MFMA>
+hipError_t launch_group_acc_form(int64_t M, int64_t N, int64_t K, const int8_t *q, const void *packed,
                                  int32_t *acc, hipStream_t st) {
     const dim3 grid((unsigned)(row_blocks(N) * (K / kGroup)));
     const uint8_t *p = (const uint8_t *)packed;
+#define MBQ_GA(MM) group_acc_kernel<BITS, MM, MFMA><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K)
     switch (M) {
-        case 1: group_acc_kernel<BITS, 1><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
-        case 2: group_acc_kernel<BITS, 2><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
-        case 3: group_acc_kernel<BITS, 3><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
-        case 4: group_acc_kernel<BITS, 4><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
-        case 5: group_acc_kernel<BITS, 5><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
-        case 6: group_acc_kernel<BITS, 6><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
-        case 7: group_acc_kernel<BITS, 7><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
-        default: group_acc_kernel<BITS, 8><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K); break;
+        case 1: MBQ_GA(1); break;
+        case 2: MBQ_GA(2); break;
+        case 3: MBQ_GA(3); break;
+        case 4: MBQ_GA(4); break;
+        case 5: MBQ_GA(5); break;
+        case 6: MBQ_GA(6); break;
+        case 7: MBQ_GA(7); break;
+        default: MBQ_GA(8); break;
     }
+#undef MBQ_GA
     return hipGetLastError();
 }
 
@@ -309,10 +323,13 @@ hipError_t launch_linear(int bits, int64_t M, int64_t N, int64_t K, const int8_t
                      : launch_linear_bits<6>(M, N, K, q, s, packed, y, y_stride, ws, plan, st);
 }
 
-hipError_t launch_group_acc(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q,
+hipError_t launch_group_acc(int bits, bool mfma, int64_t M, int64_t N, int64_t K, const int8_t *q,
                             const void *packed, int32_t *acc, hipStream_t st) {
-    return bits == 4 ? launch_group_acc_bits<4>(M, N, K, q, packed, acc, st)
-                     : launch_group_acc_bits<6>(M, N, K, q, packed, acc, st);
+    if (bits == 4)
+        return mfma ? launch_group_acc_form<4, true>(M, N, K, q, packed, acc, st)
+                    : launch_group_acc_form<4, false>(M, N, K, q, packed, acc, st);
+    return mfma ? launch_group_acc_form<6, true>(M, N, K, q, packed, acc, st)
+                : launch_group_acc_form<6, false>(M, N, K, q, packed, acc, st);
 }
 
 }  // namespace mbq

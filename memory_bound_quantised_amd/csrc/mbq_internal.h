@@ -245,19 +245,26 @@ __device__ __forceinline__ v4i unpack_half(const v4i (&w)[Layout<BITS>::kSlabs],
     }
 }
 
-// acc[i][j] (output lanes 0..15 only) = group sums of weight row 4 * lane + i
-// against activation row j; qa points at the lane's 32 activation bytes
-// (row (lane & 15) of the group's k slice lane >> 4).
+// acc[i][j] = group sum (2^kAccShift * w times q, exact int32) of weight
+// row 4 * (lane & 15) + i of the tile against activation row 4 * (lane >> 4)
+// + j; a0 / a1 are the lane's two 16-byte halves of its 32-k activation slice
+// (row lane & 15 of the group's k slice lane >> 4).  This is the one
+// matrix-core implementation: the per-op linear, the fused walk and the
+// group-sum test entry point all call it.
 template <int BITS>
-__device__ __forceinline__ void mfma_tile(const v4i (&w)[Layout<BITS>::kSlabs], const int8_t *qa, v4i (&acc)[4]) {
-    const v4i a0 = *reinterpret_cast<const v4i *>(qa);
-    const v4i a1 = *reinterpret_cast<const v4i *>(qa + 16);
+__device__ __forceinline__ void mfma_tile_regs(const v4i (&w)[Layout<BITS>::kSlabs], v4i a0, v4i a1,
+                                               v4i (&acc)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const v4i z = {0, 0, 0, 0};
         acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, unpack_half<BITS>(w, i, 0), z, 0, 0, 0);
         acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, unpack_half<BITS>(w, i, 1), acc[i], 0, 0, 0);
     }
+}
+// The same with the lane's activation slice read from memory at qa.
+template <int BITS>
+__device__ __forceinline__ void mfma_tile(const v4i (&w)[Layout<BITS>::kSlabs], const int8_t *qa, v4i (&acc)[4]) {
+    mfma_tile_regs<BITS>(w, *reinterpret_cast<const v4i *>(qa), *reinterpret_cast<const v4i *>(qa + 16), acc);
 }
 
 template <int BITS, int M, typename Act>
@@ -269,17 +276,6 @@ __device__ __forceinline__ void dot_tile(const v4i (&w)[Layout<BITS>::kSlabs], A
 }
 
 // The lane's slabs and its four rows' fp16 scales (packed in two dwords).
-// The same product with the lane's activation slice already in registers.
-template <int BITS>
-__device__ __forceinline__ void mfma_tile_regs(const v4i (&w)[Layout<BITS>::kSlabs], v4i a0, v4i a1,
-                                               v4i (&acc)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const v4i z = {0, 0, 0, 0};
-        acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, unpack_half<BITS>(w, i, 0), z, 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, unpack_half<BITS>(w, i, 1), acc[i], 0, 0, 0);
-    }
-}
 template <int BITS>
 __device__ __forceinline__ void load_tile(const uint8_t *tile, int lane, v4i (&w)[Layout<BITS>::kSlabs],
                                           v2u &scales) {
@@ -381,5 +377,25 @@ __device__ __forceinline__ T slice_reduce(const T (&f)[4]) {
     return swap16_sum(g0, g1);             // even 16-lane rows keep g0, odd keep g1
 }
 __device__ __forceinline__ int slice_row(int lane) { return 4 * (lane & 15) + (lane >> 4); }
+
+// The v_dot4 form of a tile's group sums: lane l ends with gs[m] = the exact
+// int32 group sum (2^kAccShift * w times q over the group's 128 k) of weight
+// row slice_row(l) against activation row m.  The four k slices' sums are
+// added in int32 before any scaling, so the value is the same exact integer
+// the matrix-core form produces.
+template <int BITS, int M, typename Act>
+__device__ __forceinline__ void group_sums_dot(const v4i (&w)[Layout<BITS>::kSlabs], Act act, int (&gs)[M]) {
+    int acc[4][M];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[i][m] = 0;
+    dot_tile<BITS, M>(w, act, acc);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int f[4] = {acc[0][m], acc[1][m], acc[2][m], acc[3][m]};
+        gs[m] = slice_reduce(f);
+    }
+}
 
 }  // namespace mbq

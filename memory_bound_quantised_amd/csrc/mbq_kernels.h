@@ -88,8 +88,12 @@ LinearPlan plan_linear(int bits, int64_t M, int64_t N, int64_t K);
 hipError_t launch_linear(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,
                          const void *packed, void *y, int64_t y_stride, void *ws, const LinearPlan &plan,
                          hipStream_t st);
-hipError_t launch_group_acc(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q,
+// Exact int32 group sums through the matrix-core (mfma) or v_dot4 tile form.
+hipError_t launch_group_acc(int bits, bool mfma, int64_t M, int64_t N, int64_t K, const int8_t *q,
                             const void *packed, int32_t *acc, hipStream_t st);
+
+// HBM stream-read ceiling (ceiling.hip): one pass over bytes (a multiple of 1 KiB).
+hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink, int n_cu, hipStream_t st);
 
 // Fused decode-step walk (persistent kernel).
 struct SeqBuild {

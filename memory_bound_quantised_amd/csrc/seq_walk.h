@@ -200,15 +200,31 @@ __device__ void external_stats(const SeqPlan *P, int w, int waves, int lane, uin
 
 // ---------------------------------------------------------------- phase prologue (workgroup-wide)
 
-template <int M>
-constexpr int stat_batch() { return M < 3 ? 4 : (M < 5 ? 2 : 1); }   // stats records per lane per round trip
-// Input words (2 columns each) per thread per round trip.  Five or more rows
-// take half batches: with full ones the bit-6 walks of seven and eight rows
-// were seen to hand over wrong values for rows 0-3 of the first phase, a
-// failure whose cause was not found (it came and went with unrelated changes
-// to the kernel's code), and which half batches have not shown.
-template <int M>
-constexpr int x_batch() { return M < 5 ? 4 : 2; }
+// ---------------------------------------------------------------- vector-memory budget
+//
+// A wave's outstanding vector-memory instructions (loads and stores) are
+// tracked by a counter whose waits encode at most 63: with more in flight a
+// wait for a given load can return before that load has landed.  Every point
+// where a wave waits on a load must therefore see at most 63 in flight.  At
+// the phase entry a wave still has its primed weight ring (ring_depth tiles of
+// kSlabs + 1 loads each) and the next phase's metadata (kMetaIters loads) in
+// flight; wave 0 adds a batch of statistics records (3M loads per record per
+// lane), and every wave a batch of input words (M loads per word, plus one
+// for the norm weights of a weighted RMSNorm).  The batch sizes are derived
+// from that budget, at most 4.
+constexpr int kVmemLimit = 63;
+
+template <int BITS, int M>
+constexpr int ring_depth_of();
+template <int BITS, int M>
+constexpr int entry_inflight() { return ring_depth_of<BITS, M>() * (Layout<BITS>::kSlabs + 1) + kMetaIters; }
+constexpr int batch_within(int free_slots, int per_item) {
+    return free_slots / per_item >= 4 ? 4 : free_slots / per_item;
+}
+template <int BITS, int M>   // stats records per lane per round trip (wave 0)
+constexpr int stat_batch() { return batch_within(kVmemLimit - entry_inflight<BITS, M>(), 3 * M); }
+template <int BITS, int M, bool X>   // input words (2 columns each) per thread per round trip
+constexpr int x_batch() { return batch_within(kVmemLimit - entry_inflight<BITS, M>(), M + (X ? 1 : 0)); }
 
 // int8 code of t at scale s (rinv = 1 / s): rint(t / s) clamped to +-127.
 // The product t * rinv is within two ulps of the correctly rounded quotient,
@@ -224,17 +240,17 @@ __device__ __forceinline__ float quant_code(float t, float s, float rinv, bool r
 // Quantise the workgroup's input words [0, words) (bf16 pairs from column
 // k_lo on) into LDS, polling tagged words until current.  WEIGHTED multiplies
 // by the norm weights before the RMSNorm scaling (x * w exactly, then * r).
-template <int M, bool WEIGHTED>
+template <int BITS, int M, bool WEIGHTED>
 __device__ __forceinline__ void quant_cols(const SeqPlan *P, const Lay &L, const SeqPhase &ph, const SeqWgHead &h,
                                            uint32_t want, int words, bool norm, const float (&s)[M],
                                            const float (&r)[M], const float (&rinv)[M], const bool (&rinv_ok)[M]) {
     const bool tagged_in = ph.in_xt != nullptr;
     const uint64_t *xsrc = ph.in_xt + (h.k_lo >> 1);
-    for (int j0 = 0; j0 < words; j0 += x_batch<M>() * kSeqThreads) {
-        uint64_t xw[x_batch<M>()][M];
-        uint32_t ww[WEIGHTED ? x_batch<M>() : 1];
+    for (int j0 = 0; j0 < words; j0 += x_batch<BITS, M, WEIGHTED>() * kSeqThreads) {
+        uint64_t xw[x_batch<BITS, M, WEIGHTED>()][M];
+        uint32_t ww[WEIGHTED ? x_batch<BITS, M, WEIGHTED>() : 1];
 #pragma unroll
-        for (int u = 0; u < x_batch<M>(); ++u) {
+        for (int u = 0; u < x_batch<BITS, M, WEIGHTED>(); ++u) {
             const int j = j0 + threadIdx.x + u * kSeqThreads;
             if (WEIGHTED) ww[WEIGHTED ? u : 0] = j < words ? *gptr(ph.norm_w + (h.k_lo >> 1) + j) : 0u;
 #pragma unroll
@@ -250,13 +266,13 @@ __device__ __forceinline__ void quant_cols(const SeqPlan *P, const Lay &L, const
             for (;;) {
                 bool stale = false;
 #pragma unroll
-                for (int u = 0; u < x_batch<M>(); ++u)
+                for (int u = 0; u < x_batch<BITS, M, WEIGHTED>(); ++u)
 #pragma unroll
                     for (int m = 0; m < M; ++m)
                         stale |= j0 + (int)threadIdx.x + u * kSeqThreads < words && tag_of(xw[u][m]) != want;
                 if (!wave_any(stale) || gave_up(P, spins)) break;
 #pragma unroll
-                for (int u = 0; u < x_batch<M>(); ++u) {
+                for (int u = 0; u < x_batch<BITS, M, WEIGHTED>(); ++u) {
                     const int j = j0 + threadIdx.x + u * kSeqThreads;
 #pragma unroll
                     for (int m = 0; m < M; ++m)
@@ -266,7 +282,7 @@ __device__ __forceinline__ void quant_cols(const SeqPlan *P, const Lay &L, const
             }
         }
 #pragma unroll
-        for (int u = 0; u < x_batch<M>(); ++u) {
+        for (int u = 0; u < x_batch<BITS, M, WEIGHTED>(); ++u) {
             const int j = j0 + threadIdx.x + u * kSeqThreads;
             if (j >= words) continue;
 #pragma unroll
@@ -300,7 +316,7 @@ __device__ __forceinline__ void quant_cols(const SeqPlan *P, const Lay &L, const
 // contiguous reads keeps the polling traffic small: every workgroup polls at
 // once, and a flood of polls slows every other memory request.  The next
 // phase's metadata is fetched meanwhile.
-template <int M, bool X>
+template <int BITS, int M, bool X>
 __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int p, uint32_t gen, int wg,
                                             float (*s_sh)[kMaxM], float (*r_sh)[kMaxM]) {
     const int lane = threadIdx.x & 63;
@@ -333,7 +349,7 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
             }
             const int64_t stride = cload(&P->stat_stride);
             const uint64_t *stats = cload(&P->stats) + (wg % kStatReplicas) * cload(&P->stat_rep) + ph.in_rec;
-            constexpr int kStatBatch = stat_batch<M>();
+            constexpr int kStatBatch = stat_batch<BITS, M>();
             for (int base = 0; base < ph.in_nrec; base += 64 * kStatBatch) {
                 uint64_t v[kStatBatch][3 * M];
 #pragma unroll
@@ -404,9 +420,9 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
     // weighted RMSNorm: a copy of the loop of its own, so that the others
     // carry none of its registers
     if (X && uniform(weighted ? 1 : 0))
-        quant_cols<M, X>(P, L, ph, h, want, words, norm, s, r, rinv, rinv_ok);
+        quant_cols<BITS, M, X>(P, L, ph, h, want, words, norm, s, r, rinv, rinv_ok);
     else
-        quant_cols<M, false>(P, L, ph, h, want, words, norm, s, r, rinv, rinv_ok);
+        quant_cols<BITS, M, false>(P, L, ph, h, want, words, norm, s, r, rinv, rinv_ok);
     store_meta(L, p + 1, pre);
     __syncthreads();
 }
@@ -452,7 +468,9 @@ __device__ __forceinline__ void gather_sum(const SeqPlan *P, const uint64_t *are
 #pragma unroll
         for (int u = 0; u < B; ++u) {
             if constexpr (PAIR) {
-                if (uniform(c0 + u == split)) {   // wave-uniform: plain blocks pay nothing
+                // only a split inside the range starts the up sums here; a
+                // range ending at the split is all gate sums (handled below)
+                if (uniform(c0 + u == split && c0 + u < c_end)) {   // wave-uniform: plain blocks pay nothing
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
                         tot2[m] = tot[m];
@@ -674,12 +692,27 @@ struct Slot {
 #define MBQ_RING_W6 6
 #endif
 template <int BITS, int M>
-constexpr int ring_depth() {
+constexpr int ring_depth_of() {
     return BITS == 4 ? (M < 4 ? MBQ_RING_W4 : (MBQ_RING_W4 < 6 ? MBQ_RING_W4 : 6))
                      : (M < 4 ? MBQ_RING_W6 : (MBQ_RING_W6 < 5 ? MBQ_RING_W6 : 5));
 }
-static_assert(ring_depth<4, 1>() * (Layout<4>::kSlabs + 1) <= 63, "vmcnt limit");
-static_assert(ring_depth<6, 1>() * (Layout<6>::kSlabs + 1) <= 63, "vmcnt limit");
+template <int BITS, int M>
+constexpr int ring_depth() { return ring_depth_of<BITS, M>(); }
+
+// The budget at every wait point (see kVmemLimit): phase entry with the
+// statistics batch (wave 0) or an input batch (every wave, weighted form
+// included); a finaliser's gather (no ring primed: finalisers gather first)
+// with 32 / M contributions of M words; a non-finaliser priming the ring
+// behind its partial stores (at most M per segment it merges, one segment per
+// wave at a time, plus the stores still in flight).
+template <int BITS, int M, bool X>
+constexpr bool vmem_budget_ok() {
+    return stat_batch<BITS, M>() >= 1 && x_batch<BITS, M, X>() >= 1 &&
+           entry_inflight<BITS, M>() + stat_batch<BITS, M>() * 3 * M <= kVmemLimit &&
+           entry_inflight<BITS, M>() + x_batch<BITS, M, X>() * (M + (X ? 1 : 0)) <= kVmemLimit &&
+           (32 / M) * M <= kVmemLimit &&
+           ring_depth_of<BITS, M>() * (Layout<BITS>::kSlabs + 1) + kMaxM <= kVmemLimit;
+}
 
 // Issue side: a cursor over the wave's run list.  Everything here is
 // wave-uniform and read with scalar loads.
@@ -854,6 +887,7 @@ __device__ __forceinline__ void stream_phase(const Lay &L, Issue &is, int lane, 
 template <int BITS, int M, bool X>
 __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const SeqPlan *__restrict__ P, uint32_t *err,
                                                           uint32_t gen) {
+    static_assert(vmem_budget_ok<BITS, M, X>(), "a wait point could see more than 63 vector-memory ops in flight");
     __shared__ float s_sh[2][kMaxM];
     __shared__ float r_sh[2][kMaxM];
     __shared__ float c_sh[kSeqWaves * (X ? 2 : 1) * M * 64];   // shared gathers of a finaliser
@@ -900,7 +934,7 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const SeqPlan *__restr
     // to stay resident in the instruction cache, which two CUs share.
     prime<BITS, D, 0, D>(is, lane, meta_head(L, 0)->tiles[wi], ring);
     for (int p = 0;; ++p) {
-        enter_phase<M, X>(P, L, p, gen, wg, s_sh, r_sh);
+        enter_phase<BITS, M, X>(P, L, p, gen, wg, s_sh, r_sh);
         stream_phase<BITS, M, D>(L, is, lane, uniform(meta_head(L, p)->tiles[wi]), ring, facc, lp_w);
         leave_phase<M>(P, L, p, gen);
         // Finalisers hand the phase over while their memory queue is empty;

@@ -137,6 +137,11 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     std::vector<int> last_writer(n_bufs, -1);
     struct Ext { int buf, buf2; int64_t K; const void *w; int64_t rec, xt; int n_rb, rb_first; };
     std::vector<Ext> ext;
+    // Buffers some phase reads as an input written before the walk.  Phases
+    // read such an input with plain loads when they enter, and the walk has no
+    // ordering between that read and a write by a later, unrelated phase, so
+    // an op that overwrites one of them is refused (the unfused call runs it).
+    std::vector<char> ext_read(n_bufs, 0);
     for (int p = 0; p < n_ph; ++p) {
         const mbq_op &o0 = ops[ph[p].first];
         const bool swiglu = o0.prologue == MBQ_PRO_SWIGLU_QUANT;
@@ -169,8 +174,11 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
                 e = (int)ext.size() - 1;
             }
             in_ext[p] = e;
+            ext_read[o0.in_buf] = 1;
+            if (buf2 >= 0) ext_read[buf2] = 1;
         }
         for (int i = ph[p].first; i < ph[p].first + ph[p].count; ++i) {
+            if (ext_read[ops[i].out_buf]) return MBQ_ERR_PROGRAM;
             phase_of[i] = p;
             last_writer[ops[i].out_buf] = i;
         }
@@ -333,6 +341,33 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
         for (int wg = 0; wg * kSeqWaves < g.W; ++wg) {
             const int t0 = g.start(wg * kSeqWaves), t1 = g.start(std::min((wg + 1) * kSeqWaves, g.W)) - 1;
             if (t1 >= t0) seg_cap = std::max(seg_cap, g.segment(t1) - g.segment(t0) + 1);
+        }
+    }
+    // Outputs are written with plain stores by the workgroup that finalises
+    // each row block, and two phases' finalisers need not be ordered (nothing
+    // may wait for an output no op reads).  A buffer written by several ops
+    // is therefore accepted only when every row block of it is finalised by
+    // the same workgroup each time: one workgroup, one L2, program order.
+    {
+        std::vector<std::vector<int>> rb_fin(n_ph);
+        for (int p = 0; p < n_ph; ++p) {
+            rb_fin[p].assign(geo[p].R, -1);
+            for (size_t u = 0; u < units[p].size(); ++u) {
+                rb_fin[p][units[p][u].rb] = unit_fin[p][u];
+                if (units[p][u].rb2 >= 0) rb_fin[p][units[p][u].rb2] = unit_fin[p][u];
+            }
+        }
+        std::vector<int> first_writer(n_bufs, -1);
+        for (int i = 0; i < n_ops; ++i) {
+            const int b = ops[i].out_buf, j = first_writer[b];
+            if (j < 0) {
+                first_writer[b] = i;
+                continue;
+            }
+            const int pi = phase_of[i], pj = phase_of[j];
+            const int bi = rb_base[pi][i - ph[pi].first], bj = rb_base[pj][j - ph[pj].first];
+            for (int64_t r = 0; r < row_blocks(ops[i].N); ++r)
+                if (rb_fin[pi][bi + r] != rb_fin[pj][bj + r]) return MBQ_ERR_PROGRAM;
         }
     }
     const int blk_bytes = (int)up(sizeof(SeqWgHead) + seg_cap * sizeof(SeqWgSeg) + fin_cap * sizeof(SeqFin), 16);

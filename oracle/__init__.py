@@ -57,6 +57,7 @@ def _load():
         lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_to_f64.restype = ctypes.c_double
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_w4_code.argtypes = [P, I64]
         lib.oracle_w6_code.argtypes = [P, I64]
         _lib = lib
@@ -133,6 +134,11 @@ def linear(bits: int, q: np.ndarray, s: np.ndarray, canon: np.ndarray, scales: n
 def num_threads() -> int:
     """OpenMP threads the oracle's loops run on."""
     return int(_load().oracle_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """Run later oracle calls on n OpenMP threads (timing only; results do not depend on it)."""
+    _load().oracle_set_threads(int(n))
 
 
 def f64_to_bf16(v: float) -> int:

@@ -294,6 +294,9 @@ int oracle_decode_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int
 /* Threads the OpenMP loops above use (reported with CPU timings). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 
+/* Threads for later calls (the CPU-baseline timing runs on all cores and on one). */
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 /* Exposed for the tests of the number formats. */
 uint16_t oracle_f64_to_bf16(double v) { return f64_to_bf16(v); }
 double oracle_f16_to_f64(uint16_t h) { return f16_to_f64(h); }

@@ -78,8 +78,19 @@ def test_linear_argument_validation():
     assert f(1, 4096, 4096, A, A, A, A, None, ws_need, None) == -5          # no workspace
     assert L.mbq_w6a8_linear(1, 64, 128, A, A, A, A, A + 8, 1 << 30, None) == -4   # ws alignment
     assert L.mbq_linear_workspace_bytes(7, 1, 64, 128) == -3
-    assert L.mbq_linear_group_acc(5, 1, 64, 128, A, A, A, None) == -3
-    assert L.mbq_linear_group_acc(4, 1, 64, 128, None, A, A, None) == -1
+    assert L.mbq_linear_group_acc(5, 1, 1, 64, 128, A, A, A, None) == -3
+    assert L.mbq_linear_group_acc(4, 1, 1, 64, 128, None, A, A, None) == -1
+    assert L.mbq_linear_group_acc(4, 2, 1, 64, 128, A, A, A, None) == -2    # no such tile form
+    assert L.mbq_linear_group_acc(4, 0, 9, 64, 128, A, A, A, None) == -2
+
+
+def test_stream_read_validation():
+    L = mbq.lib()
+    assert L.mbq_stream_read(None, 1024, A, None) == -1
+    assert L.mbq_stream_read(A, 1024, None, None) == -1
+    assert L.mbq_stream_read(A, 0, A, None) == -2
+    assert L.mbq_stream_read(A, 1000, A, None) == -2          # not whole KiB
+    assert L.mbq_stream_read(A + 16, 1024, A, None) == -4     # buffer not 256-aligned
 
 
 def test_quant_and_pack_validation():
@@ -185,6 +196,38 @@ def test_sequence_fused_dataflow_rules():
         need = L.mbq_sequence_workspace_bytes(prog, len(ops), W, 6, 2)
         assert need > 0, name          # the unfused walk takes every one of them
         st = L.mbq_sequence_prepare(prog, len(ops), bufs, W, 6, 2, A, need, None, ctypes.byref(info))
+        assert (st != -6) == ok, f"{name}: status {st}"
+        assert st != 0, name
+
+
+def test_sequence_fused_buffer_hazards():
+    """Op lists whose buffer reuse the fused walk cannot order are refused by it
+    (MBQ_ERR_PROGRAM before any device call) and still accepted by the unfused
+    walk: an op overwriting a buffer an earlier phase read as an input from
+    before the walk, and one buffer written through two different finaliser
+    mappings.  Buffers: 0 x [256]; 1 y [512]; 2 w [256]; 3 v [256]."""
+    L = mbq.lib()
+    W = (ctypes.c_int64 * 4)(256, 512, 256, 256)
+    bufs = (ctypes.c_void_p * 4)(*([A] * 4))
+    info = mbq.MbqSequenceInfo()
+    cases = {
+        # x is read from before the walk by the first phase, then overwritten
+        "write after an external read": ([_op(4, 1, 512, 256, 0, 1), _op(4, 0, 256, 256, 2, 0)], False),
+        # y written first as the first op of its phase, later as the second:
+        # its row blocks go to other finalising workgroups the second time
+        "rewrite through other finalisers": ([_op(4, 1, 512, 256, 0, 1), _op(4, 1, 256, 256, 0, 2),
+                                              _op(4, 0, 256, 256, 2, 3), _op(4, 0, 512, 256, 2, 1)], False),
+        # the same rewrite with the same position in its phase is ordered
+        "rewrite through the same finalisers": ([_op(4, 1, 512, 256, 0, 1), _op(4, 1, 256, 256, 0, 2),
+                                                 _op(4, 0, 512, 256, 2, 1), _op(4, 0, 256, 256, 2, 3)], True),
+        # a buffer written in the walk and read back by later phases is fine
+        "produced then consumed": ([_op(4, 1, 256, 256, 0, 2), _op(4, 0, 512, 256, 2, 1)], True),
+    }
+    for name, (ops, ok) in cases.items():
+        prog = _program(ops)
+        need = L.mbq_sequence_workspace_bytes(prog, len(ops), W, 4, 1)
+        assert need > 0, name          # the unfused walk takes every one of them
+        st = L.mbq_sequence_prepare(prog, len(ops), bufs, W, 4, 1, A, need, None, ctypes.byref(info))
         assert (st != -6) == ok, f"{name}: status {st}"
         assert st != 0, name
 

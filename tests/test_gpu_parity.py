@@ -154,30 +154,56 @@ def test_pack_pads_rows_with_zeros(bits):
 
 
 # ---------------------------------------------------------------- exact integer sums
+#
+# mbq_linear_group_acc runs the product's own tile functions: FORM_MFMA is the
+# matrix-core tile of the per-op linears (every M) and of the walk from M = 2,
+# FORM_DOT4 the v_dot4 tile of the walk at M = 1.  Both must give the exact
+# integer sums.
 
+FORMS = [mbq.FORM_DOT4, mbq.FORM_MFMA]
+
+
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("bits", [4, 6])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("N,K", [(64, 128), (200, 1152)])
-def test_group_acc_bit_exact(bits, M, N, K):
+def test_group_acc_bit_exact(bits, M, N, K, form):
     canon, S = synth.weights(bits, N, K, seed=11 + N)
     x = synth.activations(M, K, seed=5)
     q, _ = oracle.quantize_act(x)
-    acc = mbq.linear_group_acc(bits, dev(q), packed_on_device(bits, canon, S, N, K), N)
+    acc = mbq.linear_group_acc(bits, dev(q), packed_on_device(bits, canon, S, N, K), N, form=form)
     assert np.array_equal(host(acc), oracle.group_acc(bits, q, canon))
 
 
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("bits", [4, 6])
-def test_group_acc_extreme_codes(bits):
-    # every weight at the most negative code and every activation at -127:
-    # the largest group sums the format allows (130048 for W4, 520192 for W6)
-    N, K, M = 64, 256, 4
-    lo = -8 if bits == 4 else -32
+@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("N,K", [(5120, 17408), (17408, 5120), (16384, 5120)])
+def test_group_acc_bit_exact_full_27b_shapes(bits, M, N, K, form):
+    """The 27B-shaped matrices at full size: every group sum of every row."""
+    canon, S = synth.weights(bits, N, K, seed=N + K + bits)
+    x = synth.activations(M, K, seed=17 + M)
+    q, _ = oracle.quantize_act(x)
+    acc = mbq.linear_group_acc(bits, dev(q), packed_on_device(bits, canon, S, N, K), N, form=form)
+    assert np.array_equal(host(acc), oracle.group_acc(bits, q, canon))
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("bits", [4, 6])
+@pytest.mark.parametrize("lo_code,q_val", [(True, -127), (True, 127), (False, 127), (False, -127)])
+def test_group_acc_extreme_codes(bits, form, lo_code, q_val):
+    # every weight at the most negative (or most positive) code and every
+    # activation at +-127: the largest group sums the format allows
+    # (|sum| up to 130048 for W4, 520192 for W6), with both signs
+    N, K, M = 64, 256, 8
+    code = (-8 if bits == 4 else -32) if lo_code else (7 if bits == 4 else 31)
     from tests.codes import pack
-    canon = pack(bits, np.full((N, K), lo))
+    canon = pack(bits, np.full((N, K), code))
     S = np.ones((N, K // 128), np.float16)
-    q = np.full((M, K), -127, np.int8)
-    acc = mbq.linear_group_acc(bits, dev(q), packed_on_device(bits, canon, S, N, K), N)
-    assert np.all(host(acc) == 128 * 127 * -lo)
+    q = np.full((M, K), q_val, np.int8)
+    acc = host(mbq.linear_group_acc(bits, dev(q), packed_on_device(bits, canon, S, N, K), N, form=form))
+    assert np.all(acc == 128 * q_val * code)
+    assert np.array_equal(acc, oracle.group_acc(bits, q, canon))
 
 
 # ---------------------------------------------------------------- the linear
@@ -308,15 +334,42 @@ def test_layer_sequence_teacher_forced_small(bits, M, fused):
         assert_close_bf16(bufs[o["out_buf"]], ref, o["name"])
 
 
+def _bf16_steps(b):
+    """bf16 bit patterns -> integers ordered like the values (+0 and -0 equal)."""
+    b = b.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def _gpu_swiglu(g_bits, u_bits):
+    """The gated values h = bf16(silu(g) * u) as the GPU computes them (fp32, the
+    library's expf), from the per-op SwiGLU quantisation kernel, which runs the
+    same device function on the same bytes as the walk's gate/up finalisers."""
+    import torch
+    h = torch.zeros(g_bits.shape, dtype=torch.bfloat16, device="cuda")
+    mbq.quantize_act(dev(g_bits), up=dev(u_bits), h_out=h)
+    return host(h)
+
+
 def _oracle_op_rows(bits, bufs, o, mats, rows=None):
-    """Oracle outputs of op o from the walk's own input buffers (teacher forced)."""
+    """Oracle outputs of op o from the walk's own input buffers (teacher forced).
+
+    A SwiGLU op is teacher-forced at its gated input: the GPU evaluates silu in
+    fp32 and the oracle in fp64, so h may differ by one bf16 step, and a code
+    flipped by that step moves an output with heavy cancellation by more than
+    the linear's tolerance.  The oracle therefore quantises the GPU's h (pinned
+    here to the fp64 definition within one bf16 step) and runs the linear on
+    it; the quantisation of a given h is bit-exact on both sides."""
     x = np.ascontiguousarray(bufs[o["in_buf"]][:, :o["K"]])
-    u = (np.ascontiguousarray(bufs[o["in_buf2"]][:, :o["K"]])
-         if o["prologue"] == oracle.PRO_SWIGLU_QUANT else None)
     canon, S = mats[o["matrix"]]
     if rows is not None:
         canon, S = canon[rows], S[rows]
-    return oracle.op(bits, x, o["prologue"], canon, S, o.get("norm_w"), u)
+    if o["prologue"] == oracle.PRO_SWIGLU_QUANT:
+        u = np.ascontiguousarray(bufs[o["in_buf2"]][:, :o["K"]])
+        h = _gpu_swiglu(x, u)
+        d = np.abs(_bf16_steps(h) - _bf16_steps(oracle.swiglu_bf16(x, u)))
+        assert d.max() <= 1, f"{o['name']}: gated input {int(d.max())} bf16 steps from the fp64 definition"
+        return oracle.op(bits, h, oracle.PRO_QUANT, canon, S)
+    return oracle.op(bits, x, o["prologue"], canon, S, o.get("norm_w"), None)
 
 
 @pytest.mark.parametrize("fused", [True, False])
@@ -392,17 +445,32 @@ def test_layer_sequence_9b_layers_teacher_forced(bits, M):
         assert_close_bf16(bufs[o["out_buf"]][:, rows], ref, o["name"])
 
 
-@pytest.mark.parametrize("M", [1, 3, 8])
-def test_layer_sequence_27b_layer_teacher_forced(M):
-    """One 27B-shaped layer: q is 16384 wide and o reads its first 8192 columns."""
-    ops, mats, bufs, _ = _run_sequence(4, synth.layer_shapes_27b, 1, M, distinct=True)
+@pytest.mark.parametrize("bits,M", [(4, 1), (4, 2), (4, 3), (4, 4), (4, 8), (6, 1), (6, 3), (6, 4)])
+def test_layer_sequence_27b_layer_teacher_forced(bits, M):
+    """One 27B-shaped layer (W4 over the M = 1..4 sweep and M = 8; W6 at M = 1, 3
+    and 4): q is 16384 wide and o reads its first 8192 columns."""
+    ops, mats, bufs, _ = _run_sequence(bits, synth.layer_shapes_27b, 1, M, distinct=True)
     rng = np.random.default_rng(5)
     for o in ops:
         x = np.ascontiguousarray(bufs[o["in_buf"]][:, :o["K"]])
         canon, S = mats[o["matrix"]]
         rows = sample_rows(rng, o["N"], 128)
-        ref = oracle_rows(4, x, o["prologue"], canon, S, rows)
+        ref = oracle_rows(bits, x, o["prologue"], canon, S, rows)
         assert_close_bf16(bufs[o["out_buf"]][:, rows], ref, o["name"])
+
+
+@pytest.mark.parametrize("bits,M", [(4, 1), (4, 2), (4, 3), (4, 4), (4, 8), (6, 3), (6, 4)])
+def test_layer_sequence_27b_layer_swiglu_dataflow(bits, M):
+    """The same layer through the walk's other kernel form: weighted RMSNorms in
+    front of q/k/v and gate/up, the SwiGLU gate in front of down.  From M = 3 on
+    a finalising workgroup's waves share each gate/up pair's gather, and a
+    share can end exactly where the gate's contributions end and the up's
+    begin (equal counts): that share holds gate sums only."""
+    ops, mats, bufs, _ = _run_sequence(bits, synth.layer_shapes_27b, 1, M, distinct=True, dataflow="swiglu")
+    rng = np.random.default_rng(8)
+    for o in ops:
+        rows = sample_rows(rng, o["N"], 128)
+        assert_close_bf16(bufs[o["out_buf"]][:, rows], _oracle_op_rows(bits, bufs, o, mats, rows), o["name"])
 
 
 @pytest.mark.parametrize("bits", [4, 6])
@@ -446,3 +514,33 @@ def test_layer_sequence_bench_configuration(M):
         assert_close_bf16(bufs[o["out_buf"]][:, rows], ref, o["name"])
     for b in bufs:
         assert np.all(np.isfinite(synth.bf16_bits_to_f32(b)))
+
+
+@pytest.mark.parametrize("bits", [4, 6])
+def test_fused_and_unfused_walks_share_one_workspace(bits):
+    """The fused walk, then the unfused one, then the fused one again, all on one
+    workspace: the two forms use disjoint regions of it, so each run matches the
+    oracle (teacher forced) and the fused plan survives the unfused run."""
+    import torch
+    M = 3
+    ops, widths = synth.layer_program(_small_shapes, 2, distinct_buffers=True)
+    mats, dev_ops = {}, []
+    for o in ops:
+        mats[o["matrix"]] = synth.weights(bits, o["N"], o["K"], seed=1 + o["matrix"])
+        dev_ops.append(dict(bits=bits, prologue=o["prologue"], N=o["N"], K=o["K"], in_buf=o["in_buf"],
+                            out_buf=o["out_buf"], packed=packed_on_device(bits, *mats[o["matrix"]], o["N"], o["K"])))
+    bufs = [torch.zeros((M, w), dtype=torch.bfloat16, device="cuda") for w in widths]
+    x0 = synth.activations(M, widths[0])
+    fused = mbq.LayerSequence(dev_ops, bufs, M, fused=True)
+    unfused = mbq.LayerSequence(dev_ops, bufs, M, fused=False, ws=fused.ws)
+    for seq in (fused, unfused, fused, unfused):
+        for b in bufs:
+            b.zero_()
+        bufs[0].copy_(dev(x0))
+        seq.run()
+        if seq.fused:
+            seq.check()
+        torch.cuda.synchronize()
+        hb = [host(b) for b in bufs]
+        for o in ops:
+            assert_close_bf16(hb[o["out_buf"]], _oracle_op_rows(bits, hb, o, mats), o["name"])
