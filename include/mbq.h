@@ -174,6 +174,21 @@ int mbq_w6a8_linear(int64_t M, int64_t N, int64_t K, const int8_t *q, const floa
                     const void *packed, void *y_bf16, void *ws, int64_t ws_bytes,
                     void *stream);
 
+/* The same linear for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument.  Its split-K counters and partials live in an array of
+ * 8 MiB + 64 KiB inside the library's device code (one per GPU it runs on,
+ * held until the process ends), which holds the scratch of every supported
+ * shape; the first call on a device looks up that array and zeroes its
+ * counters with a small kernel on `stream`, and every completed call leaves
+ * them zero again.  The call itself allocates nothing.  All calls on one GPU
+ * share the array, so calls that overlap in time on one GPU (different
+ * streams, not synchronised) race.  bits is 4 or 6; other arguments and
+ * results as mbq_w4a8_linear.  Returns MBQ_ERR_WORKSPACE if a shape ever
+ * needed more scratch than the array holds. */
+int mbq_linear_noalloc(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,
+                       const void *packed, void *y_bf16, void *stream);
+
 /* The exact int32 group sums acc[m][n][g] (device int32 [M][N][K/128]) that the
  * linears rescale, for tests.  `form` picks the tile code that produces them,
  * each being the very function the product runs:

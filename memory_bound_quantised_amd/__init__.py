@@ -29,7 +29,7 @@ EXPORTS = ["mbq_status_string", "mbq_last_hip_error", "mbq_version", "mbq_packed
            "mbq_w6a8_linear", "mbq_linear_group_acc", "mbq_sequence_workspace_bytes",
            "mbq_sequence_prepare", "mbq_sequence_run", "mbq_sequence_check", "mbq_layer_sequence",
            "mbq_layer_sequence_unfused", "mbq_attention_workspace_bytes", "mbq_decode_attention",
-           "mbq_stream_read"]
+           "mbq_stream_read", "mbq_linear_noalloc"]
 
 
 class MbqError(RuntimeError):
@@ -99,6 +99,7 @@ def lib() -> ctypes.CDLL:
         L.mbq_sequence_run.argtypes = [P, P, P]
         L.mbq_sequence_check.argtypes = [P, P]
         L.mbq_stream_read.argtypes = [P, I64, P, P]
+        L.mbq_linear_noalloc.argtypes = [ctypes.c_int, I64, I64, I64, P, P, P, P, P]
         for name in EXPORTS:
             if name not in ("mbq_status_string", "mbq_last_hip_error", "mbq_version",
                             "mbq_packed_bytes", "mbq_linear_workspace_bytes",
@@ -252,6 +253,15 @@ def linear(bits: int, q, s, packed, N: int, ws=None, out=None):
     fn = lib().mbq_w4a8_linear if bits == 4 else lib().mbq_w6a8_linear
     _check("mbq_w%da8_linear" % bits, fn(M, N, K, _ptr(q), _ptr(s), _ptr(packed), _ptr(out),
                                          _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def linear_noalloc(bits: int, q, s, packed, N: int, out):
+    """The linear on the library's own device scratch (mbq_linear_noalloc): no
+    workspace; out is a caller-provided bf16 [M][N] tensor."""
+    M, K = q.shape
+    _check("mbq_linear_noalloc", lib().mbq_linear_noalloc(bits, M, N, K, _ptr(q), _ptr(s), _ptr(packed),
+                                                          _ptr(out), _stream()))
     return out
 
 

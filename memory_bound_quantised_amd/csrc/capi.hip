@@ -218,6 +218,20 @@ int mbq_w6a8_linear(int64_t M, int64_t N, int64_t K, const int8_t *q, const floa
     return linear_common(6, M, N, K, q, s, packed, y_bf16, ws, ws_bytes, stream);
 }
 
+int mbq_linear_noalloc(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,
+                       const void *packed, void *y_bf16, void *stream) {
+    if (!bits_ok(bits)) return MBQ_ERR_BITS;
+    if (!q || !s || !packed || !y_bf16) return MBQ_ERR_NULL;
+    if (!m_ok(M) || !n_ok(N) || !k_ok(K)) return MBQ_ERR_SHAPE;
+    if (!aligned(packed, 256) || !aligned(q, 16) || !aligned(s, 4) || !aligned(y_bf16, 16)) return MBQ_ERR_ALIGN;
+    if (plan_linear(bits, M, N, K).ws_bytes > noalloc_scratch_bytes()) return MBQ_ERR_WORKSPACE;
+    int st = check_device();
+    if (st) return st;
+    hipError_t he = hipSuccess;
+    st = linear_noalloc(bits, M, N, K, q, s, packed, y_bf16, (hipStream_t)stream, &he);
+    return st == MBQ_ERR_HIP ? hip_fail(he) : st;
+}
+
 int mbq_linear_group_acc(int bits, int form, int64_t M, int64_t N, int64_t K, const int8_t *q,
                          const void *packed, int32_t *acc, void *stream) {
     if (!bits_ok(bits)) return MBQ_ERR_BITS;

@@ -84,6 +84,27 @@ def test_linear_argument_validation():
     assert L.mbq_linear_group_acc(4, 0, 9, 64, 128, A, A, A, None) == -2
 
 
+def test_linear_noalloc_validation():
+    """Argument checks of the allocation-free linear, all before any device call."""
+    L = mbq.lib()
+    f = L.mbq_linear_noalloc
+    assert f(5, 1, 4096, 4096, A, A, A, A, None) == -3                  # bits
+    assert f(4, 1, 4096, 4096, None, A, A, A, None) == -1               # null q
+    assert f(4, 1, 4096, 4096, A, A, A, None, None) == -1               # null y
+    assert f(4, 9, 4096, 4096, A, A, A, A, None) == -2                  # M = 9
+    assert f(4, 1, 4096, 4000, A, A, A, A, None) == -2                  # K % 128
+    assert f(4, 1, 4096, 4096, A, A, A + 16, A, None) == -4             # packed not 256-aligned
+    # the library's array (8 MiB + 64 KiB) holds the split-K scratch of every
+    # supported shape: the planner keeps row blocks x splits below 4096
+    cap = (8 << 20) + (64 << 10)
+    worst = 0
+    for N in [1, 64, 1000, 4096, 5120, 17408, 64 * 2047, 64 * 2048, 1 << 20]:
+        for K in [128, 1024, 4096, 17408, 1 << 20, 1 << 24]:
+            for bits in (4, 6):
+                worst = max(worst, L.mbq_linear_workspace_bytes(bits, 8, N, K))
+    assert 0 < worst <= cap
+
+
 def test_stream_read_validation():
     L = mbq.lib()
     assert L.mbq_stream_read(None, 1024, A, None) == -1
