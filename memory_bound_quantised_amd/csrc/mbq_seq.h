@@ -7,29 +7,32 @@
 
 namespace mbq {
 
-constexpr int kSeqWaves = 4;                   // waves per workgroup
-constexpr int kSeqThreads = 64 * kSeqWaves;
+constexpr int kSeqWaves = 4;                   // compute waves per workgroup
+constexpr int kSeqThreads = 64 * kSeqWaves;    // their threads (the loaders' come after)
+constexpr int kSeqLoaders = 2;                 // loader waves per workgroup, each feeding kSeqWaves / kSeqLoaders
+constexpr int kSeqFed = kSeqWaves / kSeqLoaders;
+constexpr int kSeqBlock = kSeqThreads + 64 * kSeqLoaders;
 
-// Workgroup roles.  Finalising workgroups gather the partials of row blocks
-// and publish their outputs; the others, once their partials are out, start
-// loading the next phase's weights at once, which keeps the memory busy while
-// the finalisers (whose memory queues are then empty) run the phase hand-over.
-// The dispatcher deals workgroups to the 8 XCDs in turn, so the odd
-// workgroups fill XCDs 1, 3, 5 and 7, and workgroups 3 mod 4 fill XCDs 3 and
-// 7: the hand-over's requests then cross XCDs with no weight loads queued.
-// Up to M = 3 a quarter of the workgroups finalise (their gathers are short),
-// from M = 4 on half of them, and always half in walks with SwiGLU pairs
-// (a pair is two row blocks: a quarter of the grid would take some in turn).
-__host__ __device__ inline bool quarter_finalise(int grid, int M, bool full) { return M <= 3 && !full && grid >= 8; }
+// Every workgroup finalises: the row blocks of a phase are dealt to all
+// workgroups in turn, so each gathers at most a block or two per wave and
+// the hand-over's gathers are spread over the whole chip.  (Weight loads go
+// through the loader waves, so a finalising workgroup's polls queue behind
+// no weight loads of its own compute waves.)
+#ifndef MBQ_FIN_EVERY
+#define MBQ_FIN_EVERY 1   // workgroups wg with wg % MBQ_FIN_EVERY == MBQ_FIN_EVERY - 1 finalise
+#endif
+__host__ __device__ inline bool quarter_finalise(int grid, int M, bool full) { return MBQ_FIN_EVERY > 1; }
 __host__ __device__ inline bool is_final_wg(int wg, int grid, int M, bool full) {
-    if (grid == 1) return true;
-    return quarter_finalise(grid, M, full) ? (wg & 3) == 3 : (wg & 1) != 0;
+    return grid < MBQ_FIN_EVERY || wg % MBQ_FIN_EVERY == MBQ_FIN_EVERY - 1;
 }
 constexpr int kChunkGroups = 8;                // k groups per k chunk (1024 k)
 constexpr int kCounterStride = 32;             // u32 words between phase counters (one 128-B line each)
 constexpr int kStatReplicas = 8;               // copies of the stats records, one per XCD
 constexpr int kMaxPhases = 1000;               // < 2^kRunPhaseBits
 constexpr int kMetaMaxBytes = 4096;           // phase record + workgroup block, per LDS slot
+constexpr int kMaxRingSlots = 16;              // weight-ring tiles per compute wave, at most
+constexpr int kRecBuf = 64;                    // run records the loader buffers per compute wave (LDS)
+constexpr int kRecHalf = kRecBuf / 2;          // read this far ahead, half a buffer at a time
 constexpr uint64_t kPlanMagic = 0x6d62712d73657133ull;  // "mbq-seq3"
 
 // Every value that one wave hands to another travels in a 64-bit word whose
@@ -138,7 +141,7 @@ struct SeqPlan {
     // the kernel that handles them (the other form carries none of their
     // instructions or registers); 0: only the plain and weightless-norm prologues
     int32_t full;
-    int32_t pad;
+    int32_t ring_slots;      // LDS ring slots (tiles) per compute wave
     const SeqPhase *phases;
     const SeqExt *ext;
     uint32_t *err;           // nonzero after a wait gave up

@@ -21,7 +21,7 @@ hipError_t launch_sequence(int bits, int64_t M, bool full, int grid, int lds_byt
                            uint32_t gen, hipStream_t st) {
     void *args[] = {(void *)&plan, (void *)&err, (void *)&gen};
     const void *fn = full ? seq_kernel_full(bits, M) : seq_kernel_plain(bits, M);
-    return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kSeqThreads), args, (unsigned)lds_bytes, st);
+    return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kSeqBlock), args, (unsigned)lds_bytes, st);
 }
 
 }  // namespace mbq

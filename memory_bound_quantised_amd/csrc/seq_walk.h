@@ -11,10 +11,16 @@
 // chunk first keeps the k range a workgroup touches -- and so the activations
 // it quantises into LDS -- to one or two chunks.
 //
-// Dataflow instead of grid barriers: every wave keeps a register ring of
-// tiles in flight across phase boundaries (weights do not depend on
-// activations).  Everything one wave hands to another is a 64-bit word whose
-// high half is an epoch tag, so one load fetches and validates it:
+// Weight stream decoupled from the dataflow: a fifth wave per workgroup, the
+// loader, streams the tiles of the four compute waves into per-wave rings in
+// LDS (LDS-DMA loads, a fixed number of tiles in flight), across phase
+// boundaries and without waiting for anything but ring space, since weights
+// do not depend on activations.  While the compute waves wait for a phase's
+// input, the bus keeps delivering the next tiles.
+//
+// Dataflow instead of grid barriers.  Everything one wave hands to another is
+// a 64-bit word whose high half is an epoch tag, so one load fetches and
+// validates it:
 //   - a wave that finishes part of a row block stores its fp32 partial;
 //   - the owner of the row block's last tile gathers the parts in a fixed
 //     order (bitwise reproducible results), writes the bf16 outputs, a tagged
@@ -74,7 +80,69 @@ struct Lay {
     int grid;
     int n_phases;
     int part_stride;  // contributions per parity half of the partial area
+    int ring_off;     // LDS offset of the weight rings
+    int ring_slots;   // tiles per compute wave's ring
+    int rec_off;      // LDS offset of the loader's run records (kSeqWaves x kRecBuf)
+    int hdr_off;      // LDS offset of the per-slot run headers (kSeqWaves x kMaxRingSlots words)
+    // Plan pointers used every phase, read once at kernel start: re-reading
+    // them from the plan costs a scalar-cache round trip at every phase entry.
+    const SeqPhase *phases;
+    const uint8_t *blocks;
+    uint64_t *stats;
+    int64_t stat_stride, stat_rep;
+    uint64_t *partials;
 };
+
+// ---------------------------------------------------------------- LDS control words
+//
+// [0..3] tiles arrived in each compute wave's ring (the loader adds), [4..7]
+// tiles each compute wave has consumed (it stores), [8] barrier arrivals,
+// [9] barrier generation.
+__shared__ uint32_t g_ctl[16];
+constexpr int kCtlArrived = 0, kCtlConsumed = 4, kCtlBarCount = 8, kCtlBarGen = 9;
+
+#define MBQ_LDS __attribute__((address_space(3)))
+__device__ __forceinline__ MBQ_LDS uint32_t *ctl(int i) { return (MBQ_LDS uint32_t *)&g_ctl[i]; }
+__device__ __forceinline__ uint32_t ctl_load(int i) {
+    return __hip_atomic_load(ctl(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void ctl_store(int i, uint32_t v) {
+    __hip_atomic_store(ctl(i), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// The loader's own LDS operations, as inline assembly.  After an LDS-DMA
+// load the compiler waits for every vector-memory operation in flight before
+// each later LDS access it generates (it cannot tell the DMA's destination
+// from other LDS words), which would drain the weight stream at every tile.
+// The loader orders its LDS accesses against its DMA loads itself (a tile is
+// published only after its own wait on the vector-memory counter), so these
+// forms carry no such wait.  A read waits for its own result inside the
+// same block; the outputs are always used.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const MBQ_LDS void *)p;
+}
+__device__ __forceinline__ void lds_add_u32_asm(uint32_t addr, uint32_t v) {
+    asm volatile("ds_add_u32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_write_u32_asm(uint32_t addr, uint32_t v) {
+    asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_read_u32_asm(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+__device__ __forceinline__ v4i lds_read_b128_asm(uint32_t addr) {
+    v4i v;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
+// Wait for this wave's LDS operations (lgkmcnt 0; vector-memory counts untouched).
+__device__ __forceinline__ void lds_done() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 __device__ __forceinline__ float *lds_partials(const Lay &L, int M) { return reinterpret_cast<float *>(g_lds + M * L.qs); }
 __device__ __forceinline__ int8_t *lds_meta(const Lay &L, int p) { return g_lds + L.meta_off + (p & 1) * L.meta_bytes; }
@@ -101,13 +169,18 @@ __device__ __forceinline__ void fetch_meta(const SeqPlan *P, const Lay &L, int p
     if (p >= L.n_phases) return;
     constexpr int kPhDw = (int)(sizeof(SeqPhase) / 4);
     const int n_dw = kPhDw + L.blk_bytes / 4;
-    const uint32_t *ph = reinterpret_cast<const uint32_t *>(cload(&P->phases) + p);
+    const uint32_t *ph = reinterpret_cast<const uint32_t *>(L.phases + p);
     const uint32_t *blk =
-        reinterpret_cast<const uint32_t *>(cload(&P->blocks) + ((int64_t)p * L.grid + wg) * L.blk_bytes);
+        reinterpret_cast<const uint32_t *>(L.blocks + ((int64_t)p * L.grid + wg) * L.blk_bytes);
+    // Every thread loads all kMetaIters words, clamped into the record: a
+    // conditional load into this array makes the compiler copy (and so wait
+    // for) the loaded value at once, which would put a memory round trip at
+    // the start of every phase.  store_meta writes only the words in range.
 #pragma unroll
     for (int it = 0; it < kMetaIters; ++it) {
-        const int i = (int)threadIdx.x + it * kSeqThreads;
-        if (i < n_dw) v[it] = i < kPhDw ? *gptr(ph + i) : *gptr(blk + (i - kPhDw));
+        const int i = min((int)threadIdx.x + it * kSeqThreads, n_dw - 1);
+        const uint32_t *src = i < kPhDw ? ph + i : blk + (i - kPhDw);
+        v[it] = *gptr(src);
     }
 }
 __device__ __forceinline__ void store_meta(const Lay &L, int p, const uint32_t (&v)[kMetaIters]) {
@@ -129,6 +202,68 @@ __device__ __forceinline__ bool gave_up(const SeqPlan *P, int64_t &spins) {
     }
     __builtin_amdgcn_s_sleep(2);
     return false;
+}
+
+// ---------------------------------------------------------------- vector-memory budget
+//
+// A wave's outstanding vector-memory instructions (loads and stores alike)
+// are tracked by a counter whose waits encode at most 63: with more in flight
+// a wait for a given load can return before that load has landed.  Compute
+// waves issue no weight loads (the loader does), but their partial,
+// output and statistics stores can still be in flight when they poll, so
+// every batch of loads first makes room for itself: vm_room<n>() waits until
+// at most 63 - n operations are outstanding.  Batch sizes leave room for the
+// next phase's metadata loads (kMetaIters) and are at most 4.
+constexpr int kVmemLimit = 63;
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (0xF << 8); }
+template <int N>
+__device__ __forceinline__ void vm_room() {
+    static_assert(N >= 1 && N <= kVmemLimit, "a batch must fit the counter");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kVmemLimit - N));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+constexpr int batch_within(int free_slots, int per_item) {
+    return free_slots / per_item >= 4 ? 4 : free_slots / per_item;
+}
+// Statistics records per lane per round trip (wave 0): also at most 24
+// words in flight, which bounds the registers the batch holds (two per word).
+template <int M>
+constexpr int stat_batch() { return batch_within(24, 3 * M) >= 1 ? batch_within(24, 3 * M) : 1; }
+// Input words (2 columns each) per thread per round trip: at most 16 words
+// in flight per thread (the registers a batch holds, two per word).
+template <int M, bool X>
+constexpr int x_batch() { return batch_within(16, M) >= 1 ? batch_within(16, M) : 1; }
+
+// Barrier of the four compute waves (the loader never joins one: it must
+// keep streaming).  LDS executes each wave's operations in order, so every
+// LDS write a wave made before arriving is visible to a wave that has seen
+// the generation change.  Bounded like every other wait.
+__device__ __forceinline__ void cw_sync(const SeqPlan *P) {
+    const int lane = threadIdx.x & 63;
+    lds_done();
+    const uint32_t gen = uniform((int)ctl_load(kCtlBarGen));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    uint32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(ctl(kCtlBarCount), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
+    if (old == kSeqWaves - 1) {
+        if (lane == 0) {
+            ctl_store(kCtlBarCount, 0u);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            ctl_store(kCtlBarGen, gen + 1);
+        }
+    } else {
+        int64_t spins = 0;
+        while (uniform((int)ctl_load(kCtlBarGen)) == (int)gen) {
+            if (++spins > kSpinLimit) {
+                store_shared(P->err, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    lds_done();
 }
 
 // True if any lane of the wave passes true.
@@ -167,6 +302,7 @@ __device__ void external_stats(const SeqPlan *P, int w, int waves, int lane, uin
     uint64_t *stats = cload(&P->stats);
     const int64_t stride = cload(&P->stat_stride), rep = cload(&P->stat_rep);
     for (int b = w; b < n_ext_rb; b += waves) {
+        vm_room<2 * M + 1>();
         int e = 0;
         while (e + 1 < n_ext && b >= cload(ext, e + 1).rb_first) ++e;
         const SeqExt x = cload(ext, e);
@@ -200,32 +336,6 @@ __device__ void external_stats(const SeqPlan *P, int w, int waves, int lane, uin
 
 // ---------------------------------------------------------------- phase prologue (workgroup-wide)
 
-// ---------------------------------------------------------------- vector-memory budget
-//
-// A wave's outstanding vector-memory instructions (loads and stores) are
-// tracked by a counter whose waits encode at most 63: with more in flight a
-// wait for a given load can return before that load has landed.  Every point
-// where a wave waits on a load must therefore see at most 63 in flight.  At
-// the phase entry a wave still has its primed weight ring (ring_depth tiles of
-// kSlabs + 1 loads each) and the next phase's metadata (kMetaIters loads) in
-// flight; wave 0 adds a batch of statistics records (3M loads per record per
-// lane), and every wave a batch of input words (M loads per word, plus one
-// for the norm weights of a weighted RMSNorm).  The batch sizes are derived
-// from that budget, at most 4.
-constexpr int kVmemLimit = 63;
-
-template <int BITS, int M>
-constexpr int ring_depth_of();
-template <int BITS, int M>
-constexpr int entry_inflight() { return ring_depth_of<BITS, M>() * (Layout<BITS>::kSlabs + 1) + kMetaIters; }
-constexpr int batch_within(int free_slots, int per_item) {
-    return free_slots / per_item >= 4 ? 4 : free_slots / per_item;
-}
-template <int BITS, int M>   // stats records per lane per round trip (wave 0)
-constexpr int stat_batch() { return batch_within(kVmemLimit - entry_inflight<BITS, M>(), 3 * M); }
-template <int BITS, int M, bool X>   // input words (2 columns each) per thread per round trip
-constexpr int x_batch() { return batch_within(kVmemLimit - entry_inflight<BITS, M>(), M + (X ? 1 : 0)); }
-
 // int8 code of t at scale s (rinv = 1 / s): rint(t / s) clamped to +-127.
 // The product t * rinv is within two ulps of the correctly rounded quotient,
 // so it rounds to the same integer unless it lies next to a half-integer;
@@ -237,57 +347,91 @@ __device__ __forceinline__ float quant_code(float t, float s, float rinv, bool r
     return fminf(fmaxf(rintf(x), -127.0f), 127.0f);
 }
 
-// Quantise the workgroup's input words [0, words) (bf16 pairs from column
-// k_lo on) into LDS, polling tagged words until current.  WEIGHTED multiplies
-// by the norm weights before the RMSNorm scaling (x * w exactly, then * r).
-template <int BITS, int M, bool WEIGHTED>
-__device__ __forceinline__ void quant_cols(const SeqPlan *P, const Lay &L, const SeqPhase &ph, const SeqWgHead &h,
-                                           uint32_t want, int words, bool norm, const float (&s)[M],
-                                           const float (&r)[M], const float (&rinv)[M], const bool (&rinv_ok)[M]) {
+// Input words of the workgroup's column range: a batch is XB words (two
+// bf16 columns each) per thread, for each of the M rows, tagged 64-bit words
+// from the producer's copy (or plain words of an input written before the
+// walk).  Loading, settling (re-polling stale tags) and quantising are split
+// so that the first batch can be loaded while wave 0 waits for the
+// statistics.
+template <int M, int XB>
+struct Words {
+    uint64_t v[XB][M];
+};
+
+template <int M, int XB>
+__device__ __forceinline__ void issue_words(Words<M, XB> &w, const SeqPhase &ph, const SeqWgHead &h, int j0,
+                                            int words) {
+    vm_room<XB * M>();
     const bool tagged_in = ph.in_xt != nullptr;
     const uint64_t *xsrc = ph.in_xt + (h.k_lo >> 1);
-    for (int j0 = 0; j0 < words; j0 += x_batch<BITS, M, WEIGHTED>() * kSeqThreads) {
-        uint64_t xw[x_batch<BITS, M, WEIGHTED>()][M];
-        uint32_t ww[WEIGHTED ? x_batch<BITS, M, WEIGHTED>() : 1];
+    // unconditional loads of an index clamped into the range (words >= 1): a
+    // conditional load would be waited for at once (see fetch_meta); the
+    // words past the range are never used
 #pragma unroll
-        for (int u = 0; u < x_batch<BITS, M, WEIGHTED>(); ++u) {
+    for (int u = 0; u < XB; ++u) {
+        const int j = min(j0 + (int)threadIdx.x + u * kSeqThreads, words - 1);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            w.v[u][m] = tagged_in ? load_shared(xsrc + (int64_t)m * ph.in_stride2 + j)
+                                  : (uint64_t)*gptr(ph.in + (int64_t)m * ph.in_stride2 + (h.k_lo >> 1) + j);
+    }
+}
+
+template <int M, int XB>
+__device__ __forceinline__ void settle_words(const SeqPlan *P, Words<M, XB> &w, const SeqPhase &ph,
+                                             const SeqWgHead &h, int j0, int words, uint32_t want) {
+    if (ph.in_xt == nullptr) return;
+    const uint64_t *xsrc = ph.in_xt + (h.k_lo >> 1);
+    int64_t spins = 0;
+    for (;;) {
+        bool stale = false;
+#pragma unroll
+        for (int u = 0; u < XB; ++u)
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                stale |= j0 + (int)threadIdx.x + u * kSeqThreads < words && tag_of(w.v[u][m]) != want;
+        if (!wave_any(stale) || gave_up(P, spins)) break;
+        vm_room<XB * M>();
+#pragma unroll
+        for (int u = 0; u < XB; ++u) {
             const int j = j0 + threadIdx.x + u * kSeqThreads;
-            if (WEIGHTED) ww[WEIGHTED ? u : 0] = j < words ? *gptr(ph.norm_w + (h.k_lo >> 1) + j) : 0u;
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                xw[u][m] = 0;
-                if (j < words)
-                    xw[u][m] = tagged_in ? load_shared(xsrc + (int64_t)m * ph.in_stride2 + j)
-                                         : (uint64_t)*gptr(ph.in + (int64_t)m * ph.in_stride2 + (h.k_lo >> 1) + j);
+            for (int m = 0; m < M; ++m)
+                if (j < words && tag_of(w.v[u][m]) != want) w.v[u][m] = load_shared(xsrc + (int64_t)m * ph.in_stride2 + j);
+        }
+    }
+}
+
+// Quantise the workgroup's input words [0, words) (bf16 pairs from column
+// k_lo on) into LDS.  WEIGHTED multiplies by the norm weights before the
+// RMSNorm scaling (x * w exactly, then * r).  With use_first, the first
+// batch is `first`, already issued (and possibly settled).
+template <int M, int XB, bool WEIGHTED, bool PRE>
+__device__ __forceinline__ void quant_cols(const SeqPlan *P, const Lay &L, const SeqPhase &ph, const SeqWgHead &h,
+                                           uint32_t want, int words, bool norm, const float (&s)[M],
+                                           const float (&r)[M], const float (&rinv)[M], const bool (&rinv_ok)[M],
+                                           const Words<M, XB> &first, bool use_first) {
+    for (int j0 = 0; j0 < words; j0 += XB * kSeqThreads) {
+        Words<M, XB> xw;
+        if (PRE && j0 == 0 && use_first) xw = first;
+        else issue_words<M, XB>(xw, ph, h, j0, words);
+        uint32_t ww[WEIGHTED ? XB : 1];
+        if (WEIGHTED) {
+            vm_room<XB>();
+#pragma unroll
+            for (int u = 0; u < XB; ++u) {
+                const int j = min(j0 + (int)threadIdx.x + u * kSeqThreads, words - 1);
+                ww[WEIGHTED ? u : 0] = *gptr(ph.norm_w + (h.k_lo >> 1) + j);
             }
         }
-        if (tagged_in) {
-            int64_t spins = 0;
-            for (;;) {
-                bool stale = false;
+        settle_words<M, XB>(P, xw, ph, h, j0, words, want);
 #pragma unroll
-                for (int u = 0; u < x_batch<BITS, M, WEIGHTED>(); ++u)
-#pragma unroll
-                    for (int m = 0; m < M; ++m)
-                        stale |= j0 + (int)threadIdx.x + u * kSeqThreads < words && tag_of(xw[u][m]) != want;
-                if (!wave_any(stale) || gave_up(P, spins)) break;
-#pragma unroll
-                for (int u = 0; u < x_batch<BITS, M, WEIGHTED>(); ++u) {
-                    const int j = j0 + threadIdx.x + u * kSeqThreads;
-#pragma unroll
-                    for (int m = 0; m < M; ++m)
-                        if (j < words && tag_of(xw[u][m]) != want)
-                            xw[u][m] = load_shared(xsrc + (int64_t)m * ph.in_stride2 + j);
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < x_batch<BITS, M, WEIGHTED>(); ++u) {
+        for (int u = 0; u < XB; ++u) {
             const int j = j0 + threadIdx.x + u * kSeqThreads;
             if (j >= words) continue;
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                const uint32_t pair = (uint32_t)xw[u][m];
+                const uint32_t pair = (uint32_t)xw.v[u][m];
                 uint32_t packed = 0;
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
@@ -322,6 +466,7 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     uint32_t pre[kMetaIters];
+    vm_room<kMetaIters>();
     fetch_meta(P, L, p + 1, wg, pre);
     const SeqPhase ph = *meta_phase(L, p);
     const SeqWgHead h = *meta_head(L, p);
@@ -331,7 +476,16 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
     const int words = (h.k_hi - h.k_lo) >> 1;          // bf16 pairs per activation row
     const bool has = h.k_hi > h.k_lo;
     const bool need_scale = has || h.n_fin > 0;   // finalising rescales by the input scale
+    // The first batch of input words goes out before the statistics poll
+    // (the producer wrote them before its statistics): waves 1..3 settle
+    // theirs while wave 0 polls, wave 0 after.  Up to four rows only: more
+    // would hold too many registers across the wait.
+    constexpr int XB = x_batch<M, X>();
+    constexpr bool kPre = M <= 4;
+    Words<M, XB> xpre;
+    if (kPre && has) issue_words<M, XB>(xpre, ph, h, 0, words);
 
+    if (kPre && has && wave != 0) settle_words<M, XB>(P, xpre, ph, h, 0, words, want);
     if (wave == 0) {
         // the partial area of this phase's parity is free once the phase two back is finalised
         if (ph.wait_n > 0) {
@@ -347,10 +501,11 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
                 ss[m] = 0.0;
                 am[m] = 0.0f;
             }
-            const int64_t stride = cload(&P->stat_stride);
-            const uint64_t *stats = cload(&P->stats) + (wg % kStatReplicas) * cload(&P->stat_rep) + ph.in_rec;
-            constexpr int kStatBatch = stat_batch<BITS, M>();
+            const int64_t stride = L.stat_stride;
+            const uint64_t *stats = L.stats + (wg % kStatReplicas) * L.stat_rep + ph.in_rec;
+            constexpr int kStatBatch = stat_batch<M>();
             for (int base = 0; base < ph.in_nrec; base += 64 * kStatBatch) {
+                vm_room<kStatBatch * 3 * M>();
                 uint64_t v[kStatBatch][3 * M];
 #pragma unroll
                 for (int u = 0; u < kStatBatch; ++u) {
@@ -407,7 +562,7 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
             }
         }
     }
-    __syncthreads();   // the scales from wave 0
+    cw_sync(P);   // the scales from wave 0
     float s[M], r[M], rinv[M];
     bool rinv_ok[M];
 #pragma unroll
@@ -420,11 +575,11 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
     // weighted RMSNorm: a copy of the loop of its own, so that the others
     // carry none of its registers
     if (X && uniform(weighted ? 1 : 0))
-        quant_cols<BITS, M, X>(P, L, ph, h, want, words, norm, s, r, rinv, rinv_ok);
+        quant_cols<M, XB, X, kPre>(P, L, ph, h, want, words, norm, s, r, rinv, rinv_ok, xpre, kPre && has);
     else
-        quant_cols<BITS, M, false>(P, L, ph, h, want, words, norm, s, r, rinv, rinv_ok);
+        quant_cols<M, XB, false, kPre>(P, L, ph, h, want, words, norm, s, r, rinv, rinv_ok, xpre, kPre && has);
     store_meta(L, p + 1, pre);
-    __syncthreads();
+    cw_sync(P);
 }
 
 // ---------------------------------------------------------------- hand-over of a phase
@@ -441,6 +596,7 @@ __device__ __forceinline__ void gather_sum(const SeqPlan *P, const uint64_t *are
     for (int m = 0; m < M; ++m) tot[m] = tot2[m] = 0.0f;
     constexpr int B = 32 / M;   // contributions per round trip (within the vector-memory counter)
     for (int c0 = c_begin; c0 < c_end; c0 += B) {
+        vm_room<B * M>();
         uint64_t v[B][M];
 #pragma unroll
         for (int u = 0; u < B; ++u) {
@@ -561,6 +717,7 @@ __device__ __forceinline__ void emit_rb_full(const SeqFin &f, uint32_t tag, cons
         }
     }
     if (uniform(f.norm_w != nullptr ? 1 : 0)) {   // the consumer's weights scale the maxima
+        vm_room<1>();
         const float wv = lane < f.stat_rows ? bf16_bits_to_f32(*gptr(f.norm_w + lane)) : 0.0f;
 #pragma unroll
         for (int m = 0; m < M; ++m) ya[m] = yv[m] * wv;   // exact: both factors are bf16
@@ -573,13 +730,13 @@ __device__ __forceinline__ void emit_rb_full(const SeqFin &f, uint32_t tag, cons
 // order) and publish one tagged partial per (segment, workgroup).
 template <int M>
 __device__ __forceinline__ void leave_phase(const SeqPlan *P, const Lay &L, int p, uint32_t gen) {
-    __syncthreads();
+    cw_sync(P);
     const SeqWgHead h = *meta_head(L, p);
     const int lane = threadIdx.x & 63;
     const int j = uniform(threadIdx.x >> 6);
     const uint32_t tag = make_tag(gen, p);
     const float *lp = lds_partials(L, M) + lane;
-    uint64_t *area = cload(&P->partials) + (int64_t)(p & 1) * L.part_stride * 64 * M;
+    uint64_t *area = L.partials + (int64_t)(p & 1) * L.part_stride * 64 * M;
     for (int e = j; e < h.n_seg; e += kSeqWaves) {
         const SeqWgSeg sg = meta_seg(L, p)[e];
         float v[M];
@@ -613,9 +770,9 @@ __device__ __forceinline__ void finalize_phase(const SeqPlan *P, const Lay &L, i
     const int lane = threadIdx.x & 63;
     const int j = uniform(threadIdx.x >> 6);
     const uint32_t tag = make_tag(gen, p);
-    const uint64_t *area = cload(&P->partials) + (int64_t)(p & 1) * L.part_stride * 64 * M;
+    const uint64_t *area = L.partials + (int64_t)(p & 1) * L.part_stride * 64 * M;
     uint32_t *fin_count = meta_phase(L, p)->fin_count;
-    const int64_t stat_stride = cload(&P->stat_stride), stat_rep = cload(&P->stat_rep);
+    const int64_t stat_stride = L.stat_stride, stat_rep = L.stat_rep;
     constexpr int B = 32 / M;
     bool share = false;
     // at M = 1 one round trip holds 32 contributions: the shared form stays out
@@ -646,7 +803,7 @@ __device__ __forceinline__ void finalize_phase(const SeqPlan *P, const Lay &L, i
                 c_sh[((j * NS + 0) * M + m) * 64 + lane] = tot[m];
                 if constexpr (X) c_sh[((j * NS + 1) * M + m) * 64 + lane] = tot2[m];
             }
-            __syncthreads();   // every wave passes here exactly once
+            cw_sync(P);   // every wave passes here exactly once
             if (part != 0) break;
 #pragma unroll
             for (int m = 0; m < M; ++m) tot[m] = tot2[m] = 0.0f;
@@ -679,65 +836,209 @@ struct Slot {
     uint32_t hdr;   // the run header if this tile opens a run, else 0
 };
 
-// Tiles in flight per wave.  A wave can have at most 63 vector loads
-// outstanding and a tile takes kSlabs + 1 of them; the ring stays well below
-// that: the in-flight bytes of the whole grid only need to cover the memory
-// latency, and every byte beyond that lengthens the queue that the phase
-// hand-over's own requests wait in.  M = 4 trims it to stay within 512
-// registers (vector plus accumulation registers).
-#ifndef MBQ_RING_W4
-#define MBQ_RING_W4 8
+// Tiles each loader keeps in flight (the CU's two loaders together): enough
+// bytes per CU for the bus to stay busy (about 32-40 KiB per CU reached the
+// stream ceiling), few enough that a poll from the same CU is not queued
+// behind a long line of weight loads.
+// The window also fixes the vector-memory wait after each tile, so it must
+// stay within the 63-op counter: (tiles - 1) x loads per tile <= 63.
+#ifndef MBQ_LOADER_TILES_W4
+#define MBQ_LOADER_TILES_W4 4
 #endif
-#ifndef MBQ_RING_W6
-#define MBQ_RING_W6 6
+#ifndef MBQ_LOADER_TILES_W6
+#define MBQ_LOADER_TILES_W6 3
 #endif
-template <int BITS, int M>
-constexpr int ring_depth_of() {
-    return BITS == 4 ? (M < 4 ? MBQ_RING_W4 : (MBQ_RING_W4 < 6 ? MBQ_RING_W4 : 6))
-                     : (M < 4 ? MBQ_RING_W6 : (MBQ_RING_W6 < 5 ? MBQ_RING_W6 : 5));
+template <int BITS>
+constexpr int loader_window() { return BITS == 4 ? MBQ_LOADER_TILES_W4 : MBQ_LOADER_TILES_W6; }
+template <int BITS>
+constexpr int loads_per_tile() { return Layout<BITS>::kSlabs + 1; }
+static_assert((loader_window<4>() - 1) * loads_per_tile<4>() <= kVmemLimit, "loader window within vmcnt");
+static_assert((loader_window<6>() - 1) * loads_per_tile<6>() <= kVmemLimit, "loader window within vmcnt");
+constexpr int kLdsDmaNt = 2;
+// Offset of a tile's LDS/global base from its start: the slabs and scales lie
+// within +-kDmaMid of it, inside the instruction offset's range (+-4 KiB).
+template <int BITS>
+constexpr int kDmaMid = BITS == 4 ? 2048 : 3072;
+static_assert(Layout<4>::kWeightBytes - kDmaMid<4> < 4096 && Layout<6>::kWeightBytes - kDmaMid<6> < 4096,
+              "DMA offsets within range");
+// The tile's scales (128 bytes at kWeightBytes) on lanes 0..7, same base.
+template <int BITS>
+__device__ __forceinline__ void dma_scales(const uint8_t *g16, int8_t *dst) {
+    constexpr int kOff = Layout<BITS>::kWeightBytes - kDmaMid<BITS>;
+    __builtin_amdgcn_global_load_lds((const MBQ_GLOBAL void *)g16, (MBQ_LDS void *)dst, 16, kOff, kLdsDmaNt);
 }
-template <int BITS, int M>
-constexpr int ring_depth() { return ring_depth_of<BITS, M>(); }
+// Slab J.. of a tile from g16 (the lane's address at the tile's base) into
+// LDS at dst (the slot's base); the instruction offset must be a constant.
+template <int BITS, int J>
+__device__ __forceinline__ void dma_slabs(const uint8_t *g16, int8_t *dst) {
+    if constexpr (J < Layout<BITS>::kSlabs) {
+        __builtin_amdgcn_global_load_lds((const MBQ_GLOBAL void *)g16, (MBQ_LDS void *)dst, 16,
+                                         J * kSlab - kDmaMid<BITS>, kLdsDmaNt);
+        dma_slabs<BITS, J + 1>(g16, dst);
+    }
+}   // cache policy of the LDS-DMA loads: non-temporal
 
-// The budget at every wait point (see kVmemLimit): phase entry with the
-// statistics batch (wave 0) or an input batch (every wave, weighted form
-// included); a finaliser's gather (no ring primed: finalisers gather first)
-// with 32 / M contributions of M words; a non-finaliser priming the ring
-// behind its partial stores (at most M per segment it merges, one segment per
-// wave at a time, plus the stores still in flight).
-template <int BITS, int M, bool X>
-constexpr bool vmem_budget_ok() {
-    return stat_batch<BITS, M>() >= 1 && x_batch<BITS, M, X>() >= 1 &&
-           entry_inflight<BITS, M>() + stat_batch<BITS, M>() * 3 * M <= kVmemLimit &&
-           entry_inflight<BITS, M>() + x_batch<BITS, M, X>() * (M + (X ? 1 : 0)) <= kVmemLimit &&
-           (32 / M) * M <= kVmemLimit &&
-           ring_depth_of<BITS, M>() * (Layout<BITS>::kSlabs + 1) + kMaxM <= kVmemLimit;
-}
-
-// Issue side: a cursor over the wave's run list.  Everything here is
-// wave-uniform and read with scalar loads.
-struct Issue {
-    const SeqRun *runs;
-    int next;              // next run to open
-    int left;              // tiles left in the open run
-    const uint8_t *src;    // next tile
+// Position in a compute wave's LDS ring.
+struct RingPos {
+    int gt;         // tiles of this wave consumed so far (all phases)
+    int slot;       // ring slot of tile gt
+    int arrived;    // last arrival count read
 };
 
-// Load the wave's next tile into slot s.
+// Read the wave's next tile and its run header from its ring (waiting for
+// the loader if needed), then hand the slot back.
 template <int BITS>
-__device__ __forceinline__ void issue(Issue &is, int lane, Slot<BITS> &s) {
-    uint32_t hdr = 0;
-    if (is.left == 0) {
-        const SeqRun r = cload(is.runs, is.next);
-        ++is.next;
-        is.src = r.src;
-        is.left = (int)r.n;
-        hdr = r.hdr;
+__device__ __forceinline__ void take_tile(const SeqPlan *P, const Lay &L, int wi, int lane, RingPos &rp,
+                                          Slot<BITS> &s) {
+    using Lt = Layout<BITS>;
+    if (rp.arrived <= rp.gt) {
+        int64_t spins = 0;
+        for (;;) {
+            rp.arrived = uniform((int)ctl_load(kCtlArrived + wi));
+            if (rp.arrived > rp.gt) break;
+            if (++spins > kSpinLimit) {   // the loader gave up: carry on with what is there
+                store_shared(P->err, 1u);
+                rp.arrived = rp.gt + 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
     }
-    s.hdr = hdr;
-    load_tile<BITS>(is.src, lane, s.w, s.sc);
-    is.src += Layout<BITS>::kTileBytes;
-    --is.left;
+    const int8_t *t = g_lds + L.ring_off + (wi * L.ring_slots + rp.slot) * Lt::kTileBytes;
+#pragma unroll
+    for (int j = 0; j < Lt::kSlabs; ++j) s.w[j] = *((const MBQ_LDS v4i *)(t + j * kSlab) + lane);
+    s.sc = *((const MBQ_LDS v2u *)(t + Lt::kWeightBytes) + (lane & 15));
+    s.hdr = (uint32_t)uniform((int)*(const MBQ_LDS uint32_t *)(g_lds + L.hdr_off + (wi * kMaxRingSlots + rp.slot) * 4));
+    lds_done();   // the slot's bytes are in registers: the loader may refill it
+    ++rp.gt;
+    rp.slot = rp.slot + 1 == L.ring_slots ? 0 : rp.slot + 1;
+    if (lane == 0) ctl_store(kCtlConsumed + wi, (uint32_t)rp.gt);
+}
+
+// The loader wave: walks the four compute waves' run lists in turn, putting
+// each next tile into its wave's ring as soon as the ring has a free slot,
+// with at most loader_window tiles in flight; a tile is published (arrival
+// count of its wave) once the loads after it leave only the window's newest
+// in flight.  It waits for nothing but ring space and its own loads.
+//
+// The run records come through LDS too: each wave's list is read 32 records
+// ahead with LDS-DMA loads into a 64-record buffer, so opening a run costs an
+// LDS read, not a scalar-cache miss (one such miss, serialised over four
+// waves' lists, stalls the whole stream for a memory round trip).  The
+// loader writes each tile's run header (or 0) next to its ring slot for the
+// compute wave.  A record block is used at least 32 runs after its loads
+// were issued, and every tile after it waits until at most loader_window
+// tiles are in flight, so by then it has landed.
+template <int BITS>
+__device__ void loader(const SeqPlan *P, const Lay &L, int wg, int lane, int w0) {
+    using Lt = Layout<BITS>;
+    constexpr int T = Lt::kTileBytes;
+    constexpr int NL = loads_per_tile<BITS>();
+    constexpr int WT = loader_window<BITS>();
+    static_assert(kRecHalf >= WT, "a record block lands before it is used");
+    const int S = L.ring_slots;
+    const SeqWave *wtab = cload(&P->wtab);
+    const SeqRun *runs0 = cload(&P->runs);
+    const SeqRun *runs[kSeqFed];
+    const uint8_t *src[kSeqFed];
+    uint32_t hdr_next[kSeqFed];
+    int next[kSeqFed], left[kSeqFed], issued[kSeqFed], total[kSeqFed], cons[kSeqFed], slot[kSeqFed];
+    const auto rec_lds = [&](int w, int i) {
+        return (const MBQ_LDS SeqRun *)(g_lds + L.rec_off + ((w0 + w) * kRecBuf + (i & (kRecBuf - 1))) * (int)sizeof(SeqRun));
+    };
+    const auto fetch_records = [&](int w, int first, int n) {   // records [first, first + n) into the buffer
+        if (lane < n)
+            __builtin_amdgcn_global_load_lds((const MBQ_GLOBAL void *)(runs[w] + first + lane),
+                                             (MBQ_LDS void *)(g_lds + L.rec_off +
+                                                              ((w0 + w) * kRecBuf + (first & (kRecBuf - 1))) *
+                                                                  (int)sizeof(SeqRun)),
+                                             16, 0, 0);
+    };
+#pragma unroll
+    for (int w = 0; w < kSeqFed; ++w) {
+        const SeqWave sw = cload(wtab, wg * kSeqWaves + w0 + w);
+        runs[w] = runs0 + sw.run_begin;
+        total[w] = sw.tiles;
+        src[w] = nullptr;
+        hdr_next[w] = 0;
+        next[w] = left[w] = issued[w] = cons[w] = slot[w] = 0;
+        fetch_records(w, 0, kRecBuf);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // Compute wave of each tile in flight, oldest in the low bits: 2 bits per
+    // tile, at most WT <= 32 tiles.
+    static_assert(WT <= 32 && kSeqFed <= 4, "in-flight order fits 64 bits");
+    uint64_t order = 0;
+    int seq = 0, pub = 0;
+    int64_t spins = 0;
+    auto publish_oldest = [&]() {
+        const int wd = (int)(order & 3u);
+        order >>= 2;
+        ++pub;
+        if (lane == 0) lds_add_u32_asm(lds_addr(&g_ctl[kCtlArrived + w0 + wd]), 1u);
+    };
+    for (;;) {
+        bool any = false, pending = false;
+#pragma unroll
+        for (int w = 0; w < kSeqFed; ++w) {
+            if (issued[w] >= total[w]) continue;
+            pending = true;
+            if (issued[w] - cons[w] >= S) {
+                cons[w] = uniform((int)lds_read_u32_asm(lds_addr(&g_ctl[kCtlConsumed + w0 + w])));
+                if (issued[w] - cons[w] >= S) continue;
+            }
+            uint32_t hdr = 0;
+            if (left[w] == 0) {
+                // the record's four dwords (src low, src high, hdr, n), one LDS read
+                const v4i rec = lds_read_b128_asm(lds_addr((const void *)rec_lds(w, next[w])));
+                const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane(rec.x);
+                const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane(rec.y);
+                src[w] = (const uint8_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+                hdr = (uint32_t)__builtin_amdgcn_readfirstlane(rec.z);
+                left[w] = __builtin_amdgcn_readfirstlane(rec.w);
+                ++next[w];
+                if ((next[w] & (kRecHalf - 1)) == 0) fetch_records(w, next[w] + kRecHalf, kRecHalf);
+            }
+            // one LDS base and one address per tile, centred so that every
+            // slab and the scales are within the instruction's offset range;
+            // the offset moves the global and the LDS address alike
+            int8_t *dst = g_lds + L.ring_off + ((w0 + w) * S + slot[w]) * T + kDmaMid<BITS>;
+            const uint8_t *g16 = src[w] + kDmaMid<BITS> + lane * 16;
+            dma_slabs<BITS, 0>(g16, dst);
+            // the 64 rows' fp16 scales: 128 bytes, 16 per lane on 8 lanes (a
+            // narrower load would not do: LDS-DMA places every lane's data at
+            // least a dword apart)
+            if (lane < 8) dma_scales<BITS>(g16, dst);
+            if (lane == 0) lds_write_u32_asm(lds_addr(g_lds + L.hdr_off + ((w0 + w) * kMaxRingSlots + slot[w]) * 4), hdr);
+            src[w] += T;
+            --left[w];
+            ++issued[w];
+            slot[w] = slot[w] + 1 == S ? 0 : slot[w] + 1;
+            order |= (uint64_t)w << (2 * (seq - pub));
+            ++seq;
+            if (seq - pub >= WT) {
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL * (WT - 1)));   // the oldest tile has landed
+                publish_oldest();
+            }
+            any = true;
+        }
+        if (any) {
+            spins = 0;
+            continue;
+        }
+        if (pub < seq) {   // every ring full (or every list done): land and publish the rest
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            while (pub < seq) publish_oldest();
+            continue;
+        }
+        if (!pending) break;
+        if (++spins > kSpinLimit) {   // no compute wave hands a slot back: give up
+            store_shared(P->err, 1u);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 // Park the open run's partial (segment sums of 4 rows x M per lane, reduced
@@ -835,48 +1136,17 @@ __device__ __forceinline__ void compute(const Lay &L, int lane, Compute &c, floa
     c.q += kGroup;
 }
 
-// Start a phase's stream: ring slots [A, B) with the wave's tiles A..B-1 of
-// n that exist (the ring may be primed in two steps).
-// Issue the first min(n, B) - A tiles of a phase into the ring.  Paced
-// priming spaces the tiles ~0.2 us apart: the grid primes all at once when a
-// phase ends, and a burst of that size delays the hand-over's own requests.
-template <int BITS, int D, int A, int B>
-__device__ __forceinline__ void prime(Issue &is, int lane, int n, Slot<BITS> (&ring)[D], bool paced = false) {
-#pragma unroll
-    for (int i = A; i < B; ++i)
-        if (i < n) {
-            issue<BITS>(is, lane, ring[i]);
-            if (paced) __builtin_amdgcn_s_sleep(8);
-        }
-}
-
-// One phase of the wave: n tiles through the ring, which was primed with the
-// first min(n, D).  No load of the next phase is issued here, so the wave's
-// memory queue is empty when the phase's partials go out.  While at least D
-// more tiles follow, every slot is refilled (a fixed load count, so each wait
-// leaves the later tiles in flight); the last two ring rounds refill only
-// what exists.  Nothing is loaded for nothing: even a load that reads no
-// memory costs address-unit time that the hand-over's own requests need.
-template <int BITS, int M, int D>
-__device__ __forceinline__ void stream_phase(const Lay &L, Issue &is, int lane, int n, Slot<BITS> (&ring)[D],
+// One phase of a compute wave: its n tiles from the ring, in run order.
+template <int BITS, int M>
+__device__ __forceinline__ void stream_phase(const SeqPlan *P, const Lay &L, int wi, int lane, RingPos &rp, int n,
                                              float (&facc)[4][acc_rows<M>()], float *lp_w) {
     Compute c;
     c.slot = -1;
     c.q = 0;
-    int i0 = 0;
-    for (; i0 + 2 * D <= n; i0 += D) {
-#pragma unroll
-        for (int i = 0; i < D; ++i) {
-            compute<BITS, M>(L, lane, c, facc, ring[i], lp_w);
-            issue<BITS>(is, lane, ring[i]);
-        }
-    }
-    for (; i0 < n; i0 += D) {
-#pragma unroll
-        for (int i = 0; i < D; ++i) {
-            if (i0 + i < n) compute<BITS, M>(L, lane, c, facc, ring[i], lp_w);
-            if (i0 + i + D < n) issue<BITS>(is, lane, ring[i]);
-        }
+    for (int t = 0; t < n; ++t) {
+        Slot<BITS> s;
+        take_tile<BITS>(P, L, wi, lane, rp, s);
+        compute<BITS, M>(L, lane, c, facc, s, lp_w);
     }
     if constexpr (use_mfma<M>())
         close_segment_mfma<M>(c.slot, facc, lp_w, lane);
@@ -885,9 +1155,8 @@ __device__ __forceinline__ void stream_phase(const Lay &L, Issue &is, int lane, 
 }
 
 template <int BITS, int M, bool X>
-__global__ __launch_bounds__(kSeqThreads) void seq_kernel(const SeqPlan *__restrict__ P, uint32_t *err,
-                                                          uint32_t gen) {
-    static_assert(vmem_budget_ok<BITS, M, X>(), "a wait point could see more than 63 vector-memory ops in flight");
+__global__ __launch_bounds__(kSeqBlock) void seq_kernel(const SeqPlan *__restrict__ P, uint32_t *err,
+                                                        uint32_t gen) {
     __shared__ float s_sh[2][kMaxM];
     __shared__ float r_sh[2][kMaxM];
     __shared__ float c_sh[kSeqWaves * (X ? 2 : 1) * M * 64];   // shared gathers of a finaliser
@@ -909,48 +1178,56 @@ __global__ __launch_bounds__(kSeqThreads) void seq_kernel(const SeqPlan *__restr
     L.part_stride = cload(&P->part_stride);
     L.meta_off = M * L.qs + kSeqWaves * L.slots * M * 64 * 4;
     L.meta_bytes = ((int)sizeof(SeqPhase) + L.blk_bytes + 15) & ~15;
-    const bool finaliser = is_final_wg(wg, L.grid, M, X);
+    L.rec_off = L.meta_off + 2 * L.meta_bytes;
+    L.hdr_off = L.rec_off + kSeqWaves * kRecBuf * (int)sizeof(SeqRun);
+    L.ring_off = L.hdr_off + kSeqWaves * kMaxRingSlots * 4;
+    L.ring_slots = cload(&P->ring_slots);
+    L.phases = cload(&P->phases);
+    L.blocks = cload(&P->blocks);
+    L.stats = cload(&P->stats);
+    L.stat_stride = cload(&P->stat_stride);
+    L.stat_rep = cload(&P->stat_rep);
+    L.partials = cload(&P->partials);
 
-    {   // metadata of the first phase
+    if (threadIdx.x < 16) g_ctl[threadIdx.x] = 0u;
+    if (wi < kSeqWaves) {   // metadata of the first phase
         uint32_t pre[kMetaIters];
         fetch_meta(P, L, 0, wg, pre);
         store_meta(L, 0, pre);
     }
-    external_stats<M>(P, wg * kSeqWaves + wi, L.grid * kSeqWaves, lane, gen);
-    __syncthreads();
+    __syncthreads();   // the only barrier the loader joins
+    if (wi >= kSeqWaves) {
+        loader<BITS>(P, L, wg, lane, (wi - kSeqWaves) * kSeqFed);
+        return;
+    }
 
-    const SeqWave wv = cload(cload(&P->wtab), wg * kSeqWaves + wi);
-    Issue is;
-    is.runs = cload(&P->runs) + wv.run_begin;
-    is.next = 0;
-    is.left = 0;
-    is.src = nullptr;
+    const bool finaliser = is_final_wg(wg, L.grid, M, X);
+    external_stats<M>(P, wg * kSeqWaves + wi, L.grid * kSeqWaves, lane, gen);
+    cw_sync(P);
+
+    RingPos rp;
+    rp.gt = 0;
+    rp.slot = 0;
+    rp.arrived = 0;
     float *lp_w = lds_partials(L, M) + (wi * L.slots * M) * 64;
     float facc[4][acc_rows<M>()];
-    constexpr int D = ring_depth<BITS, M>();
-    Slot<BITS> ring[D];
 
     // One code path per step, each step once per phase: the whole loop has
     // to stay resident in the instruction cache, which two CUs share.
-    prime<BITS, D, 0, D>(is, lane, meta_head(L, 0)->tiles[wi], ring);
     for (int p = 0;; ++p) {
         enter_phase<BITS, M, X>(P, L, p, gen, wg, s_sh, r_sh);
-        stream_phase<BITS, M, D>(L, is, lane, uniform(meta_head(L, p)->tiles[wi]), ring, facc, lp_w);
+        stream_phase<BITS, M>(P, L, wi, lane, rp, uniform(meta_head(L, p)->tiles[wi]), facc, lp_w);
         leave_phase<M>(P, L, p, gen);
-        // Finalisers hand the phase over while their memory queue is empty;
-        // the others start the next phase's weight stream (wave 0 at once,
-        // the rest paced), after a barrier that keeps any wave's loads from
-        // queueing ahead of another wave's partials.
+        // Finalisers hand the phase over; the others go straight on to the
+        // next phase's entry (the loader has been streaming its tiles).
         if (finaliser) finalize_phase<BITS, M, X>(P, L, p, gen, s_sh[p & 1], c_sh);
-        else __syncthreads();
         if (p + 1 == L.n_phases) break;
-        prime<BITS, D, 0, D>(is, lane, uniform(meta_head(L, p + 1)->tiles[wi]), ring, wi != 0);
     }
 
     // The last workgroup to exit clears the counters for the next launch
     // (every wave's counter increments have completed before it counts out).
     wait_memory();
-    __syncthreads();
+    cw_sync(P);
     if (threadIdx.x == 0) {
         uint32_t *cnt = cload(&P->counters);
         if (counter_add(cnt + (int64_t)L.n_phases * kCounterStride, 1u) == (uint32_t)(L.grid - 1))

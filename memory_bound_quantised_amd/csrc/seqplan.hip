@@ -71,8 +71,9 @@ double other_weight(int64_t M, bool quarter) {
         return v > 0.05 && v < 20.0 ? v : 0.0;
     }();
     if (env > 0.0) return env;
-    if (quarter) return 3.0;
-    return M >= 3 ? 2.0 : 1.0;
+    (void)M;
+    // every workgroup finalising: equal shares; a subset finalising streams less
+    return quarter ? 3.0 : 1.0;
 }
 
 }  // namespace
@@ -374,11 +375,19 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     const int fin_off = (int)(sizeof(SeqWgHead) + seg_cap * sizeof(SeqWgSeg));
     if ((int64_t)sizeof(SeqPhase) + blk_bytes > kMetaMaxBytes) return MBQ_ERR_SHAPE;
 
-    // ---- LDS: activations, partial slots, two metadata slots
+    // ---- LDS: activations, partial slots, two metadata slots, then the
+    // compute waves' weight rings in what is left of the CU's 160 KiB (less
+    // the kernel's static LDS: scales, shared-gather sums, control words)
     const int q_stride = (int)up(q_span, 16);
     const int64_t meta_bytes = up(sizeof(SeqPhase) + blk_bytes, 16);
-    const int64_t lds = M * q_stride + (int64_t)kSeqWaves * slots * M * 64 * 4 + 2 * meta_bytes;
-    if (lds > 132 * 1024) return MBQ_ERR_SHAPE;   // plus the kernel's static LDS (up to 17 KB)
+    // ... plus the loader's run-record buffers and the per-slot run headers
+    const int64_t lds_fixed = M * q_stride + (int64_t)kSeqWaves * slots * M * 64 * 4 + 2 * meta_bytes +
+                              (int64_t)kSeqWaves * kRecBuf * (int64_t)sizeof(SeqRun) + kSeqWaves * kMaxRingSlots * 4;
+    const int64_t lds_static = 2 * 2 * kMaxM * 4 + (int64_t)kSeqWaves * (full ? 2 : 1) * M * 64 * 4 + 16 * 4;
+    const int64_t lds_avail = 160 * 1024 - 1024 - lds_static - lds_fixed;   // 1 KiB of slack for alignment
+    const int64_t ring_slots = std::min<int64_t>(kMaxRingSlots, lds_avail / (kSeqWaves * tile_bytes));
+    if (ring_slots < 2) return MBQ_ERR_SHAPE;
+    const int64_t lds = lds_fixed + ring_slots * kSeqWaves * tile_bytes;
 
     // ---- workspace layout
     const int64_t off_err = 0;
@@ -393,7 +402,9 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     const int64_t off_phases = up(off_ext + (int64_t)ext.size() * sizeof(SeqExt), 64);
     const int64_t off_wtab = up(off_phases + (int64_t)n_ph * sizeof(SeqPhase), 64);
     const int64_t off_runs = up(off_wtab + (int64_t)waves * sizeof(SeqWave), 64);
-    const int64_t off_blocks = up(off_runs + n_runs * (int64_t)sizeof(SeqRun), 64);
+    // the loader reads each wave's records up to a buffer (kRecBuf) past its
+    // last run: zero records after the table keep those reads inside it
+    const int64_t off_blocks = up(off_runs + (n_runs + kRecBuf) * (int64_t)sizeof(SeqRun), 64);
     const int64_t total = up(off_blocks + (int64_t)n_ph * grid * blk_bytes, 256);
     if (!out) return total;
 
@@ -423,6 +434,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     plan.seg_cap = seg_cap;
     plan.part_stride = part_stride;
     plan.full = full ? 1 : 0;
+    plan.ring_slots = (int32_t)ring_slots;
     plan.phases = reinterpret_cast<const SeqPhase *>(dev(off_phases));
     plan.ext = reinterpret_cast<const SeqExt *>(dev(off_ext));
     plan.err = reinterpret_cast<uint32_t *>(dev(off_err));
