@@ -175,7 +175,7 @@ __device__ __forceinline__ void fetch_meta(const SeqPlan *P, const Lay &L, int p
     // Every thread loads all kMetaIters words, clamped into the record: a
     // conditional load into this array makes the compiler copy (and so wait
     // for) the loaded value at once, which would put a memory round trip at
-    // the start of every phase.  store_meta writes only the words in range.
+    // the start of every phase.
 #pragma unroll
     for (int it = 0; it < kMetaIters; ++it) {
         const int i = min((int)threadIdx.x + it * kSeqThreads, n_dw - 1);
@@ -183,15 +183,16 @@ __device__ __forceinline__ void fetch_meta(const SeqPlan *P, const Lay &L, int p
         v[it] = *gptr(src);
     }
 }
+// Every word is written, the clamped ones onto the record's last word (which
+// they hold): a loaded word left unwritten on some path would stay pending in
+// the compiler's view, and it would then wait for every memory operation in
+// flight at the next phase's entry.
 __device__ __forceinline__ void store_meta(const Lay &L, int p, const uint32_t (&v)[kMetaIters]) {
     if (p >= L.n_phases) return;
     const int n_dw = (int)(sizeof(SeqPhase) / 4) + L.blk_bytes / 4;
     uint32_t *dst = reinterpret_cast<uint32_t *>(lds_meta(L, p));
 #pragma unroll
-    for (int it = 0; it < kMetaIters; ++it) {
-        const int i = (int)threadIdx.x + it * kSeqThreads;
-        if (i < n_dw) dst[i] = v[it];
-    }
+    for (int it = 0; it < kMetaIters; ++it) dst[min((int)threadIdx.x + it * kSeqThreads, n_dw - 1)] = v[it];
 }
 
 __device__ __forceinline__ bool gave_up(const SeqPlan *P, int64_t &spins) {
