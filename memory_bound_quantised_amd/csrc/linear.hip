@@ -5,9 +5,12 @@
 // matrix; every weight is read once for about one operation, so the kernel is
 // a stream over the packed weights.
 //
-// Work split: each wave owns one row block (64 rows, one per lane) and a
-// contiguous range of its k groups (a "split"), the next tile loading while
-// the current one is summed.  For every 64x128 tile the
+// Two forms.  Split form: each wave owns one row block (64 rows, one per
+// lane) and a contiguous range of its k groups (a "split"), the next tile
+// loading while the current one is summed.  Row-block form (below, for
+// matrices whose row blocks fill the chip in one round): one workgroup per
+// row block, its waves splitting the k groups and adding their sums through
+// LDS, so nothing is combined across workgroups.  For every 64x128 tile the
 // lane unpacks its 128 codes to int8, takes int8 dot products against the
 // activation (wave-uniform, so it is read through the scalar unit and shared
 // by all 64 rows), sums them exactly in int32, and adds the group's
@@ -31,6 +34,15 @@ constexpr int kTargetWaves = 2048;   // about 8 waves per CU on 256 CUs
 #endif
 constexpr int kTilesPerWave = MBQ_LIN_TILES;   // a split's tiles, at least (when the matrix has enough)
 constexpr int kMaxSplits = 16;       // a row block's partials, at most
+#ifndef MBQ_LIN_RB_MIN_BLOCKS
+#define MBQ_LIN_RB_MIN_BLOCKS 48
+#endif
+#ifndef MBQ_LIN_RB_MAX_BLOCKS
+#define MBQ_LIN_RB_MAX_BLOCKS 256
+#endif
+#ifndef MBQ_LIN_RB_MAX_GROUPS
+#define MBQ_LIN_RB_MAX_GROUPS 64
+#endif
 #ifndef MBQ_LIN_MFMA_MIN_M
 #define MBQ_LIN_MFMA_MIN_M 1
 #endif
@@ -200,6 +212,122 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void linear_kernel(
     if (lane == 0) store_shared(&counters[rb], 0u);
 }
 
+// Row-block form: one workgroup of W waves per row block, wave w taking the
+// contiguous k groups [G w / W, G (w + 1) / W),
+// the waves' sums added in wave order through LDS.  No partials leave the
+// workgroup, so no counter or second pass: with enough row blocks to fill
+// the chip this is a single memory round trip deep.  A wave loads up to
+// SHOT tiles all at once; a longer range goes in batches of two through a
+// ping-pong pair of register sets.  Loads are unconditional, at an index
+// clamped into the range, so that none is waited for early; the repeats of
+// the last tile hit the cache and are never summed.
+// (W, SHOT) per shape, measured on 4096 x 4096, 16384 x 5120 and 5120 x 8192
+// (each within its registers without spills):
+//   k groups <= 32: 16 x 2 for W4 up to three rows, else 8 x 4;
+//   more k groups:   4 x 8 (a wave's longer range keeps more tiles in flight).
+template <int BITS>
+constexpr int rb_batch() { return 2; }
+
+template <int BITS, int M, int TB>
+struct RbBatch {
+    v4i w[TB][Layout<BITS>::kSlabs];
+    v2u sc[TB];
+    v4i a0[TB], a1[TB];
+};
+
+template <int BITS, int M, int TB>
+__device__ __forceinline__ void rb_load(RbBatch<BITS, M, TB> &b, const uint8_t *tiles, const v4i *qrow, int gb,
+                                        int g_last, int lane) {
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+        const int g = min(gb + u, g_last);
+        load_tile<BITS>(tiles + (int64_t)g * Layout<BITS>::kTileBytes, lane, b.w[u], b.sc[u]);
+        b.a0[u] = *gptr(qrow + g * 8);
+        b.a1[u] = *gptr(qrow + g * 8 + 1);
+    }
+}
+
+template <int BITS, int M, int TB, int AR>
+__device__ __forceinline__ void rb_sum(const RbBatch<BITS, M, TB> &b, int gb, int g1, float (&facc)[4][AR]) {
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+        if (gb + u < g1) {
+            v4i acc[4];
+            mfma_tile_regs<BITS>(b.w[u], b.a0[u], b.a1[u], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float S = row_scale(b.sc[u], i);
+#pragma unroll
+                for (int j = 0; j < AR; ++j) facc[i][j] = fmaf((float)acc[i][j], S, facc[i][j]);
+            }
+        }
+    }
+}
+
+template <int BITS, int M, int W, int SHOT>
+__global__ __launch_bounds__(64 * W) void linear_rb_kernel(
+    const uint8_t *__restrict__ packed, const int8_t *__restrict__ q, const float *__restrict__ s,
+    uint16_t *__restrict__ y, int64_t y_stride, int N, int K) {
+    using L = Layout<BITS>;
+    constexpr int TB = rb_batch<BITS>();
+    constexpr int AR = M > 4 ? 4 : M;
+    __shared__ float red[W][M][64];
+    const int lane = threadIdx.x & 63;
+    const int w = uniform(threadIdx.x >> 6);
+    const int rb = blockIdx.x;
+    const int G = K >> 7;
+    const int g0 = (int)((int64_t)G * w / W), g1 = (int)((int64_t)G * (w + 1) / W);
+    const uint8_t *tiles = packed + (int64_t)rb * G * L::kTileBytes;
+    // lane l sums weight rows 4 (l & 15) + i for activation rows 4 (l >> 4) + j
+    // (rows past M are computed from row 0 and dropped), as the split form
+    const int am = (lane & 15) < M ? (lane & 15) : 0;
+    const v4i *qrow = reinterpret_cast<const v4i *>(q + (int64_t)am * K + (lane >> 4) * 32);
+    float facc[4][AR];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < AR; ++j) facc[i][j] = 0.0f;
+    if (g1 - g0 > 0 && g1 - g0 <= SHOT) {
+        // every tile of the wave in flight at once, summed in the same branch
+        RbBatch<BITS, M, SHOT> A;
+        rb_load<BITS, M, SHOT>(A, tiles, qrow, g0, g1 - 1, lane);
+        rb_sum<BITS, M, SHOT, AR>(A, g0, g1, facc);
+    } else if (g1 - g0 > SHOT) {
+        RbBatch<BITS, M, TB> A, B;
+        rb_load<BITS, M, TB>(A, tiles, qrow, g0, g1 - 1, lane);
+        {
+            for (int gb = g0;;) {
+                rb_load<BITS, M, TB>(B, tiles, qrow, gb + TB, g1 - 1, lane);
+                rb_sum<BITS, M, TB, AR>(A, gb, g1, facc);
+                gb += TB;
+                if (gb >= g1) break;
+                rb_load<BITS, M, TB>(A, tiles, qrow, gb + TB, g1 - 1, lane);
+                rb_sum<BITS, M, TB, AR>(B, gb, g1, facc);
+                gb += TB;
+                if (gb >= g1) break;
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < AR; ++j) {
+        const int m = 4 * (lane >> 4) + j;
+        if (m < M) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[w][m][4 * (lane & 15) + i] = facc[i][j];
+        }
+    }
+    __syncthreads();
+    const float unscale = 1.0f / (float)(1 << L::kAccShift);   // exact power of two
+    for (int t = threadIdx.x; t < M * 64; t += 64 * W) {
+        const int m = t >> 6, r = t & 63;
+        float tot = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < W; ++ww) tot += red[ww][m][r];
+        const int n = rb * 64 + r;
+        if (n < N) y[m * y_stride + n] = (uint16_t)f32_to_bf16_bits(s[m] * (tot * unscale));
+    }
+}
+
 // Exact int32 group sums for the tests: one wave per tile, through the same
 // tile functions the product runs.  MFMA = true: mfma_tile_regs, the form of
 // the per-op linear (every M) and of the fused walk from two rows on, with
@@ -244,10 +372,40 @@ __global__ __launch_bounds__(64) void group_acc_kernel(const uint8_t *__restrict
     }
 }
 
+template <int BITS, int M>
+void launch_rb(const uint8_t *pk, const int8_t *q, const float *s, uint16_t *y, int64_t y_stride, int64_t N,
+               int64_t K, int64_t n_rb, int64_t groups, hipStream_t st) {
+    const dim3 grid((unsigned)n_rb);
+    if (groups > 32) {
+        linear_rb_kernel<BITS, M, 4, 8><<<grid, dim3(64 * 4), 0, st>>>(pk, q, s, y, y_stride, (int)N, (int)K);
+    } else if constexpr (BITS == 4 && M <= 3) {
+        linear_rb_kernel<BITS, M, 16, 2><<<grid, dim3(64 * 16), 0, st>>>(pk, q, s, y, y_stride, (int)N, (int)K);
+    } else {
+        linear_rb_kernel<BITS, M, 8, 4><<<grid, dim3(64 * 8), 0, st>>>(pk, q, s, y, y_stride, (int)N, (int)K);
+    }
+}
+
 template <int BITS>
 hipError_t launch_linear_bits(int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,
                               const void *packed, void *y, int64_t y_stride, void *ws,
                               const LinearPlan &plan, hipStream_t st) {
+    const uint8_t *pk = (const uint8_t *)packed;
+    uint16_t *yv = (uint16_t *)y;
+    if (plan.rb_form) {
+#define MBQ_RB(MM) launch_rb<BITS, MM>(pk, q, s, yv, y_stride, N, K, plan.n_rb, plan.groups, st)
+        switch (M) {
+            case 1: MBQ_RB(1); break;
+            case 2: MBQ_RB(2); break;
+            case 3: MBQ_RB(3); break;
+            case 4: MBQ_RB(4); break;
+            case 5: MBQ_RB(5); break;
+            case 6: MBQ_RB(6); break;
+            case 7: MBQ_RB(7); break;
+            default: MBQ_RB(8); break;
+        }
+#undef MBQ_RB
+        return hipGetLastError();
+    }
     const int64_t items = plan.n_rb * plan.splits;
     const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock));
     const dim3 block(64 * kWavesPerBlock);
@@ -313,6 +471,12 @@ LinearPlan plan_linear(int bits, int64_t M, int64_t N, int64_t K) {
     if (sp < 1) sp = 1;
     p.splits = sp;
     p.ws_bytes = kCounterBytes + (sp > 1 ? p.n_rb * sp * M * 64 * 4 : 0);
+    // The row-block form where the row blocks fill most of the chip in one
+    // round (a second round of workgroups costs more than the split form's
+    // combine) and each wave's k range is a few tiles (its pipeline is two
+    // batches deep).
+    p.rb_form = p.n_rb >= MBQ_LIN_RB_MIN_BLOCKS && p.n_rb <= MBQ_LIN_RB_MAX_BLOCKS &&
+                p.groups <= MBQ_LIN_RB_MAX_GROUPS;
     return p;
 }
 

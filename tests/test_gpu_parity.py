@@ -219,6 +219,22 @@ def test_linear_vs_oracle(bits, M, N, K):
     assert_close_bf16(host(y), oracle.linear(bits, q, s, canon, S), f"W{bits} M={M} {N}x{K}")
 
 
+# The row-block form of the linear (one workgroup per 64-row block, 48..256
+# blocks, up to 64 k groups): its edges.  3070 x 4224: 48 blocks, the last one
+# 62 rows, 33 groups over 16 or 8 waves (uneven ranges, some past the
+# all-at-once count, so through the batched loop); 16384 x 128: 256 blocks of
+# one group (most waves idle); 3100 x 8192: 64 groups over 4 waves (batched).
+@pytest.mark.parametrize("bits", [4, 6])
+@pytest.mark.parametrize("M", [1, 3, 4, 8])
+@pytest.mark.parametrize("N,K", [(3070, 4224), (16384, 128), (3100, 8192)])
+def test_linear_row_block_form_vs_oracle(bits, M, N, K):
+    canon, S = synth.weights(bits, N, K, seed=N ^ K)
+    x = synth.activations(M, K)
+    q, s = oracle.quantize_act(x)
+    y = mbq.linear(bits, dev(q), dev(s), packed_on_device(bits, canon, S, N, K), N)
+    assert_close_bf16(host(y), oracle.linear(bits, q, s, canon, S), f"W{bits} M={M} {N}x{K}")
+
+
 # Full-size shapes of the 9B- and 27B-shaped decode steps; outputs checked on sampled rows.
 FULL_SHAPES = [(4096, 4096), (1024, 4096), (12288, 4096), (4096, 12288), (16384, 5120),
                (1024, 5120), (5120, 8192), (17408, 5120), (5120, 17408)]
