@@ -757,11 +757,15 @@ __device__ __forceinline__ void leave_phase(const SeqPlan *P, const Lay &L, int 
     }
 }
 
+// Contributions above which the waves of a finaliser with one or two row
+// blocks share each block's gather (the fixed-order sum of the parts).
+constexpr int kShareContribs = 8;
+
 // A finalising workgroup's row blocks of phase p, spread over its waves.
-// With one or two blocks and more contributions than one round trip gathers,
-// 4 / n_fin waves share each block: each sums a contiguous quarter (or half)
-// of its contributions, and the block's first wave adds those sums in wave
-// order (a fixed order, so results stay reproducible) and emits the block.
+// With one or two blocks and more than kShareContribs contributions, 4 / n_fin
+// waves share each block: each sums a contiguous quarter (or half) of its
+// contributions, and the block's first wave adds those sums in wave order (a
+// fixed order, so results stay reproducible) and emits the block.
 // c_sh: kSeqWaves x (X ? 2 : 1) x M x 64 floats of LDS.
 // Inline: a call would wait for every outstanding store on entry and exit.
 template <int BITS, int M, bool X>
@@ -774,15 +778,16 @@ __device__ __forceinline__ void finalize_phase(const SeqPlan *P, const Lay &L, i
     const uint64_t *area = L.partials + (int64_t)(p & 1) * L.part_stride * 64 * M;
     uint32_t *fin_count = meta_phase(L, p)->fin_count;
     const int64_t stat_stride = L.stat_stride, stat_rep = L.stat_rep;
-    constexpr int B = 32 / M;
+    // The choice depends on the plan alone, never on M, so that a row's sums
+    // are added in the same order whatever the number of rows (a walk of M
+    // rows gives each row the bits of that row's own walk).
     bool share = false;
-    // at M = 1 one round trip holds 32 contributions: the shared form stays out
-    if (M > 1 && h.n_fin >= 1 && h.n_fin <= 2)
+    if (h.n_fin >= 1 && h.n_fin <= 2)
         for (int i = 0; i < h.n_fin; ++i) {
             const SeqFin &f = meta_fin(L, p)[i];
-            share |= f.nc + f.nc_2 > B;
+            share |= f.nc + f.nc_2 > kShareContribs;
         }
-    share = M > 1 && uniform(share ? 1 : 0) != 0;
+    share = uniform(share ? 1 : 0) != 0;
     // shared: wave j takes part j % g of block j / g (one pass); else wave j
     // takes blocks j, j + 4, ... whole
     const int g = share ? kSeqWaves / h.n_fin : 1;
@@ -1058,10 +1063,14 @@ __device__ __forceinline__ void close_segment(int slot, float (&facc)[4][M], flo
     }
 }
 
-// Matrix-core products from this many activation rows on (a 16-row product
-// costs one instruction whatever M is; below it, v_dot4 is cheaper).
+// Matrix-core products at every M: each lane accumulates exact int32 group
+// sums of whole rows, so a row's fp32 sum is the same sequence of operations
+// whatever M is (the v_dot4 form sums k slices separately and reduces them at
+// the end, which rounds differently).  A tile's products take a small part of
+// the time its bytes take to arrive, so M = 1 pays nothing measurable for the
+// 16-row instruction.
 #ifndef MBQ_MFMA_MIN_M
-#define MBQ_MFMA_MIN_M 2
+#define MBQ_MFMA_MIN_M 1
 #endif
 template <int M>
 constexpr bool use_mfma() { return M >= MBQ_MFMA_MIN_M; }

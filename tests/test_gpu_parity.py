@@ -296,7 +296,8 @@ def test_linear_workspace_reused_across_shapes():
 
 # ---------------------------------------------------------------- decode-step walk
 
-def _run_sequence(bits, shapes_fn, n_layers, M, distinct, seed_base=0, fused=True, runs=1, dataflow="plain"):
+def _run_sequence(bits, shapes_fn, n_layers, M, distinct, seed_base=0, fused=True, runs=1, dataflow="plain",
+                  x0=None):
     import torch
     ops, widths = synth.layer_program(shapes_fn, n_layers, distinct_buffers=distinct, dataflow=dataflow)
     mats = {}
@@ -317,7 +318,8 @@ def _run_sequence(bits, shapes_fn, n_layers, M, distinct, seed_base=0, fused=Tru
             d["in_buf2"] = o["in_buf2"]
         dev_ops.append(d)
     bufs = [torch.zeros((M, w), dtype=torch.bfloat16, device="cuda") for w in widths]
-    x0 = synth.activations(M, widths[0])
+    if x0 is None:
+        x0 = synth.activations(M, widths[0])
     bufs[0].copy_(dev(x0))
     seq = mbq.LayerSequence(dev_ops, bufs, M, fused=fused)
     outs = []
@@ -511,6 +513,22 @@ def test_layer_sequence_shared_gathers_reproducible(shapes, M, dataflow):
     _, _, outs, _ = _run_sequence(4, fn, 1, M, distinct=True, runs=2, dataflow=dataflow)
     for a, b in zip(outs[0], outs[1]):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("shapes,layers,M,bits,dataflow", [
+    ("small", 3, 3, 4, "plain"), ("small", 3, 8, 6, "swiglu"), ("27b", 1, 3, 4, "plain"), ("9b", 1, 4, 6, "swiglu")])
+def test_layer_sequence_batch_invariant(shapes, layers, M, bits, dataflow, fused):
+    """Row m of an M-row walk is bitwise the walk of that row alone: every
+    intermediate buffer of every layer (the verify rows cost nothing in the
+    quality of what is computed for each of them)."""
+    fn = {"small": _small_shapes, "27b": synth.layer_shapes_27b, "9b": synth.layer_shapes_9b}[shapes]
+    _, _, outs, x0 = _run_sequence(bits, fn, layers, M, distinct=True, fused=fused, dataflow=dataflow)
+    for m in range(M):
+        _, _, one, _ = _run_sequence(bits, fn, layers, 1, distinct=True, fused=fused, dataflow=dataflow,
+                                     x0=x0[m:m + 1])
+        for i, (a, b) in enumerate(zip(outs, one)):
+            assert np.array_equal(a[m:m + 1], b), f"row {m} of buffer {i}"
 
 
 @pytest.mark.parametrize("M", [1, 3])
