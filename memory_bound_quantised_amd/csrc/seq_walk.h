@@ -586,7 +586,7 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
 // ---------------------------------------------------------------- hand-over of a phase
 
 // Sum contributions [c_begin, c_end) of the partial area (lane l's M tagged
-// words of contribution c at area + (c * 64 + l) * M) in their fixed order
+// words of contribution c at area + (c * M + m) * 64 + l) in their fixed order
 // into tot, re-polling stale words.  PAIR: contributions from index split on
 // (a gate block's up partner) go to a fresh sum: the sums before it end up in
 // tot2.
@@ -601,9 +601,9 @@ __device__ __forceinline__ void gather_sum(const SeqPlan *P, const uint64_t *are
         uint64_t v[B][M];
 #pragma unroll
         for (int u = 0; u < B; ++u) {
-            const uint64_t *src = area + ((int64_t)(c0 + u) * 64 + lane) * M;
+            const uint64_t *src = area + (int64_t)(c0 + u) * M * 64 + lane;
 #pragma unroll
-            for (int m = 0; m < M; ++m) v[u][m] = c0 + u < c_end ? load_shared(src + m) : 0;
+            for (int m = 0; m < M; ++m) v[u][m] = c0 + u < c_end ? load_shared(src + m * 64) : 0;
         }
         // re-poll every stale word together: one round trip per round
         int64_t spins = 0;
@@ -616,10 +616,10 @@ __device__ __forceinline__ void gather_sum(const SeqPlan *P, const uint64_t *are
             if (!wave_any(stale) || gave_up(P, spins)) break;
 #pragma unroll
             for (int u = 0; u < B; ++u) {
-                const uint64_t *src = area + ((int64_t)(c0 + u) * 64 + lane) * M;
+                const uint64_t *src = area + (int64_t)(c0 + u) * M * 64 + lane;
 #pragma unroll
                 for (int m = 0; m < M; ++m)
-                    if (c0 + u < c_end && tag_of(v[u][m]) != tag) v[u][m] = load_shared(src + m);
+                    if (c0 + u < c_end && tag_of(v[u][m]) != tag) v[u][m] = load_shared(src + m * 64);
             }
         }
 #pragma unroll
@@ -751,9 +751,12 @@ __device__ __forceinline__ void leave_phase(const SeqPlan *P, const Lay &L, int 
                 for (int m = 0; m < M; ++m) v[m] += src[m * 64];
             }
         }
-        uint64_t *dst = area + ((int64_t)sg.cidx * 64 + lane) * M;
+        // row m's 64 words side by side: each store is one contiguous 512-byte
+        // run (a lane's M words side by side would scatter every store over
+        // M times as many lines, each written through in part)
+        uint64_t *dst = area + (int64_t)sg.cidx * M * 64 + lane;
 #pragma unroll
-        for (int m = 0; m < M; ++m) store_shared(dst + m, tagged(__float_as_uint(v[m]), tag));
+        for (int m = 0; m < M; ++m) store_shared(dst + m * 64, tagged(__float_as_uint(v[m]), tag));
     }
 }
 
