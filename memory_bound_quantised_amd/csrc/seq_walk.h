@@ -273,24 +273,34 @@ __device__ __forceinline__ bool wave_any(bool b) { return __builtin_amdgcn_ballo
 // Publish one stats record (word 0 of copy 0 at rec, word c of copy k at
 // rec + k * rep + c * stride) from per-lane values: v feeds the sum of
 // squares, a the maximum magnitude (lanes past the stats rows pass 0).  Lane
-// 63 holds the reductions; lanes 0 .. kStatReplicas-1 write one copy each.
+// 63 holds the reductions; every lane then writes one (copy, word) of the
+// record, kStatReplicas copies of each word side by side in lane order, so the
+// 3M words of all copies take 3M / 8 stores (rounded up), not 3M: every store
+// counts against the wave's 63 memory operations in flight until it has
+// reached memory.
 template <int M>
 __device__ __forceinline__ void publish_stats(uint64_t *rec, int64_t stride, int64_t rep, const float (&v)[M],
                                               const float (&a)[M], uint32_t tag, int lane) {
+    uint32_t w[3 * M];   // the record's words (wave-uniform)
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         const double ss = wave_sum63((double)v[m] * (double)v[m]);
         const float am = wave_max63(fabsf(a[m]));
         const uint64_t bits = (uint64_t)__double_as_longlong(ss);
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bits, 63);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), 63);
-        const uint32_t amb = (uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(am), 63);
-        if (lane < kStatReplicas) {
-            uint64_t *d = rec + lane * rep;
-            store_shared(d + (3 * m) * stride, tagged(amb, tag));
-            store_shared(d + (3 * m + 1) * stride, tagged(lo, tag));
-            store_shared(d + (3 * m + 2) * stride, tagged(hi, tag));
-        }
+        w[3 * m + 1] = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bits, 63);
+        w[3 * m + 2] = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), 63);
+        w[3 * m] = (uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(am), 63);
+    }
+    static_assert(64 % kStatReplicas == 0, "whole words per store");
+    constexpr int kWordsPerStore = 64 / kStatReplicas;
+    const int k = lane % kStatReplicas;
+#pragma unroll
+    for (int c0 = 0; c0 < 3 * M; c0 += kWordsPerStore) {
+        const int c = c0 + lane / kStatReplicas;
+        uint32_t val = w[c0];
+#pragma unroll
+        for (int i = 1; i < kWordsPerStore && c0 + i < 3 * M; ++i) val = c == c0 + i ? w[c0 + i] : val;
+        if (c < 3 * M) store_shared(rec + k * rep + c * stride, tagged(val, tag));
     }
 }
 
