@@ -278,8 +278,9 @@ def run_linear_config(mbq, copies=128, reps=8):
     """The single 4096 x 4096 W4A8 linear at M = 1 (activations N(0,1) bf16, int4
     codes uniform, fp16 group-128 scales U(0.005, 0.02)) over `copies` distinct
     packed matrices used in turn (8.65 MB each, together over 1 GB, so no copy is
-    still cached when it comes round again): the linear alone, and the per-row
-    quantisation followed by the linear."""
+    still cached when it comes round again): the linear alone, the per-row
+    quantisation followed by the linear, and the linear with the quantisation
+    inside it (mbq_linear_prologue)."""
     import torch
     N = K = 4096
     bits = 4
@@ -306,9 +307,16 @@ def run_linear_config(mbq, copies=128, reps=8):
         mbq._check("mbq_w4a8_linear", L.mbq_w4a8_linear(1, N, K, qb.data_ptr(), sb.data_ptr(),
                                                         packed[i].data_ptr(), y.data_ptr(), ws.data_ptr(),
                                                         ws.numel(), st()))
+    fws = torch.zeros(mbq.linear_prologue_workspace_bytes(bits, 1, N, K), dtype=torch.uint8, device="cuda")
+
+    def fused(i):   # the quantisation inside the linear: one call
+        mbq._check("mbq_linear_prologue", L.mbq_linear_prologue(bits, mbq.PRO_QUANT, 1, N, K, x.data_ptr(), None, None,
+                                                                packed[i].data_ptr(), y.data_ptr(), fws.data_ptr(),
+                                                                fws.numel(), st()))
     wb = synth.weight_bytes(bits, [("w", K, N)])
     lin_ms, lin_best, mode = _graph_time(lin, copies, reps)
     ql_ms, ql_best, _ = _graph_time(quant_lin, copies, reps)
+    fu_ms, fu_best, _ = _graph_time(fused, copies, reps)
     assert torch.isfinite(y.float()).all()
     del packed
     torch.cuda.empty_cache()
@@ -318,7 +326,9 @@ def run_linear_config(mbq, copies=128, reps=8):
             "linear_pct_hbm_peak": round(100 * wb / (lin_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
             "linear_us_best": round(lin_best * 1e3, 3),
             "quant_plus_linear_us": round(ql_ms * 1e3, 3),
-            "quant_plus_linear_GB/s": round(wb / (ql_ms / 1e3) / 1e9, 1)}
+            "quant_plus_linear_GB/s": round(wb / (ql_ms / 1e3) / 1e9, 1),
+            "quant_inside_linear_us": round(fu_ms * 1e3, 3),
+            "quant_inside_linear_GB/s": round(wb / (fu_ms / 1e3) / 1e9, 1)}
 
 
 def cpu_model():

@@ -174,6 +174,41 @@ int mbq_w6a8_linear(int64_t M, int64_t N, int64_t K, const int8_t *q, const floa
                     const void *packed, void *y_bf16, void *ws, int64_t ws_bytes,
                     void *stream);
 
+/* The linear with the quantisation, and the prologue before it, inside it
+ * (page "Doubling LLM token rates in ComfyUI", "Optimizing the Linear
+ * Kernel": the quantisation absorbs the RMSNorm or SwiGLU in front of it, so
+ * the intermediate is never written).  y = the linear of (q, s), where (q, s)
+ * is what mbq_quantize_act, mbq_rmsnorm_quantize_act,
+ * mbq_wrmsnorm_quantize_act or mbq_swiglu_quantize_act gives for the rows.
+ *   bits      4 or 6.
+ *   prologue  MBQ_PRO_QUANT: the rows x themselves; MBQ_PRO_RMSNORM_QUANT:
+ *             the weightless RMSNorm of x; MBQ_PRO_WRMSNORM_QUANT: the
+ *             RMSNorm of x weighted by w; MBQ_PRO_SWIGLU_QUANT: silu(x) * u,
+ *             x being the gate rows and u the up rows.
+ *   x_bf16, u_bf16  bf16 [M][K], row-major, 16-byte aligned; u_bf16 null
+ *             unless the prologue is SwiGLU.
+ *   w_bf16    bf16 [K] norm weights, 16-byte aligned; null unless weighted.
+ *   packed, y_bf16, stream  as mbq_w4a8_linear.
+ *   ws        device workspace, 256-byte aligned, of
+ *             mbq_linear_prologue_workspace_bytes(bits, M, N, K) bytes,
+ *             zero-filled before its first use (as for the linear).
+ * Where the linear's one-workgroup-per-row-block form applies (48..256 row
+ * blocks of 64 rows, K up to 8192) every workgroup runs the prologue and the
+ * quantisation on the rows into its LDS and reads its activation codes from
+ * there: one launch, nothing written but y.  Other shapes run the prologue
+ * and quantisation as a launch of their own into the workspace first.  The
+ * codes and scales are computed by the same routine as the quantisation
+ * calls', so y equals those calls followed by the linear bit for bit (a
+ * block of another size sums the fp64 squares of a norm in another order,
+ * which could move r only where the mean square lies within a few units of
+ * 2^-40 of an fp32 rounding boundary).
+ * Returns MBQ_ERR_PROGRAM for an unknown prologue, MBQ_ERR_NULL for a
+ * missing pointer the prologue needs, and otherwise as mbq_w4a8_linear. */
+int64_t mbq_linear_prologue_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K);
+int mbq_linear_prologue(int bits, int prologue, int64_t M, int64_t N, int64_t K, const void *x_bf16,
+                        const void *u_bf16, const void *w_bf16, const void *packed, void *y_bf16, void *ws,
+                        int64_t ws_bytes, void *stream);
+
 /* The same linear for callers that cannot allocate (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): no
  * workspace argument.  Its split-K counters and partials live in an array of

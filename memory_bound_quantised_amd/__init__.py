@@ -15,8 +15,6 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmbq.so")
 
-PRO_QUANT = 0
-PRO_RMSNORM_QUANT = 1
 STATUS = {0: "MBQ_OK", -1: "MBQ_ERR_NULL", -2: "MBQ_ERR_SHAPE", -3: "MBQ_ERR_BITS",
           -4: "MBQ_ERR_ALIGN", -5: "MBQ_ERR_WORKSPACE", -6: "MBQ_ERR_PROGRAM",
           -7: "MBQ_ERR_HIP", -8: "MBQ_ERR_DEVICE", -9: "MBQ_ERR_TIMEOUT"}
@@ -29,7 +27,8 @@ EXPORTS = ["mbq_status_string", "mbq_last_hip_error", "mbq_version", "mbq_packed
            "mbq_w6a8_linear", "mbq_linear_group_acc", "mbq_sequence_workspace_bytes",
            "mbq_sequence_prepare", "mbq_sequence_run", "mbq_sequence_check", "mbq_layer_sequence",
            "mbq_layer_sequence_unfused", "mbq_attention_workspace_bytes", "mbq_decode_attention",
-           "mbq_stream_read", "mbq_linear_noalloc"]
+           "mbq_stream_read", "mbq_linear_noalloc", "mbq_linear_prologue_workspace_bytes",
+           "mbq_linear_prologue"]
 
 
 class MbqError(RuntimeError):
@@ -100,10 +99,14 @@ def lib() -> ctypes.CDLL:
         L.mbq_sequence_check.argtypes = [P, P]
         L.mbq_stream_read.argtypes = [P, I64, P, P]
         L.mbq_linear_noalloc.argtypes = [ctypes.c_int, I64, I64, I64, P, P, P, P, P]
+        L.mbq_linear_prologue_workspace_bytes.argtypes = [ctypes.c_int, I64, I64, I64]
+        L.mbq_linear_prologue_workspace_bytes.restype = I64
+        L.mbq_linear_prologue.argtypes = [ctypes.c_int, ctypes.c_int, I64, I64, I64, P, P, P, P, P, P, I64, P]
         for name in EXPORTS:
             if name not in ("mbq_status_string", "mbq_last_hip_error", "mbq_version",
                             "mbq_packed_bytes", "mbq_linear_workspace_bytes",
-                            "mbq_sequence_workspace_bytes", "mbq_attention_workspace_bytes"):
+                            "mbq_sequence_workspace_bytes", "mbq_attention_workspace_bytes",
+                            "mbq_linear_prologue_workspace_bytes"):
                 getattr(L, name).restype = ctypes.c_int
         _lib_handle = L
     return _lib_handle
@@ -262,6 +265,30 @@ def linear_noalloc(bits: int, q, s, packed, N: int, out):
     M, K = q.shape
     _check("mbq_linear_noalloc", lib().mbq_linear_noalloc(bits, M, N, K, _ptr(q), _ptr(s), _ptr(packed),
                                                           _ptr(out), _stream()))
+    return out
+
+
+def linear_prologue_workspace_bytes(bits: int, M: int, N: int, K: int) -> int:
+    n = lib().mbq_linear_prologue_workspace_bytes(bits, M, N, K)
+    if n < 0:
+        raise MbqError("mbq_linear_prologue_workspace_bytes", n)
+    return n
+
+
+def linear_prologue(bits: int, x_bf16, packed, N: int, prologue: int = PRO_QUANT, up=None, norm_w=None,
+                    ws=None, out=None):
+    """The linear with the quantisation and its prologue inside it
+    (mbq_linear_prologue): bf16 rows x [M][K] (the gate rows for SwiGLU, with
+    up [M][K]; norm_w [K] for the weighted RMSNorm) -> bf16 y [M][N]."""
+    import torch
+    M, K = x_bf16.shape
+    if ws is None:
+        ws = _zeros(linear_prologue_workspace_bytes(bits, M, N, K), x_bf16.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x_bf16.device)
+    _check("mbq_linear_prologue", lib().mbq_linear_prologue(
+        bits, prologue, M, N, K, _ptr(x_bf16), _ptr(up) if up is not None else None,
+        _ptr(norm_w) if norm_w is not None else None, _ptr(packed), _ptr(out), _ptr(ws), ws.numel(), _stream()))
     return out
 
 

@@ -218,6 +218,35 @@ int mbq_w6a8_linear(int64_t M, int64_t N, int64_t K, const int8_t *q, const floa
     return linear_common(6, M, N, K, q, s, packed, y_bf16, ws, ws_bytes, stream);
 }
 
+int64_t mbq_linear_prologue_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K) {
+    if (!bits_ok(bits)) return MBQ_ERR_BITS;
+    if (!m_ok(M) || !n_ok(N) || !k_ok(K)) return MBQ_ERR_SHAPE;
+    return linear_prologue_ws_bytes(bits, M, N, K);
+}
+
+int mbq_linear_prologue(int bits, int prologue, int64_t M, int64_t N, int64_t K, const void *x_bf16,
+                        const void *u_bf16, const void *w_bf16, const void *packed, void *y_bf16, void *ws,
+                        int64_t ws_bytes, void *stream) {
+    if (!bits_ok(bits)) return MBQ_ERR_BITS;
+    if (prologue < MBQ_PRO_QUANT || prologue > MBQ_PRO_SWIGLU_QUANT) return MBQ_ERR_PROGRAM;
+    if (!x_bf16 || !packed || !y_bf16) return MBQ_ERR_NULL;
+    if (prologue == MBQ_PRO_SWIGLU_QUANT && !u_bf16) return MBQ_ERR_NULL;
+    if (prologue == MBQ_PRO_WRMSNORM_QUANT && !w_bf16) return MBQ_ERR_NULL;
+    if (!m_ok(M) || !n_ok(N) || !k_ok(K)) return MBQ_ERR_SHAPE;
+    if (!aligned(packed, 256) || !aligned(x_bf16, 16) || !aligned(y_bf16, 16) ||
+        (u_bf16 && !aligned(u_bf16, 16)) || (w_bf16 && !aligned(w_bf16, 16)))
+        return MBQ_ERR_ALIGN;
+    if (!ws || ws_bytes < linear_prologue_ws_bytes(bits, M, N, K)) return MBQ_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return MBQ_ERR_ALIGN;
+    int st = check_device();
+    if (st) return st;
+    const void *u = prologue == MBQ_PRO_SWIGLU_QUANT ? u_bf16 : nullptr;
+    const void *w = prologue == MBQ_PRO_WRMSNORM_QUANT ? w_bf16 : nullptr;
+    hipError_t e = launch_linear_prologue(bits, prologue, M, N, K, x_bf16, u, w, packed, y_bf16, ws,
+                                          (hipStream_t)stream);
+    return e == hipSuccess ? MBQ_OK : hip_fail(e);
+}
+
 int mbq_linear_noalloc(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,
                        const void *packed, void *y_bf16, void *stream) {
     if (!bits_ok(bits)) return MBQ_ERR_BITS;

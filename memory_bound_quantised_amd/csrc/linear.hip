@@ -22,6 +22,7 @@
 // split-prefix decode attention ("Paying attention to the attention!").
 #include "mbq_internal.h"
 #include "mbq_kernels.h"
+#include "quant_rows.h"
 
 namespace mbq {
 
@@ -235,15 +236,23 @@ struct RbBatch {
     v4i a0[TB], a1[TB];
 };
 
-template <int BITS, int M, int TB>
-__device__ __forceinline__ void rb_load(RbBatch<BITS, M, TB> &b, const uint8_t *tiles, const v4i *qrow, int gb,
-                                        int g_last, int lane) {
+// The activation halves of group g come from global memory (qrow) or, when
+// the workgroup quantised its rows itself, from LDS (qlds).
+template <int BITS, int M, int TB, bool QLDS>
+__device__ __forceinline__ void rb_load(RbBatch<BITS, M, TB> &b, const uint8_t *tiles, const v4i *qrow,
+                                        const __attribute__((address_space(3))) v4i *qlds, int gb, int g_last,
+                                        int lane) {
 #pragma unroll
     for (int u = 0; u < TB; ++u) {
         const int g = min(gb + u, g_last);
         load_tile<BITS>(tiles + (int64_t)g * Layout<BITS>::kTileBytes, lane, b.w[u], b.sc[u]);
-        b.a0[u] = *gptr(qrow + g * 8);
-        b.a1[u] = *gptr(qrow + g * 8 + 1);
+        if constexpr (QLDS) {
+            b.a0[u] = qlds[g * 8];
+            b.a1[u] = qlds[g * 8 + 1];
+        } else {
+            b.a0[u] = *gptr(qrow + g * 8);
+            b.a1[u] = *gptr(qrow + g * 8 + 1);
+        }
     }
 }
 
@@ -264,14 +273,57 @@ __device__ __forceinline__ void rb_sum(const RbBatch<BITS, M, TB> &b, int gb, in
     }
 }
 
-template <int BITS, int M, int W, int SHOT>
+// One activation row into LDS through prologue PRO and the quantisation.
+template <int PRO, int NT>
+__device__ __forceinline__ float rb_quant_row(int8_t *q_row, const uint16_t *x, const uint16_t *u, const uint16_t *wn,
+                                              int K, double *red_d, float *red_f) {
+    const auto put = [&](int64_t c, uint32_t lo, uint32_t hi) {
+        *reinterpret_cast<uint2 *>(q_row + 8 * c) = make_uint2(lo, hi);
+    };
+    const auto none = [](int64_t, const float (&)[8]) {};
+    return quant_row<PRO, NT, false>(x, u, wn, K, red_d, red_f, put, none);
+}
+
+// QF false: q and s come quantised from global memory.  QF true: the
+// workgroup runs prologue `pro` (an MBQ_PRO_* value) and the quantisation on
+// the bf16 rows x (and u, wn) itself, into dynamic LDS (M x K codes), first.
+template <int BITS, int M, int W, int SHOT, bool QF>
 __global__ __launch_bounds__(64 * W) void linear_rb_kernel(
     const uint8_t *__restrict__ packed, const int8_t *__restrict__ q, const float *__restrict__ s,
-    uint16_t *__restrict__ y, int64_t y_stride, int N, int K) {
+    uint16_t *__restrict__ y, int64_t y_stride, int N, int K, int pro, const uint16_t *__restrict__ x,
+    const uint16_t *__restrict__ u, const uint16_t *__restrict__ wn) {
     using L = Layout<BITS>;
     constexpr int TB = rb_batch<BITS>();
     constexpr int AR = M > 4 ? 4 : M;
+    constexpr bool kQlds = QF;
     __shared__ float red[W][M][64];
+    __shared__ float s_lds[M];
+    extern __shared__ __align__(16) int8_t q_lds[];
+    if constexpr (QF) {
+        __shared__ double red_d[W];
+        __shared__ float red_f[W];
+        for (int m = 0; m < M; ++m) {
+            int8_t *qr = q_lds + (int64_t)m * K;
+            const uint16_t *xr = x + (int64_t)m * K, *ur = u ? u + (int64_t)m * K : nullptr;
+            float sc;
+            switch (pro) {
+                case MBQ_PRO_RMSNORM_QUANT:
+                    sc = rb_quant_row<MBQ_PRO_RMSNORM_QUANT, 64 * W>(qr, xr, ur, wn, K, red_d, red_f);
+                    break;
+                case MBQ_PRO_WRMSNORM_QUANT:
+                    sc = rb_quant_row<MBQ_PRO_WRMSNORM_QUANT, 64 * W>(qr, xr, ur, wn, K, red_d, red_f);
+                    break;
+                case MBQ_PRO_SWIGLU_QUANT:
+                    sc = rb_quant_row<MBQ_PRO_SWIGLU_QUANT, 64 * W>(qr, xr, ur, wn, K, red_d, red_f);
+                    break;
+                default:
+                    sc = rb_quant_row<MBQ_PRO_QUANT, 64 * W>(qr, xr, ur, wn, K, red_d, red_f);
+                    break;
+            }
+            if (threadIdx.x == 0) s_lds[m] = sc;
+        }
+        __syncthreads();
+    }
     const int lane = threadIdx.x & 63;
     const int w = uniform(threadIdx.x >> 6);
     const int rb = blockIdx.x;
@@ -281,7 +333,10 @@ __global__ __launch_bounds__(64 * W) void linear_rb_kernel(
     // lane l sums weight rows 4 (l & 15) + i for activation rows 4 (l >> 4) + j
     // (rows past M are computed from row 0 and dropped), as the split form
     const int am = (lane & 15) < M ? (lane & 15) : 0;
-    const v4i *qrow = reinterpret_cast<const v4i *>(q + (int64_t)am * K + (lane >> 4) * 32);
+    const v4i *qrow = kQlds ? nullptr : reinterpret_cast<const v4i *>(q + (int64_t)am * K + (lane >> 4) * 32);
+    const __attribute__((address_space(3))) v4i *qlds =
+        reinterpret_cast<const __attribute__((address_space(3))) v4i *>(
+            (const __attribute__((address_space(3))) int8_t *)q_lds + (int64_t)am * K + (lane >> 4) * 32);
     float facc[4][AR];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -290,18 +345,18 @@ __global__ __launch_bounds__(64 * W) void linear_rb_kernel(
     if (g1 - g0 > 0 && g1 - g0 <= SHOT) {
         // every tile of the wave in flight at once, summed in the same branch
         RbBatch<BITS, M, SHOT> A;
-        rb_load<BITS, M, SHOT>(A, tiles, qrow, g0, g1 - 1, lane);
+        rb_load<BITS, M, SHOT, kQlds>(A, tiles, qrow, qlds, g0, g1 - 1, lane);
         rb_sum<BITS, M, SHOT, AR>(A, g0, g1, facc);
     } else if (g1 - g0 > SHOT) {
         RbBatch<BITS, M, TB> A, B;
-        rb_load<BITS, M, TB>(A, tiles, qrow, g0, g1 - 1, lane);
+        rb_load<BITS, M, TB, kQlds>(A, tiles, qrow, qlds, g0, g1 - 1, lane);
         {
             for (int gb = g0;;) {
-                rb_load<BITS, M, TB>(B, tiles, qrow, gb + TB, g1 - 1, lane);
+                rb_load<BITS, M, TB, kQlds>(B, tiles, qrow, qlds, gb + TB, g1 - 1, lane);
                 rb_sum<BITS, M, TB, AR>(A, gb, g1, facc);
                 gb += TB;
                 if (gb >= g1) break;
-                rb_load<BITS, M, TB>(A, tiles, qrow, gb + TB, g1 - 1, lane);
+                rb_load<BITS, M, TB, kQlds>(A, tiles, qrow, qlds, gb + TB, g1 - 1, lane);
                 rb_sum<BITS, M, TB, AR>(B, gb, g1, facc);
                 gb += TB;
                 if (gb >= g1) break;
@@ -324,7 +379,8 @@ __global__ __launch_bounds__(64 * W) void linear_rb_kernel(
 #pragma unroll
         for (int ww = 0; ww < W; ++ww) tot += red[ww][m][r];
         const int n = rb * 64 + r;
-        if (n < N) y[m * y_stride + n] = (uint16_t)f32_to_bf16_bits(s[m] * (tot * unscale));
+        const float sm = kQlds ? s_lds[m] : s[m];
+        if (n < N) y[m * y_stride + n] = (uint16_t)f32_to_bf16_bits(sm * (tot * unscale));
     }
 }
 
@@ -372,16 +428,21 @@ __global__ __launch_bounds__(64) void group_acc_kernel(const uint8_t *__restrict
     }
 }
 
-template <int BITS, int M>
+template <int BITS, int M, bool QF>
 void launch_rb(const uint8_t *pk, const int8_t *q, const float *s, uint16_t *y, int64_t y_stride, int64_t N,
-               int64_t K, int64_t n_rb, int64_t groups, hipStream_t st) {
+               int64_t K, int64_t n_rb, int64_t groups, int pro, const uint16_t *x, const uint16_t *u,
+               const uint16_t *wn, hipStream_t st) {
     const dim3 grid((unsigned)n_rb);
+    const size_t lds = QF ? (size_t)(M * K) : 0;
     if (groups > 32) {
-        linear_rb_kernel<BITS, M, 4, 8><<<grid, dim3(64 * 4), 0, st>>>(pk, q, s, y, y_stride, (int)N, (int)K);
+        linear_rb_kernel<BITS, M, 4, 8, QF><<<grid, dim3(64 * 4), lds, st>>>(pk, q, s, y, y_stride, (int)N, (int)K,
+                                                                             pro, x, u, wn);
     } else if constexpr (BITS == 4 && M <= 3) {
-        linear_rb_kernel<BITS, M, 16, 2><<<grid, dim3(64 * 16), 0, st>>>(pk, q, s, y, y_stride, (int)N, (int)K);
+        linear_rb_kernel<BITS, M, 16, 2, QF><<<grid, dim3(64 * 16), lds, st>>>(pk, q, s, y, y_stride, (int)N,
+                                                                               (int)K, pro, x, u, wn);
     } else {
-        linear_rb_kernel<BITS, M, 8, 4><<<grid, dim3(64 * 8), 0, st>>>(pk, q, s, y, y_stride, (int)N, (int)K);
+        linear_rb_kernel<BITS, M, 8, 4, QF><<<grid, dim3(64 * 8), lds, st>>>(pk, q, s, y, y_stride, (int)N, (int)K,
+                                                                             pro, x, u, wn);
     }
 }
 
@@ -392,7 +453,7 @@ hipError_t launch_linear_bits(int64_t M, int64_t N, int64_t K, const int8_t *q, 
     const uint8_t *pk = (const uint8_t *)packed;
     uint16_t *yv = (uint16_t *)y;
     if (plan.rb_form) {
-#define MBQ_RB(MM) launch_rb<BITS, MM>(pk, q, s, yv, y_stride, N, K, plan.n_rb, plan.groups, st)
+#define MBQ_RB(MM) launch_rb<BITS, MM, false>(pk, q, s, yv, y_stride, N, K, plan.n_rb, plan.groups, 0, nullptr, nullptr, nullptr, st)
         switch (M) {
             case 1: MBQ_RB(1); break;
             case 2: MBQ_RB(2); break;
@@ -485,6 +546,48 @@ hipError_t launch_linear(int bits, int64_t M, int64_t N, int64_t K, const int8_t
                          hipStream_t st) {
     return bits == 4 ? launch_linear_bits<4>(M, N, K, q, s, packed, y, y_stride, ws, plan, st)
                      : launch_linear_bits<6>(M, N, K, q, s, packed, y, y_stride, ws, plan, st);
+}
+
+int64_t linear_prologue_ws_bytes(int bits, int64_t M, int64_t N, int64_t K) {
+    return (M * K + 255) / 256 * 256 + 256 + plan_linear(bits, M, N, K).ws_bytes;
+}
+
+hipError_t launch_linear_prologue(int bits, int pro, int64_t M, int64_t N, int64_t K, const void *x, const void *u,
+                                  const void *w, const void *packed, void *y, void *ws, hipStream_t st) {
+    const LinearPlan plan = plan_linear(bits, M, N, K);
+    if (plan.rb_form) {
+        const uint8_t *pk = (const uint8_t *)packed;
+        uint16_t *yv = (uint16_t *)y;
+        const uint16_t *xs = (const uint16_t *)x, *us = (const uint16_t *)u, *wn = (const uint16_t *)w;
+#define MBQ_RBF(B, MM) \
+    launch_rb<B, MM, true>(pk, nullptr, nullptr, yv, N, N, K, plan.n_rb, plan.groups, pro, xs, us, wn, st)
+#define MBQ_RBF_M(B)                   \
+    switch (M) {                       \
+        case 1: MBQ_RBF(B, 1); break;  \
+        case 2: MBQ_RBF(B, 2); break;  \
+        case 3: MBQ_RBF(B, 3); break;  \
+        case 4: MBQ_RBF(B, 4); break;  \
+        case 5: MBQ_RBF(B, 5); break;  \
+        case 6: MBQ_RBF(B, 6); break;  \
+        case 7: MBQ_RBF(B, 7); break;  \
+        default: MBQ_RBF(B, 8); break; \
+    }
+        if (bits == 4) {
+            MBQ_RBF_M(4)
+        } else {
+            MBQ_RBF_M(6)
+        }
+#undef MBQ_RBF_M
+#undef MBQ_RBF
+        return hipGetLastError();
+    }
+    // other shapes: the prologue kernel, then the split linear, through the workspace
+    int8_t *q = (int8_t *)ws;
+    float *s = (float *)((char *)ws + (M * K + 255) / 256 * 256);
+    void *lin_ws = (char *)ws + (M * K + 255) / 256 * 256 + 256;
+    hipError_t e = launch_prologue_quant(pro, M, K, x, K, u, K, w, nullptr, q, s, st);
+    if (e != hipSuccess) return e;
+    return launch_linear(bits, M, N, K, q, s, packed, y, N, lin_ws, plan, st);
 }
 
 hipError_t launch_group_acc(int bits, bool mfma, int64_t M, int64_t N, int64_t K, const int8_t *q,

@@ -89,7 +89,11 @@ LinearPlan plan_linear(int bits, int64_t M, int64_t N, int64_t K);
 hipError_t launch_linear(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,
                          const void *packed, void *y, int64_t y_stride, void *ws, const LinearPlan &plan,
                          hipStream_t st);
-// Exact int32 group sums through the matrix-core (mfma) or v_dot4 tile form.
+// The linear with its prologue and quantisation run inside it where the
+// row-block form applies, else as a prologue launch into the workspace first.
+int64_t linear_prologue_ws_bytes(int bits, int64_t M, int64_t N, int64_t K);
+hipError_t launch_linear_prologue(int bits, int pro, int64_t M, int64_t N, int64_t K, const void *x, const void *u,
+                                  const void *w, const void *packed, void *y, void *ws, hipStream_t st);
 // The linear on the library's own device scratch (noalloc.hip): status or MBQ_OK.
 int64_t noalloc_scratch_bytes();
 int linear_noalloc(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,

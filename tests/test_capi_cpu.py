@@ -105,6 +105,29 @@ def test_linear_noalloc_validation():
     assert 0 < worst <= cap
 
 
+def test_linear_prologue_validation():
+    """Argument checks of the linear with its prologue inside, all before any device call."""
+    L = mbq.lib()
+    f = L.mbq_linear_prologue
+    need = L.mbq_linear_prologue_workspace_bytes(4, 3, 4096, 4096)
+    lin = L.mbq_linear_workspace_bytes(4, 3, 4096, 4096)
+    assert need >= 3 * 4096 + 256 + lin                                          # codes, scales, linear scratch
+    assert L.mbq_linear_prologue_workspace_bytes(5, 3, 4096, 4096) == -3
+    assert L.mbq_linear_prologue_workspace_bytes(4, 9, 4096, 4096) == -2
+    def call(bits=4, pro=0, M=3, N=4096, K=4096, x=A, u=None, w=None, packed=A, y=A, ws=A, wsb=need):
+        return f(bits, pro, M, N, K, x, u, w, packed, y, ws, wsb, None)
+    assert call(bits=5) == -3
+    assert call(pro=4) == -6 and call(pro=-1) == -6                               # unknown prologue
+    assert call(x=None) == -1 and call(y=None) == -1 and call(packed=None) == -1
+    assert call(pro=3) == -1                                                      # SwiGLU without up rows
+    assert call(pro=2) == -1                                                      # weighted norm without weights
+    assert call(M=9) == -2 and call(K=4000) == -2
+    assert call(packed=A + 16) == -4 and call(x=A + 8) == -4
+    assert call(pro=3, u=A + 8) == -4 and call(pro=2, w=A + 8) == -4
+    assert call(wsb=need - 1) == -5 and call(ws=None) == -5
+    assert call(ws=A + 16) == -4
+
+
 def test_stream_read_validation():
     L = mbq.lib()
     assert L.mbq_stream_read(None, 1024, A, None) == -1

@@ -235,6 +235,36 @@ def test_linear_row_block_form_vs_oracle(bits, M, N, K):
     assert_close_bf16(host(y), oracle.linear(bits, q, s, canon, S), f"W{bits} M={M} {N}x{K}")
 
 
+# The linear with its prologue and quantisation inside it: bitwise the
+# quantisation call followed by the linear (every prologue; 4096 x 4096 and
+# 3070 x 4224 take the row-block form with 16 or 8 waves, 5120 x 8192 the one
+# with 4 waves and batched ranges, 1024 x 5120 the prologue launch and the
+# split form).
+@pytest.mark.parametrize("bits", [4, 6])
+@pytest.mark.parametrize("prologue", [0, 1, 2, 3])
+@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("N,K", [(4096, 4096), (3070, 4224), (5120, 8192), (1024, 5120)])
+def test_linear_prologue_matches_quantise_then_linear(bits, prologue, M, N, K):
+    canon, S = synth.weights(bits, N, K, seed=N + K + prologue)
+    packed = packed_on_device(bits, canon, S, N, K)
+    x = dev(synth.activations(M, K))
+    up = dev(synth.activations(M, K, seed=77)) if prologue == mbq.PRO_SWIGLU_QUANT else None
+    nw = dev(synth.norm_weights(K, 5)) if prologue == mbq.PRO_WRMSNORM_QUANT else None
+    y = host(mbq.linear_prologue(bits, x, packed, N, prologue, up=up, norm_w=nw))
+    q, s = mbq.quantize_act(x, rmsnorm=prologue == mbq.PRO_RMSNORM_QUANT, norm_w=nw, up=up)
+    ref = host(mbq.linear(bits, q, s, packed, N))
+    assert np.array_equal(y, ref), f"W{bits} prologue {prologue} M={M} {N}x{K}"
+
+
+@pytest.mark.parametrize("prologue", [0, 1])
+def test_linear_prologue_vs_oracle(prologue):
+    N, K, M = 4096, 4096, 3
+    canon, S = synth.weights(4, N, K, seed=21)
+    x = synth.activations(M, K)
+    y = host(mbq.linear_prologue(4, dev(x), packed_on_device(4, canon, S, N, K), N, prologue))
+    assert_close_bf16(y, oracle.op(4, x, prologue, canon, S), f"prologue {prologue}")
+
+
 # Full-size shapes of the 9B- and 27B-shaped decode steps; outputs checked on sampled rows.
 FULL_SHAPES = [(4096, 4096), (1024, 4096), (12288, 4096), (4096, 12288), (16384, 5120),
                (1024, 5120), (5120, 8192), (17408, 5120), (5120, 17408)]
