@@ -341,7 +341,10 @@ int mbq_sequence_prepare(const mbq_op *ops, int32_t n_ops, void *const *bufs,
  * the prepared walk with all its quantisations fused in, keeping the weight
  * stream going across op boundaries.  Enqueued on `stream`; does not wait.
  * Needs every workgroup of its grid resident at once (cooperative launch);
- * nothing else may run on the device in parallel with it. */
+ * nothing else may run on the device in parallel with it.  May be captured
+ * in a HIP graph and replayed: each launch reads the workspace's launch
+ * count on the device and tags the words it hands between workgroups with
+ * it, so a replay never takes a word an earlier launch left. */
 int mbq_sequence_run(const mbq_sequence_info *info, void *ws, void *stream);
 
 /* Wait for `stream`, then report whether the last walks run on ws completed

@@ -383,8 +383,6 @@ int64_t mbq_sequence_workspace_bytes(const mbq_op *ops, int32_t n_ops, const int
     return fused_region_bytes(ops, n_ops, buf_widths, n_bufs, M) + unfused;
 }
 
-static std::atomic<uint32_t> g_generation{0};
-
 int mbq_sequence_prepare(const mbq_op *ops, int32_t n_ops, void *const *bufs, const int64_t *buf_widths,
                          int32_t n_bufs, int64_t M, void *ws, int64_t ws_bytes, void *stream,
                          mbq_sequence_info *info) {
@@ -408,7 +406,7 @@ int mbq_sequence_prepare(const mbq_op *ops, int32_t n_ops, void *const *bufs, co
     if (need < 0) return (int)need;
     if (ws_bytes < need) return MBQ_ERR_WORKSPACE;
     hipStream_t hs = (hipStream_t)stream;
-    hipError_t e = hipMemsetAsync(ws, 0, 256, hs);
+    hipError_t e = hipMemsetAsync(ws, 0, 128, hs);   // the error word's line; the walk epoch after it stays
     if (e == hipSuccess)
         e = hipMemcpyAsync((char *)ws + b.plan_offset, b.blob.data(), b.blob.size(), hipMemcpyHostToDevice, hs);
     if (e == hipSuccess) e = hipStreamSynchronize(hs);
@@ -431,10 +429,8 @@ int mbq_sequence_run(const mbq_sequence_info *info, void *ws, void *stream) {
         info->M > kMaxM || info->grid < 1)
         return MBQ_ERR_PROGRAM;
     if (!aligned(ws, 256)) return MBQ_ERR_ALIGN;
-    uint32_t gen = (g_generation.fetch_add(1, std::memory_order_relaxed) % ((1u << 22) - 1)) + 1;
     hipError_t e = launch_sequence(info->bits, info->M, info->full != 0, info->grid, info->lds_bytes,
-                                   (const char *)ws + info->plan_offset, (uint32_t *)ws, gen,
-                                   (hipStream_t)stream);
+                                   (const char *)ws + info->plan_offset, (uint32_t *)ws, (hipStream_t)stream);
     return e == hipSuccess ? MBQ_OK : hip_fail(e);
 }
 

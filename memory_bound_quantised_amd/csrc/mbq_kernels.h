@@ -124,7 +124,6 @@ int64_t build_sequence_plan(const struct mbq_op *ops, int32_t n_ops, void *const
 // 1 only) and the full one (also weighted RMSNorms and SwiGLU inputs).
 const void *seq_kernel_plain(int bits, int64_t M);
 const void *seq_kernel_full(int bits, int64_t M);
-hipError_t launch_sequence(int bits, int64_t M, bool full, int grid, int lds_bytes, const void *plan, uint32_t *err,
-                           uint32_t gen, hipStream_t st);
+hipError_t launch_sequence(int bits, int64_t M, bool full, int grid, int lds_bytes, const void *plan, uint32_t *err, hipStream_t st);
 
 }  // namespace mbq

@@ -33,7 +33,7 @@ constexpr int kMetaMaxBytes = 4096;           // phase record + workgroup block,
 constexpr int kMaxRingSlots = 16;              // weight-ring tiles per compute wave, at most
 constexpr int kRecBuf = 64;                    // run records the loader buffers per compute wave (LDS)
 constexpr int kRecHalf = kRecBuf / 2;          // read this far ahead, half a buffer at a time
-constexpr uint64_t kPlanMagic = 0x6d62712d73657133ull;  // "mbq-seq3"
+constexpr uint64_t kPlanMagic = 0x6d62712d73657134ull;  // "mbq-seq4"
 
 // Every value that one wave hands to another travels in a 64-bit word whose
 // high half is the epoch tag of the phase that wrote it, so a single load
@@ -145,10 +145,16 @@ struct SeqPlan {
     const SeqPhase *phases;
     const SeqExt *ext;
     uint32_t *err;           // nonzero after a wait gave up
+    // Launches of the walk on this workspace so far: every workgroup reads it
+    // at the start (its tags are those of epoch + 1) and the last workgroup
+    // to exit advances it, so each launch -- a graph replay included -- has
+    // tags of its own.  Preparing a plan leaves it alone: words of an earlier
+    // plan's launches keep older tags.
+    uint32_t *epoch;
     uint64_t *stats;         // stats records, word-major
     int64_t stat_stride;     // records (words per stats word index)
     int64_t stat_rep;        // words per copy of the records
-    uint64_t *partials;      // [phase & 1][contribution][lane][m]: value bits | tag << 32
+    uint64_t *partials;      // [phase & 1][contribution][m][lane]: value bits | tag << 32
     const uint8_t *dummy;    // readable tile-sized area for loads past a stream's end
     const SeqRun *runs;      // every wave's runs, wave after wave, each in walk order
     const SeqWave *wtab;     // [waves]

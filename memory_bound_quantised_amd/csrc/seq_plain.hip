@@ -18,8 +18,8 @@ const void *seq_kernel_plain(int bits, int64_t M) {
 }
 
 hipError_t launch_sequence(int bits, int64_t M, bool full, int grid, int lds_bytes, const void *plan, uint32_t *err,
-                           uint32_t gen, hipStream_t st) {
-    void *args[] = {(void *)&plan, (void *)&err, (void *)&gen};
+                           hipStream_t st) {
+    void *args[] = {(void *)&plan, (void *)&err};
     const void *fn = full ? seq_kernel_full(bits, M) : seq_kernel_plain(bits, M);
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kSeqBlock), args, (unsigned)lds_bytes, st);
 }

@@ -1178,8 +1178,7 @@ __device__ __forceinline__ void stream_phase(const SeqPlan *P, const Lay &L, int
 }
 
 template <int BITS, int M, bool X>
-__global__ __launch_bounds__(kSeqBlock) void seq_kernel(const SeqPlan *__restrict__ P, uint32_t *err,
-                                                        uint32_t gen) {
+__global__ __launch_bounds__(kSeqBlock) void seq_kernel(const SeqPlan *__restrict__ P, uint32_t *err) {
     __shared__ float s_sh[2][kMaxM];
     __shared__ float r_sh[2][kMaxM];
     __shared__ float c_sh[kSeqWaves * (X ? 2 : 1) * M * 64];   // shared gathers of a finaliser
@@ -1191,6 +1190,10 @@ __global__ __launch_bounds__(kSeqBlock) void seq_kernel(const SeqPlan *__restric
     const int lane = threadIdx.x & 63;
     const int wi = uniform(threadIdx.x >> 6);
     const int wg = blockIdx.x;
+    // this launch's tags: those of the workspace's next epoch (22 bits, never 0)
+    uint32_t *epoch_p = cload(&P->epoch);
+    const uint32_t epoch = (uint32_t)uniform((int)load_shared(epoch_p));
+    const uint32_t gen = epoch % ((1u << 22) - 1) + 1;
     Lay L;
     L.qs = cload(&P->q_stride);
     L.slots = cload(&P->slots);
@@ -1248,13 +1251,16 @@ __global__ __launch_bounds__(kSeqBlock) void seq_kernel(const SeqPlan *__restric
     }
 
     // The last workgroup to exit clears the counters for the next launch
-    // (every wave's counter increments have completed before it counts out).
+    // (every wave's counter increments have completed before it counts out)
+    // and advances the epoch (every workgroup read it before counting out).
     wait_memory();
     cw_sync(P);
     if (threadIdx.x == 0) {
         uint32_t *cnt = cload(&P->counters);
-        if (counter_add(cnt + (int64_t)L.n_phases * kCounterStride, 1u) == (uint32_t)(L.grid - 1))
+        if (counter_add(cnt + (int64_t)L.n_phases * kCounterStride, 1u) == (uint32_t)(L.grid - 1)) {
             for (int i = 0; i <= L.n_phases; ++i) store_shared(cnt + (int64_t)i * kCounterStride, 0u);
+            store_shared(epoch_p, epoch + 1u);
+        }
     }
 }
 

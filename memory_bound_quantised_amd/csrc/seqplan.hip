@@ -438,6 +438,7 @@ int64_t build_sequence_plan(const mbq_op *ops, int32_t n_ops, void *const *bufs,
     plan.phases = reinterpret_cast<const SeqPhase *>(dev(off_phases));
     plan.ext = reinterpret_cast<const SeqExt *>(dev(off_ext));
     plan.err = reinterpret_cast<uint32_t *>(dev(off_err));
+    plan.epoch = reinterpret_cast<uint32_t *>(dev(off_err + 128));   // a line of its own, kept by prepare
     plan.stats = reinterpret_cast<uint64_t *>(dev(off_stats));
     plan.stat_stride = n_rec;
     plan.stat_rep = n_rec * 3 * M;

@@ -534,6 +534,65 @@ def test_layer_sequence_fused_deterministic_and_rerunnable(bits):
         assert_close_bf16(outs[0][o["out_buf"]], unf[o["out_buf"]], o["name"])
 
 
+@pytest.mark.parametrize("dataflow", ["plain", "swiglu"])
+def test_layer_sequence_graph_replays(dataflow):
+    """The fused walk captured in a HIP graph: each replay, on an input written
+    between replays (every other buffer zeroed), equals an eager run on that
+    input bit for bit.  Every launch tags its hand-over words with the
+    workspace's next epoch, read and advanced on the device, so a replay never
+    takes a word the previous one left."""
+    import torch
+    M = 2
+    ops, widths = synth.layer_program(_small_shapes, 3, distinct_buffers=True, dataflow=dataflow)
+    norms, dev_ops = {}, []
+    for o in ops:
+        canon, S = synth.weights(4, o["N"], o["K"], seed=300 + o["matrix"])
+        d = dict(bits=4, prologue=o["prologue"], N=o["N"], K=o["K"], packed=packed_on_device(4, canon, S, o["N"], o["K"]),
+                 in_buf=o["in_buf"], out_buf=o["out_buf"])
+        if "norm_seed" in o:
+            if o["norm_seed"] not in norms:
+                norms[o["norm_seed"]] = dev(synth.norm_weights(o["K"], o["norm_seed"]))
+            d["norm_w"] = norms[o["norm_seed"]]
+        if "in_buf2" in o:
+            d["in_buf2"] = o["in_buf2"]
+        dev_ops.append(d)
+    bufs = [torch.zeros((M, w), dtype=torch.bfloat16, device="cuda") for w in widths]
+    seq = mbq.LayerSequence(dev_ops, bufs, M, fused=True)
+    inputs = [dev(synth.activations(M, widths[0], seed=500 + i)) for i in range(3)]
+
+    def load(i):
+        for b in bufs[1:]:
+            b.zero_()
+        bufs[0].copy_(inputs[i])
+
+    eager = []
+    for i in range(3):
+        load(i)
+        seq.run()
+        seq.check()
+        eager.append([host(b) for b in bufs])
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        seq.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    try:
+        with torch.cuda.graph(g):
+            seq.run()
+    except RuntimeError as e:   # pragma: no cover - depends on the runtime
+        pytest.skip(f"the runtime does not capture the walk's cooperative launch: {e}")
+    for i in (2, 0, 1, 2, 0):
+        load(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        seq.check()
+        for k, (a, b) in enumerate(zip([host(b) for b in bufs], eager[i])):
+            assert np.array_equal(a, b), f"replay of input {i}, buffer {k}"
+
+
 @pytest.mark.parametrize("shapes,M,dataflow", [("27b", 8, "plain"), ("27b", 3, "plain"), ("9b", 4, "swiglu")])
 def test_layer_sequence_shared_gathers_reproducible(shapes, M, dataflow):
     """Where a finalising workgroup's waves share a row block's gather (the o
