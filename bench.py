@@ -176,10 +176,14 @@ def run_attention(args):
         "ms_per_step": round(r["wall_ms"], 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"split-prefix decode attention, 32 query / 4 key-value heads of 256, "
-                               f"{P}-token bf16 cache, M={args.m}", "ctx": P, "M": args.m, **ATTN_SHAPE},
+                               f"{P}-token bf16 cache, M={args.m}", "ctx": P, "M": args.m,
+                   "combine": args.attn_combine, **ATTN_SHAPE},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "decode_attention_kernel, then attn_merge_kernel when the prefix has "
-                               "several splits (timed together per call)", "achieved": round(gbs, 2),
+        "roofline": {"bound": "hbm", "kernel": ("decode_attention_kernel, then attn_merge_kernel when the prefix has "
+                                                 "several splits (timed together per call)")
+                     if args.attn_combine == "kernel" else
+                     "decode_attention_kernel, combining its splits in the same cooperative launch",
+                     "achieved": round(gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": r["kv_bytes"], "launch_ms": round(r["ms"], 4)},
     }
@@ -408,6 +412,9 @@ def main():
     ap.add_argument("--no-linear", action="store_true", help="skip the single-linear measurement")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the stream-read ceiling")
     ap.add_argument("--ctx", type=int, default=32768, help="attention: cached prefix length")
+    ap.add_argument("--attn-combine", default="kernel", choices=["kernel", "inline"],
+                    help="attention: combine the splits in a second kernel (default) or at the end of a "
+                         "cooperative split launch (sets MBQ_ATTN_COMBINE)")
     ap.add_argument("--dataflow", default="plain", choices=["plain", "swiglu"],
                     help="swiglu: weighted RMSNorms before q/k/v and gate/up, silu(gate) * up before down")
     ap.add_argument("--no-cpu", action="store_true")
@@ -428,6 +435,10 @@ def main():
     torch.cuda.set_device(0)
 
     if args.workload == "attention":
+        if args.attn_combine == "inline":
+            os.environ["MBQ_ATTN_COMBINE"] = "inline"
+        else:
+            os.environ.pop("MBQ_ATTN_COMBINE", None)
         run_attention(args)
         return
 

@@ -241,8 +241,15 @@ int mbq_linear_group_acc(int bits, int form, int64_t M, int64_t N, int64_t K, co
  * "Paying attention to the attention!": the grouped-query attention of a decode
  * step for a short query -- the committed token, or it and the MTP draft rows
  * with their causal verification -- without a materialised mask.  The cached
- * prefix is split across many workgroups; a second kernel on the same stream
- * combines their partial softmax results (none when one split covers it).
+ * prefix is split across many workgroups, and a second kernel on the same
+ * stream combines their partial softmax results (none when one split covers
+ * it).  With MBQ_ATTN_COMBINE=inline in the environment at the call, the
+ * splits of each key/value head combine them at the end of the same launch
+ * instead: the launch is cooperative (every split resident), and each split
+ * merges a share of its head's outputs once all have published.  Where the
+ * device will not take that grid at once, the second kernel combines them.
+ * The in-launch combine is the slower of the two here: the cooperative launch
+ * costs more than the second kernel.
  *
  * q: device bf16 [M][n_q][D]; k_cache, v_cache: device bf16 [n_kv][L][D]
  * (row stride D, head stride L * D) holding the M new tokens' keys and values
@@ -251,9 +258,12 @@ int mbq_linear_group_acc(int bits, int form, int64_t M, int64_t N, int64_t K, co
  * scores are scaled by 1/sqrt(D); softmax and sums in fp32.
  * Shapes: M in 1..8, D in {64, 128, 256}, n_q a multiple of n_kv with
  * (n_q / n_kv) * M <= 64, L >= P + M.  q and the caches 16-byte aligned.
- * ws: device, 256-byte aligned, >= mbq_attention_workspace_bytes(...) bytes
- * of scratch for the partial results (any contents; calls sharing a workspace
- * must not overlap).  Enqueued on `stream`. */
+ * ws: device, 256-byte aligned, >= mbq_attention_workspace_bytes(...) bytes:
+ * the partial results (scratch) and, at its start, the in-launch combine's
+ * per-head counters.  Any contents for the default combine; for the in-launch
+ * one, zero-filled before its first use (every completed call leaves the
+ * counters at zero, so one workspace serves calls of any shape in turn).
+ * Calls sharing a workspace must not overlap.  Enqueued on `stream`. */
 int64_t mbq_attention_workspace_bytes(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P);
 int mbq_decode_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P, int64_t L, const void *q,
                          const void *k_cache, const void *v_cache, void *o, void *ws, int64_t ws_bytes,

@@ -196,8 +196,9 @@ def decode_attention(q, k_cache, v_cache, P: int, out=None, ws=None):
     """Split-prefix decode attention: q bf16 [M][n_q][D]; caches bf16 [n_kv][L][D]
     holding the M new tokens' keys and values at positions P .. P+M-1.  Token i
     attends to positions 0 .. P+i.  ws: a uint8 device tensor of at least
-    attention_workspace_bytes(...) bytes (scratch, any contents); allocated here
-    when omitted."""
+    attention_workspace_bytes(...) bytes (any contents, unless MBQ_ATTN_COMBINE=inline
+    selects the in-launch combine: then zero-filled before its first use, and every
+    call leaves its counters at zero); allocated here, zero-filled, when omitted."""
     import torch
     M, n_q, D = q.shape
     n_kv, L, D2 = k_cache.shape

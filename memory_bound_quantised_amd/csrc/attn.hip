@@ -20,12 +20,20 @@
 //            where values cancel), going through LDS to take the operand
 //            layout.
 // Each workgroup publishes (m, l, o) per row (the only split of a head writes
-// the output itself), and a second kernel, wide over (head, output columns),
-// merges the splits: M = max m_s, L = sum l_s 2^(m_s - M), O = sum o_s
-// 2^(m_s - M) / L.  Merging in the split kernel itself -- the last split of a
-// head to finish -- leaves the whole merge to one workgroup, whose round trips
-// at 64 rows x 256 columns cost more than the second launch.
+// the output itself), and the splits are merged: M = max m_s, L = sum l_s
+// 2^(m_s - M), O = sum o_s 2^(m_s - M) / L.  Two combines:
+//   a second kernel (the default), wide over (head, output columns);
+//   in the same launch (MBQ_ATTN_COMBINE=inline in the environment): the
+//     launch is cooperative, so every split is resident; a split counts in on
+//     its head's counter, waits for the head's other splits, and merges a
+//     share of the head's output columns.
+// The cooperative launch alone costs more on this device than the second
+// kernel does, so the second kernel is the default.  (Having the last split
+// of a head merge everything leaves 64 rows x 256 columns over up to 128
+// splits to one workgroup: slower still.)
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 
 #include "mbq.h"
 #include "mbq_internal.h"
@@ -51,6 +59,12 @@ struct AttnArgs {
     int64_t L;                    // cache row stride (positions)
     int32_t M, n_q, n_kv, qpg, rows, P, n_split, blocks_per_split, n_blocks;
     float scale_log2;             // log2(e) / sqrt(D)
+    // The combine inside the launch (a cooperative one: every workgroup is
+    // resident): per kv head g, cnt[32 g] counts the splits that have
+    // published and cnt[32 g + 16] the ones done merging; the last of those
+    // zeroes both.  merge_inline 0: attn_merge_kernel merges afterwards.
+    uint32_t *cnt;
+    int32_t merge_inline, tpq;
 };
 
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
@@ -73,6 +87,156 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += dpp_row<0x4E>(v);
     v += dpp_row<0x141>(v);
     return v + dpp_row<0x140>(v);
+}
+
+struct MergeArgs {
+    const float *part_o, *part_ml;   // as in AttnArgs
+    uint16_t *o;
+    int32_t n_split, rows, qpg, n_q, tpq;
+};
+
+// Loads of the partials: plain, or at agent scope when they were stored in
+// the same launch by other CUs (a plain load could hit a stale cache line).
+template <bool COH>
+__device__ __forceinline__ f4 load_part4(const float *p) {
+    if constexpr (COH) {
+        const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
+        const uint64_t x = load_shared(q), y = load_shared(q + 1);
+        return f4{__uint_as_float((uint32_t)x), __uint_as_float((uint32_t)(x >> 32)),
+                  __uint_as_float((uint32_t)y), __uint_as_float((uint32_t)(y >> 32))};
+    } else {
+        return *reinterpret_cast<const f4 *>(p);
+    }
+}
+template <bool COH>
+__device__ __forceinline__ float load_part(const float *p) {
+    if constexpr (COH) return load_shared(p);
+    else return *p;
+}
+
+// Merge of one chunk of a head's outputs, wide: the chunk is the 256 / tpq
+// groups of four adjacent outputs from output e_lo on; lanes t of a group of
+// tpq consecutive lanes sum splits t, t + tpq, ... (at most 8, so tpq * 8 >=
+// the split count) with one 16-byte load each, and the group adds its lanes'
+// sums.  The weights 2^(m_s - M) / L of the rows the chunk touches (at most
+// 16) are staged first.  Scratch (LDS): w_s, l_s kMaxSplits x kMaxRowsWg
+// floats each, red kMaxRowsWg x 2.  Every thread of the workgroup calls it.
+constexpr int kMaxRowsWg = kAttnThreads * 4 / 64;   // rows a chunk touches, at most
+// a lane sums at most 8 splits and a group has at most 16 lanes
+static_assert(kMaxSplits <= 16 * 8, "the merge covers every split");
+constexpr int kMergeScratchBytes = (2 * kMaxSplits * kMaxRowsWg + 2 * kMaxRowsWg) * 4;
+template <int D, bool COH>
+__device__ __forceinline__ void merge_chunk(const MergeArgs &a, int g, int64_t e_lo, float *w_s, float *l_s,
+                                            float *red) {
+    const int tid = threadIdx.x;
+    const int n = a.n_split, rows = a.rows, tpq = a.tpq;
+    const int groups = kAttnThreads / tpq;
+    const int r_lo = (int)(e_lo / D);
+    const int r_hi = min(rows, (int)((e_lo + groups * 4 - 1) / D) + 1);
+    const int nr = r_hi - r_lo;
+    // the lane's partials (at most 8 splits: tpq * 8 >= n) go out first, so
+    // that their round trip overlaps the weights' one
+    const int64_t e0 = e_lo + (int64_t)(tid / tpq) * 4;   // the group's first output
+    const int t = tid % tpq;
+    const int r = (int)(e0 / D), d = (int)(e0 % D);
+    const bool real = r < rows;
+    f4 v[8];
+    {
+        const float *op = a.part_o + ((int64_t)g * n * rows + (real ? r : 0)) * D + d;
+        const int64_t stride = (int64_t)rows * D;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int s = t + u * tpq;
+            v[u] = real && s < n ? load_part4<COH>(op + s * stride) : f4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    }
+    const float *ml = a.part_ml + (int64_t)g * n * rows * 2;
+    for (int idx = tid; idx < n * nr; idx += kAttnThreads) {
+        const int s = idx / nr, rr = idx % nr;
+        w_s[s * kMaxRowsWg + rr] = load_part<COH>(ml + ((int64_t)s * rows + r_lo + rr) * 2);
+        l_s[s * kMaxRowsWg + rr] = load_part<COH>(ml + ((int64_t)s * rows + r_lo + rr) * 2 + 1);
+    }
+    __syncthreads();
+    {   // a wave per row: its lanes stride over the splits
+        const int lane = tid & 63, wave = tid >> 6;
+        for (int rr = wave; rr < nr; rr += kAttnThreads / 64) {
+            float mx = -INFINITY;
+            for (int s = lane; s < n; s += 64) mx = fmaxf(mx, w_s[s * kMaxRowsWg + rr]);
+            for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            float den = 0.0f;
+            for (int s = lane; s < n; s += 64)
+                if (w_s[s * kMaxRowsWg + rr] != -INFINITY)
+                    den += l_s[s * kMaxRowsWg + rr] * exp2f(w_s[s * kMaxRowsWg + rr] - mx);
+            for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+            if (lane == 0) {
+                red[rr * 2] = mx;
+                red[rr * 2 + 1] = den;
+            }
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < n * nr; idx += kAttnThreads) {
+        const int s = idx / nr, rr = idx % nr;
+        const float mt = w_s[s * kMaxRowsWg + rr];
+        w_s[s * kMaxRowsWg + rr] = mt == -INFINITY ? 0.0f : exp2f(mt - red[rr * 2]) / red[rr * 2 + 1];
+    }
+    __syncthreads();
+    f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (real) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int s = t + u * tpq;
+            if (s < n) acc += w_s[s * kMaxRowsWg + r - r_lo] * v[u];
+        }
+    }
+    for (int off = 1; off < tpq; off <<= 1)   // the group's lanes are consecutive
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
+    if (real && t == 0) {
+        const int i = r / a.qpg, j = r % a.qpg;
+        uint32_t *dst = reinterpret_cast<uint32_t *>(a.o + ((int64_t)i * a.n_q + g * a.qpg + j) * D + d);
+        dst[0] = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+        dst[1] = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+    }
+    __syncthreads();   // the scratch is reused by the next chunk
+}
+
+// The merge inside the split launch: after this split's partials have reached
+// memory it counts in on its head's counter and waits for every split of the
+// head; then the head's chunks are dealt to its splits in turn, and the last
+// split to finish merging zeroes the two counters for the next call.  Every
+// split of the head is resident (cooperative launch), so the wait ends.
+constexpr int64_t kMergeSpinLimit = 1ll << 26;
+template <int D>
+__device__ __forceinline__ void merge_in_launch(const AttnArgs &a, int g, int s, uint8_t *scratch) {
+    uint32_t *arrived = a.cnt + 32 * g, *merged = a.cnt + 32 * g + 16;
+    wait_memory();      // this thread's partial stores have reached memory
+    __syncthreads();    // and every thread's
+    if (threadIdx.x == 0) {
+        counter_add(arrived, 1u);
+        int64_t spins = 0;
+        while (load_shared(arrived) < (uint32_t)a.n_split && ++spins < kMergeSpinLimit) __builtin_amdgcn_s_sleep(2);
+    }
+    __syncthreads();   // the whole workgroup waits for thread 0
+    MergeArgs ma;
+    ma.part_o = a.part_o;
+    ma.part_ml = a.part_ml;
+    ma.o = a.o;
+    ma.n_split = a.n_split;
+    ma.rows = a.rows;
+    ma.qpg = a.qpg;
+    ma.n_q = a.n_q;
+    ma.tpq = a.tpq;
+    float *w_s = reinterpret_cast<float *>(scratch);
+    float *l_s = w_s + kMaxSplits * kMaxRowsWg;
+    float *red = l_s + kMaxSplits * kMaxRowsWg;
+    const int64_t per_chunk = kAttnThreads / a.tpq * 4;
+    const int64_t n_chunks = ((int64_t)a.rows * D + per_chunk - 1) / per_chunk;
+    for (int64_t c = s; c < n_chunks; c += a.n_split) merge_chunk<D, true>(ma, g, c * per_chunk, w_s, l_s, red);
+    if (threadIdx.x == 0 && counter_add(merged, 1u) == (uint32_t)(a.n_split - 1)) {
+        store_shared(arrived, 0u);
+        store_shared(merged, 0u);
+    }
 }
 
 // WPR: waves per 16-row query tile (4, 2 or 1 for up to 16, 32 or 64 rows);
@@ -315,13 +479,27 @@ __device__ __forceinline__ void attention_split(const AttnArgs &a) {
                 for (int c = 0; c < kCtW; ++c) dst[16 * (sw + c * WPR) + lr] = (uint16_t)f32_to_bf16_bits(o[c][j] * inv);
                 continue;
             }
+            float *po = a.part_o + (base + r) * D + 16 * sw + lr, *pml = a.part_ml + (base + r) * 2;
+            if (a.merge_inline) {   // read in this launch, maybe on another XCD: agent scope
 #pragma unroll
-            for (int c = 0; c < kCtW; ++c) a.part_o[(base + r) * D + 16 * (sw + c * WPR) + lr] = o[c][j];
-            if (lr == 0 && sw == 0) {
-                a.part_ml[(base + r) * 2] = m[j];
-                a.part_ml[(base + r) * 2 + 1] = l[j];
+                for (int c = 0; c < kCtW; ++c) store_shared(po + 16 * c * WPR, o[c][j]);
+                if (lr == 0 && sw == 0) {
+                    store_shared(pml, m[j]);
+                    store_shared(pml + 1, l[j]);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < kCtW; ++c) po[16 * c * WPR] = o[c][j];
+                if (lr == 0 && sw == 0) {
+                    pml[0] = m[j];
+                    pml[1] = l[j];
+                }
             }
         }
+    }
+    if (a.merge_inline && a.n_split > 1) {
+        __syncthreads();   // the staging LDS is free: the merge's scratch
+        merge_in_launch<D>(a, g, s, lds);
     }
 }
 
@@ -338,95 +516,14 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2,
     attention_split<D, WPR, BLK>(a);
 }
 
-struct MergeArgs {
-    const float *part_o, *part_ml;   // as in AttnArgs
-    uint16_t *o;
-    int32_t n_split, rows, qpg, n_q, tpq;
-};
-
-// Merge of the splits of one head, wide: lanes t of a group of tpq
-// consecutive lanes sum splits t, t + tpq, ... (at most 8, so tpq * 8 >= the
-// split count) for four adjacent outputs (one 16-byte load each), and the
-// group adds its lanes' sums.  A workgroup covers
-// 256 / tpq such groups; it stages the weights 2^(m_s - M) / L of the rows
-// it touches (at most 16) in LDS first.
-// a lane sums at most 8 splits and a group has at most 16 lanes
-static_assert(kMaxSplits <= 16 * 8, "the merge covers every split");
+// The merge as a second launch: a workgroup per chunk of a head.
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(MergeArgs a) {
-    constexpr int kMaxRowsWg = kAttnThreads * 4 / 64;   // rows a workgroup touches, at most
-    __shared__ float w_s[kMaxSplits][kMaxRowsWg];
-    __shared__ float l_s[kMaxSplits][kMaxRowsWg];
-    __shared__ float red[kMaxRowsWg][2];
-    const int tid = threadIdx.x, g = blockIdx.y;
-    const int n = a.n_split, rows = a.rows, tpq = a.tpq;
-    const int groups = kAttnThreads / tpq;
-    const int64_t e_lo = (int64_t)blockIdx.x * groups * 4;
-    const int r_lo = (int)(e_lo / D);
-    const int r_hi = min(rows, (int)((e_lo + groups * 4 - 1) / D) + 1);
-    const int nr = r_hi - r_lo;
-    // the lane's partials (at most 8 splits: tpq * 8 >= n) go out first, so
-    // that their round trip overlaps the weights' one
-    const int64_t e0 = e_lo + (int64_t)(tid / tpq) * 4;   // the group's first output
-    const int t = tid % tpq;
-    const int r = (int)(e0 / D), d = (int)(e0 % D);
-    const bool real = r < rows;
-    f4 v[8];
-    {
-        const float *op = a.part_o + ((int64_t)g * n * rows + (real ? r : 0)) * D + d;
-        const int64_t stride = (int64_t)rows * D;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int s = t + u * tpq;
-            v[u] = real && s < n ? *reinterpret_cast<const f4 *>(op + s * stride) : f4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-    }
-    const float *ml = a.part_ml + (int64_t)g * n * rows * 2;
-    for (int idx = tid; idx < n * nr; idx += kAttnThreads) {
-        const int s = idx / nr, rr = idx % nr;
-        w_s[s][rr] = ml[((int64_t)s * rows + r_lo + rr) * 2];
-        l_s[s][rr] = ml[((int64_t)s * rows + r_lo + rr) * 2 + 1];
-    }
-    __syncthreads();
-    {   // a wave per row: its lanes stride over the splits
-        const int lane = tid & 63, wave = tid >> 6;
-        for (int rr = wave; rr < nr; rr += kAttnThreads / 64) {
-            float mx = -INFINITY;
-            for (int s = lane; s < n; s += 64) mx = fmaxf(mx, w_s[s][rr]);
-            for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-            float den = 0.0f;
-            for (int s = lane; s < n; s += 64)
-                if (w_s[s][rr] != -INFINITY) den += l_s[s][rr] * exp2f(w_s[s][rr] - mx);
-            for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
-            if (lane == 0) {
-                red[rr][0] = mx;
-                red[rr][1] = den;
-            }
-        }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < n * nr; idx += kAttnThreads) {
-        const int s = idx / nr, rr = idx % nr;
-        const float mt = w_s[s][rr];
-        w_s[s][rr] = mt == -INFINITY ? 0.0f : exp2f(mt - red[rr][0]) / red[rr][1];
-    }
-    __syncthreads();
-    f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (real) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int s = t + u * tpq;
-            if (s < n) acc += w_s[s][r - r_lo] * v[u];
-        }
-    }
-    for (int off = 1; off < tpq; off <<= 1)   // the group's lanes are consecutive
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
-    if (!real || t != 0) return;
-    const int i = r / a.qpg, j = r % a.qpg;
-    uint32_t *dst = reinterpret_cast<uint32_t *>(a.o + ((int64_t)i * a.n_q + g * a.qpg + j) * D + d);
-    dst[0] = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
-    dst[1] = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+    __shared__ float w_s[kMaxSplits * kMaxRowsWg];
+    __shared__ float l_s[kMaxSplits * kMaxRowsWg];
+    __shared__ float red[kMaxRowsWg * 2];
+    const int64_t e_lo = (int64_t)blockIdx.x * (kAttnThreads / a.tpq) * 4;
+    merge_chunk<D, false>(a, blockIdx.y, e_lo, w_s, l_s, red);
 }
 
 }  // namespace
@@ -456,13 +553,19 @@ AttnPlan plan_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t
     // merge: lanes per group of four outputs, so that a lane sums at most 8 splits
     pl.merge_tpq = 1;
     while (pl.merge_tpq < 16 && pl.merge_tpq * 8 < pl.n_split) pl.merge_tpq *= 2;
-    // [m, l per split and row][o per split and row]
+    // [merge counters: 128 bytes per kv head][m, l per split and row][o per split and row]
     const int64_t part_ml = n_kv * pl.n_split * pl.rows * 2 * 4;
     const int64_t part_o = n_kv * pl.n_split * pl.rows * D * 4;
     auto up = [](int64_t v) { return (v + 255) / 256 * 256; };
-    pl.off_ml = 0;
-    pl.off_o = up(part_ml);
+    pl.off_cnt = 0;
+    pl.off_ml = up(n_kv * 128);
+    pl.off_o = pl.off_ml + up(part_ml);
     pl.ws_bytes = pl.off_o + up(part_o);
+    // the combine inside the launch, when asked for, borrows the staging LDS
+    // for its scratch
+    const char *combine = getenv("MBQ_ATTN_COMBINE");
+    pl.merge_inline = combine && strcmp(combine, "inline") == 0 && pl.n_split > 1 &&
+                      pl.lds_bytes >= kMergeScratchBytes;
     return pl;
 }
 
@@ -487,6 +590,8 @@ hipError_t launch_attention(const AttnPlan &pl, int64_t M, int64_t n_q, int64_t 
     a.blocks_per_split = (int32_t)pl.blocks_per_split;
     a.n_blocks = (int32_t)pl.n_blocks;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    a.cnt = (uint32_t *)((char *)ws + pl.off_cnt);
+    a.tpq = (int32_t)pl.merge_tpq;
     const int wpr = pl.rows <= 16 ? 4 : pl.rows <= 32 ? 2 : 1;
 #define MBQ_ATTN(DD)                                                                                   \
     (wpr == 4   ? reinterpret_cast<const void *>(&decode_attention_kernel<DD, 4, 64>)                   \
@@ -497,8 +602,17 @@ hipError_t launch_attention(const AttnPlan &pl, int64_t M, int64_t n_q, int64_t 
     const void *fn = D == 64 ? MBQ_ATTN(64) : D == 128 ? MBQ_ATTN(128) : MBQ_ATTN(256);
 #undef MBQ_ATTN
     void *args[] = {(void *)&a};
-    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)pl.n_split, (unsigned)n_kv), dim3(kAttnThreads), args,
-                                   (size_t)pl.lds_bytes, st);
+    const dim3 grid((unsigned)pl.n_split, (unsigned)n_kv);
+    if (pl.merge_inline) {
+        // one launch: every split resident, the merge at its end
+        a.merge_inline = 1;
+        const hipError_t e =
+            hipLaunchCooperativeKernel(fn, grid, dim3(kAttnThreads), args, (unsigned)pl.lds_bytes, st);
+        if (e == hipSuccess) return e;
+        (void)hipGetLastError();   // refused (the grid does not fit at once): merge in a second launch
+    }
+    a.merge_inline = 0;
+    const hipError_t e = hipLaunchKernel(fn, grid, dim3(kAttnThreads), args, (size_t)pl.lds_bytes, st);
     if (e != hipSuccess || pl.n_split == 1) return e;
     MergeArgs ma;
     ma.part_o = a.part_o;

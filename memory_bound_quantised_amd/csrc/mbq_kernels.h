@@ -56,8 +56,9 @@ struct AttnPlan {
     int64_t block = 64;      // positions per block
     int64_t merge_tpq = 1;   // merge lanes per four outputs
     bool two_per_cu = false; // two workgroups per CU (the split kernel's register-capped form)
-    int64_t off_ml = 0, off_o = 0, ws_bytes = 0;
+    int64_t off_cnt = 0, off_ml = 0, off_o = 0, ws_bytes = 0;
     int lds_bytes = 0;
+    bool merge_inline = false;   // merge the splits at the end of the split launch
 };
 AttnPlan plan_attention(int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P, int n_cu);
 hipError_t launch_attention(const AttnPlan &pl, int64_t M, int64_t n_q, int64_t n_kv, int64_t D, int64_t P,

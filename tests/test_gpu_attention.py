@@ -20,6 +20,17 @@ def _inputs(M, n_q, n_kv, D, L, seed):
     return q, k, v
 
 
+@pytest.fixture(params=["kernel", "inline"])
+def combine(request, monkeypatch):
+    """Both combines of the splits: the second kernel (the default) and the one
+    at the end of a cooperative split launch (MBQ_ATTN_COMBINE=inline)."""
+    if request.param == "inline":
+        monkeypatch.setenv("MBQ_ATTN_COMBINE", "inline")
+    else:
+        monkeypatch.delenv("MBQ_ATTN_COMBINE", raising=False)
+    return request.param
+
+
 def _run(q, k, v, P, ws=None):
     import torch
     out = mbq.decode_attention(dev(q).view(torch.bfloat16), dev(k).view(torch.bfloat16),
@@ -31,7 +42,7 @@ def _run(q, k, v, P, ws=None):
 @pytest.mark.parametrize("P", [0, 1, 63, 64, 65, 200, 1000])
 @pytest.mark.parametrize("M,n_q,n_kv,D", [(1, 1, 1, 64), (1, 8, 1, 128), (2, 4, 2, 256), (3, 6, 3, 64),
                                           (8, 8, 1, 256), (5, 16, 4, 128), (8, 16, 2, 64), (5, 8, 1, 256)])
-def test_decode_attention_matches_oracle(M, n_q, n_kv, D, P):
+def test_decode_attention_matches_oracle(M, n_q, n_kv, D, P, combine):
     L = P + M + 5
     q, k, v = _inputs(M, n_q, n_kv, D, L, seed=P * 31 + M * 7 + D)
     got = _run(q, k, v, P)
@@ -55,23 +66,68 @@ def test_decode_attention_causal_rows_and_heads_exactly():
     assert np.array_equal(got, oracle.decode_attention(q, k, v, P))
 
 
-def test_decode_attention_workspace_reused():
-    """Calls of different P on one workspace, which starts out as garbage."""
+def test_decode_attention_workspace_reused(combine):
+    """Calls of different P (so different split counts, 1 at P = 10) on one
+    workspace -- garbage for the second-kernel combine, zero-filled for the
+    in-launch one, whose counters must be back at zero after every call --
+    and a repeated call gives the same bits."""
     import torch
     M, n_q, n_kv, D = 4, 8, 2, 128
-    need = max(mbq.attention_workspace_bytes(M, n_q, n_kv, D, P) for P in (3000, 10))
-    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
-    for P in (3000, 10, 3000):
+    need = max(mbq.attention_workspace_bytes(M, n_q, n_kv, D, P) for P in (3000, 10, 40000))
+    ws = torch.full((need,), 0 if combine == "inline" else 0xA5, dtype=torch.uint8, device="cuda")
+    first = {}
+    for P in (3000, 10, 40000, 3000, 40000):
         L = P + M
         q, k, v = _inputs(M, n_q, n_kv, D, L, seed=P)
-        assert_close_bf16(_run(q, k, v, P, ws=ws), oracle.decode_attention(q, k, v, P), f"P={P}")
+        got = _run(q, k, v, P, ws=ws)
+        assert_close_bf16(got, oracle.decode_attention(q, k, v, P), f"P={P}")
+        if P in first:
+            assert np.array_equal(got, first[P]), f"P={P} repeated"
+        first[P] = got
 
 
 @pytest.mark.parametrize("M", [1, 4, 8])
-def test_decode_attention_27b_shape(M):
+def test_decode_attention_27b_shape(M, combine):
     """The 27B-shaped attention layer: 32 query heads, 4 key/value heads of 256,
     a 32768-token prefix (M = 4: two row tiles, two workgroups per CU)."""
     n_q, n_kv, D, P = 32, 4, 256, 32768
     L = P + M
     q, k, v = _inputs(M, n_q, n_kv, D, L, seed=77 + M)
     assert_close_bf16(_run(q, k, v, P), oracle.decode_attention(q, k, v, P), f"27B M={M}")
+
+
+def test_decode_attention_graph_replays(combine):
+    """The attention captured in a HIP graph (two launches, or one cooperative
+    launch with the merge inside): replays on queries written between them
+    equal eager calls bit for bit."""
+    import torch
+    M, n_q, n_kv, D, P = 2, 8, 2, 128, 5000
+    L = P + M
+    _, k, v = _inputs(M, n_q, n_kv, D, L, seed=9)
+    kd, vd = dev(k).view(torch.bfloat16), dev(v).view(torch.bfloat16)
+    qs = [dev(_inputs(M, n_q, n_kv, D, 16, seed=40 + i)[0]).view(torch.bfloat16) for i in range(3)]
+    qbuf = torch.empty_like(qs[0])
+    out = torch.empty((M, n_q, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(mbq.attention_workspace_bytes(M, n_q, n_kv, D, P), dtype=torch.uint8, device="cuda")
+    eager = []
+    for qi in qs:
+        qbuf.copy_(qi)
+        mbq.decode_attention(qbuf, kd, vd, P, out=out, ws=ws)
+        torch.cuda.synchronize()
+        eager.append(host(out))
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mbq.decode_attention(qbuf, kd, vd, P, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        mbq.decode_attention(qbuf, kd, vd, P, out=out, ws=ws)
+    for i in (1, 0, 2, 1):
+        qbuf.copy_(qs[i])
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), eager[i]), f"replay of query {i}"
