@@ -855,24 +855,30 @@ struct Slot {
     uint32_t hdr;   // the run header if this tile opens a run, else 0
 };
 
-// Tiles each loader keeps in flight (the CU's two loaders together): enough
-// bytes per CU for the bus to stay busy (about 32-40 KiB per CU reached the
-// stream ceiling), few enough that a poll from the same CU is not queued
-// behind a long line of weight loads.
+// Tiles each loader keeps in flight: enough bytes per CU for the bus to stay
+// busy, few enough that a poll from the same CU is not queued behind a long
+// line of weight loads.  Measured on 27B- and 9B-shaped walks: W4 3 tiles up
+// to four rows (4 cost 0.5-1 %, 2 cost 5 %), 4 from five rows on (3 cost
+// 1.7 % at M = 8); W6 2 tiles (3 cost 1 % at M = 1 and 3).
 // The window also fixes the vector-memory wait after each tile, so it must
 // stay within the 63-op counter: (tiles - 1) x loads per tile <= 63.
-#ifndef MBQ_LOADER_TILES_W4
-#define MBQ_LOADER_TILES_W4 4
-#endif
-#ifndef MBQ_LOADER_TILES_W6
-#define MBQ_LOADER_TILES_W6 3
-#endif
-template <int BITS>
-constexpr int loader_window() { return BITS == 4 ? MBQ_LOADER_TILES_W4 : MBQ_LOADER_TILES_W6; }
+constexpr int loader_window_of(int bits, int m) { return bits == 4 ? (m <= 4 ? 3 : 4) : 2; }
+template <int BITS, int M>
+constexpr int loader_window() { return loader_window_of(BITS, M); }
 template <int BITS>
 constexpr int loads_per_tile() { return Layout<BITS>::kSlabs + 1; }
-static_assert((loader_window<4>() - 1) * loads_per_tile<4>() <= kVmemLimit, "loader window within vmcnt");
-static_assert((loader_window<6>() - 1) * loads_per_tile<6>() <= kVmemLimit, "loader window within vmcnt");
+// The loader's wait takes one of two immediates: every window is the one of
+// M = 1 or the one of M = kMaxM, and the latter is the largest.
+constexpr bool two_windows(int bits) {
+    const int lo = loader_window_of(bits, 1), hi = loader_window_of(bits, kMaxM);
+    for (int m = 1; m <= kMaxM; ++m)
+        if (loader_window_of(bits, m) != lo && loader_window_of(bits, m) != hi) return false;
+    return lo <= hi;
+}
+static_assert(two_windows(4) && two_windows(6), "loader windows");
+static_assert((loader_window<4, kMaxM>() - 1) * loads_per_tile<4>() <= kVmemLimit &&
+                  (loader_window<6, kMaxM>() - 1) * loads_per_tile<6>() <= kVmemLimit,
+              "loader window within vmcnt");
 constexpr int kLdsDmaNt = 2;
 // Offset of a tile's LDS/global base from its start: the slabs and scales lie
 // within +-kDmaMid of it, inside the instruction offset's range (+-4 KiB).
@@ -949,12 +955,13 @@ __device__ __forceinline__ void take_tile(const SeqPlan *P, const Lay &L, int wi
 // were issued, and every tile after it waits until at most loader_window
 // tiles are in flight, so by then it has landed.
 template <int BITS>
-__device__ void loader(const SeqPlan *P, const Lay &L, int wg, int lane, int w0) {
+__device__ void loader(const SeqPlan *P, const Lay &L, int wg, int lane, int w0, int wt) {
     using Lt = Layout<BITS>;
     constexpr int T = Lt::kTileBytes;
     constexpr int NL = loads_per_tile<BITS>();
-    constexpr int WT = loader_window<BITS>();
-    static_assert(kRecHalf >= WT, "a record block lands before it is used");
+    // the window: loader_window<BITS, M>, a constant where the kernel calls this
+    constexpr int WT_MAX = loader_window<BITS, kMaxM>();
+    static_assert(kRecHalf >= WT_MAX, "a record block lands before it is used");
     const int S = L.ring_slots;
     const SeqWave *wtab = cload(&P->wtab);
     const SeqRun *runs0 = cload(&P->runs);
@@ -985,8 +992,8 @@ __device__ void loader(const SeqPlan *P, const Lay &L, int wg, int lane, int w0)
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     // Compute wave of each tile in flight, oldest in the low bits: 2 bits per
-    // tile, at most WT <= 32 tiles.
-    static_assert(WT <= 32 && kSeqFed <= 4, "in-flight order fits 64 bits");
+    // tile, at most 32 tiles.
+    static_assert(WT_MAX <= 32 && kSeqFed <= 4, "in-flight order fits 64 bits");
     uint64_t order = 0;
     int seq = 0, pub = 0;
     int64_t spins = 0;
@@ -1035,8 +1042,9 @@ __device__ void loader(const SeqPlan *P, const Lay &L, int wg, int lane, int w0)
             slot[w] = slot[w] + 1 == S ? 0 : slot[w] + 1;
             order |= (uint64_t)w << (2 * (seq - pub));
             ++seq;
-            if (seq - pub >= WT) {
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL * (WT - 1)));   // the oldest tile has landed
+            if (seq - pub >= wt) {   // the oldest tile has landed
+                if (wt == WT_MAX) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL * (WT_MAX - 1)));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL * (loader_window<BITS, 1>() - 1)));
                 publish_oldest();
             }
             any = true;
@@ -1223,7 +1231,7 @@ __global__ __launch_bounds__(kSeqBlock) void seq_kernel(const SeqPlan *__restric
     }
     __syncthreads();   // the only barrier the loader joins
     if (wi >= kSeqWaves) {
-        loader<BITS>(P, L, wg, lane, (wi - kSeqWaves) * kSeqFed);
+        loader<BITS>(P, L, wg, lane, (wi - kSeqWaves) * kSeqFed, loader_window<BITS, M>());
         return;
     }
 
