@@ -192,8 +192,9 @@ int mbq_w6a8_linear(int64_t M, int64_t N, int64_t K, const int8_t *q, const floa
  *   ws        device workspace, 256-byte aligned, of
  *             mbq_linear_prologue_workspace_bytes(bits, M, N, K) bytes,
  *             zero-filled before its first use (as for the linear).
- * Where the linear's one-workgroup-per-row-block form applies (48..256 row
- * blocks of 64 rows, K up to 8192) every workgroup runs the prologue and the
+ * Where the linear's one-workgroup-per-row-block form applies (up to 512
+ * row blocks of 64 rows, and K up to 6144 or at least 48 row blocks and K up
+ * to 20480) and M x K is at most 143360, every workgroup runs the prologue and the
  * quantisation on the rows into its LDS and reads its activation codes from
  * there: one launch, nothing written but y.  Other shapes run the prologue
  * and quantisation as a launch of their own into the workspace first.  The

@@ -35,15 +35,14 @@ constexpr int kTargetWaves = 2048;   // about 8 waves per CU on 256 CUs
 #endif
 constexpr int kTilesPerWave = MBQ_LIN_TILES;   // a split's tiles, at least (when the matrix has enough)
 constexpr int kMaxSplits = 16;       // a row block's partials, at most
-#ifndef MBQ_LIN_RB_MIN_BLOCKS
-#define MBQ_LIN_RB_MIN_BLOCKS 48
-#endif
-#ifndef MBQ_LIN_RB_MAX_BLOCKS
-#define MBQ_LIN_RB_MAX_BLOCKS 256
-#endif
-#ifndef MBQ_LIN_RB_MAX_GROUPS
-#define MBQ_LIN_RB_MAX_GROUPS 64
-#endif
+// Shapes of the row-block form (see plan_linear).
+constexpr int64_t kRbAnyBlocksGroups = 48;   // any row-block count up to this many k groups
+constexpr int64_t kRbMinBlocks = 48;         // more groups: at least this many row blocks,
+constexpr int64_t kRbMaxGroups = 160;        // and at most this many groups
+constexpr int64_t kRbMaxBlocks = 512;
+// The form with the prologue inside keeps the M x K activation codes in LDS,
+// next to at most 16 KiB of the kernel's own.
+constexpr int64_t kRbPrologueMaxCodes = 140 * 1024;
 #ifndef MBQ_LIN_MFMA_MIN_M
 #define MBQ_LIN_MFMA_MIN_M 1
 #endif
@@ -532,12 +531,16 @@ LinearPlan plan_linear(int bits, int64_t M, int64_t N, int64_t K) {
     if (sp < 1) sp = 1;
     p.splits = sp;
     p.ws_bytes = kCounterBytes + (sp > 1 ? p.n_rb * sp * M * 64 * 4 : 0);
-    // The row-block form where the row blocks fill most of the chip in one
-    // round (a second round of workgroups costs more than the split form's
-    // combine) and each wave's k range is a few tiles (its pipeline is two
-    // batches deep).
-    p.rb_form = p.n_rb >= MBQ_LIN_RB_MIN_BLOCKS && p.n_rb <= MBQ_LIN_RB_MAX_BLOCKS &&
-                p.groups <= MBQ_LIN_RB_MAX_GROUPS;
+    // The row-block form (a workgroup per row block, no partials, no combine)
+    // wherever one workgroup's share stays modest or the row blocks fill most
+    // of the chip; the split form's combine costs a counter and a gather round
+    // trip.  Measured against the split form (M = 1 / 4, per call in a graph):
+    // 1024 x 5120 5.7 / 6.3 against 7.3 / 9.2 us, 17408 x 5120 12.4 / 13.5
+    // against 13.5 / 15.6 us, 5120 x 17408 15.2 / 16.3 against 15.5 / 18.6 us.
+    // A few row blocks over many groups (a workgroup streaming half a MB
+    // alone) stay split.
+    p.rb_form = p.n_rb <= kRbMaxBlocks &&
+                (p.groups <= kRbAnyBlocksGroups || (p.n_rb >= kRbMinBlocks && p.groups <= kRbMaxGroups));
     return p;
 }
 
@@ -555,7 +558,7 @@ int64_t linear_prologue_ws_bytes(int bits, int64_t M, int64_t N, int64_t K) {
 hipError_t launch_linear_prologue(int bits, int pro, int64_t M, int64_t N, int64_t K, const void *x, const void *u,
                                   const void *w, const void *packed, void *y, void *ws, hipStream_t st) {
     const LinearPlan plan = plan_linear(bits, M, N, K);
-    if (plan.rb_form) {
+    if (plan.rb_form && M * K <= kRbPrologueMaxCodes) {
         const uint8_t *pk = (const uint8_t *)packed;
         uint16_t *yv = (uint16_t *)y;
         const uint16_t *xs = (const uint16_t *)x, *us = (const uint16_t *)u, *wn = (const uint16_t *)w;
@@ -581,7 +584,7 @@ hipError_t launch_linear_prologue(int bits, int pro, int64_t M, int64_t N, int64
 #undef MBQ_RBF
         return hipGetLastError();
     }
-    // other shapes: the prologue kernel, then the split linear, through the workspace
+    // other shapes: the prologue kernel, then the linear, through the workspace
     int8_t *q = (int8_t *)ws;
     float *s = (float *)((char *)ws + (M * K + 255) / 256 * 256);
     void *lin_ws = (char *)ws + (M * K + 255) / 256 * 256 + 256;

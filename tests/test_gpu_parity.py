@@ -210,7 +210,10 @@ def test_group_acc_extreme_codes(bits, form, lo_code, q_val):
 
 @pytest.mark.parametrize("bits", [4, 6])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
-@pytest.mark.parametrize("N,K", [(1, 128), (200, 1152), (1000, 4096), (4096, 4096)])
+# the row-block form (the first four) and the split form (a few row blocks over
+# many k groups; more than 512 row blocks)
+@pytest.mark.parametrize("N,K", [(1, 128), (200, 1152), (1000, 4096), (4096, 4096), (1000, 8192), (200, 17408),
+                                 (33000, 256)])
 def test_linear_vs_oracle(bits, M, N, K):
     canon, S = synth.weights(bits, N, K, seed=1)
     x = synth.activations(M, K)
@@ -219,8 +222,8 @@ def test_linear_vs_oracle(bits, M, N, K):
     assert_close_bf16(host(y), oracle.linear(bits, q, s, canon, S), f"W{bits} M={M} {N}x{K}")
 
 
-# The row-block form of the linear (one workgroup per 64-row block, 48..256
-# blocks, up to 64 k groups): its edges.  3070 x 4224: 48 blocks, the last one
+# The row-block form of the linear (one workgroup per 64-row block, no
+# partials): its edges.  3070 x 4224: 48 blocks, the last one
 # 62 rows, 33 groups over 16 or 8 waves (uneven ranges, some past the
 # all-at-once count, so through the batched loop); 16384 x 128: 256 blocks of
 # one group (most waves idle); 3100 x 8192: 64 groups over 4 waves (batched).
@@ -237,13 +240,15 @@ def test_linear_row_block_form_vs_oracle(bits, M, N, K):
 
 # The linear with its prologue and quantisation inside it: bitwise the
 # quantisation call followed by the linear (every prologue; 4096 x 4096 and
-# 3070 x 4224 take the row-block form with 16 or 8 waves, 5120 x 8192 the one
-# with 4 waves and batched ranges, 1024 x 5120 the prologue launch and the
-# split form).
+# 3070 x 4224 take the row-block form with 16 or 8 waves, 5120 x 8192,
+# 1024 x 5120 and 5120 x 17408 the one with 4 waves and batched ranges).
 @pytest.mark.parametrize("bits", [4, 6])
 @pytest.mark.parametrize("prologue", [0, 1, 2, 3])
 @pytest.mark.parametrize("M", [1, 3, 8])
-@pytest.mark.parametrize("N,K", [(4096, 4096), (3070, 4224), (5120, 8192), (1024, 5120)])
+# fused (M x K codes in LDS) except 4096 x 20480 at M = 8 (more codes than the
+# LDS holds: the prologue kernel first) and 1000 x 8192 (the split form)
+@pytest.mark.parametrize("N,K", [(4096, 4096), (3070, 4224), (5120, 8192), (1024, 5120), (5120, 17408),
+                                 (4096, 20480), (1000, 8192)])
 def test_linear_prologue_matches_quantise_then_linear(bits, prologue, M, N, K):
     canon, S = synth.weights(bits, N, K, seed=N + K + prologue)
     packed = packed_on_device(bits, canon, S, N, K)
