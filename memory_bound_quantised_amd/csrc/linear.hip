@@ -40,6 +40,7 @@ constexpr int64_t kRbAnyBlocksGroups = 48;   // any row-block count up to this m
 constexpr int64_t kRbMinBlocks = 48;         // more groups: at least this many row blocks,
 constexpr int64_t kRbMaxGroups = 160;        // and at most this many groups
 constexpr int64_t kRbMaxBlocks = 512;
+constexpr int64_t kRsMaxBlocks = 64;         // the row-set form up to this many row blocks
 // The form with the prologue inside keeps the M x K activation codes in LDS,
 // next to at most 16 KiB of the kernel's own.
 constexpr int64_t kRbPrologueMaxCodes = 140 * 1024;
@@ -221,9 +222,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void linear_kernel(
 // ping-pong pair of register sets.  Loads are unconditional, at an index
 // clamped into the range, so that none is waited for early; the repeats of
 // the last tile hit the cache and are never summed.
-// (W, SHOT) per shape, measured on 4096 x 4096, 16384 x 5120 and 5120 x 8192
-// (each within its registers without spills):
-//   k groups <= 32: 16 x 2 for W4 up to three rows, else 8 x 4;
+// (W, SHOT) per shape, never per row count, so that row m of an M-row call
+// sums in the same order as the one-row call; measured on 4096 x 4096,
+// 16384 x 5120, 5120 x 8192 and 8192 .. 32000 x 1024 .. 4096:
+//   k groups <= 32: W4 16 x 2 (8 x 4 was 5-10 % slower at one row and 10-22 %
+//                   slower at four, although 16 waves spill 8 registers from
+//                   four rows on), W6 8 x 4 (16 waves spill 50-120 registers);
 //   more k groups:   4 x 8 (a wave's longer range keeps more tiles in flight).
 template <int BITS>
 constexpr int rb_batch() { return 2; }
@@ -283,6 +287,36 @@ __device__ __forceinline__ float rb_quant_row(int8_t *q_row, const uint16_t *x, 
     return quant_row<PRO, NT, false>(x, u, wn, K, red_d, red_f, put, none);
 }
 
+// The workgroup's own prologue `pro` (an MBQ_PRO_* value) and quantisation
+// of the bf16 rows x (and u, wn) into q_lds (M x K codes) and s_lds.
+template <int M, int W>
+__device__ __forceinline__ void rb_prologue(int8_t *q_lds, float *s_lds, int K, int pro, const uint16_t *x,
+                                            const uint16_t *u, const uint16_t *wn) {
+    __shared__ double red_d[W];
+    __shared__ float red_f[W];
+    for (int m = 0; m < M; ++m) {
+        int8_t *qr = q_lds + (int64_t)m * K;
+        const uint16_t *xr = x + (int64_t)m * K, *ur = u ? u + (int64_t)m * K : nullptr;
+        float sc;
+        switch (pro) {
+            case MBQ_PRO_RMSNORM_QUANT:
+                sc = rb_quant_row<MBQ_PRO_RMSNORM_QUANT, 64 * W>(qr, xr, ur, wn, K, red_d, red_f);
+                break;
+            case MBQ_PRO_WRMSNORM_QUANT:
+                sc = rb_quant_row<MBQ_PRO_WRMSNORM_QUANT, 64 * W>(qr, xr, ur, wn, K, red_d, red_f);
+                break;
+            case MBQ_PRO_SWIGLU_QUANT:
+                sc = rb_quant_row<MBQ_PRO_SWIGLU_QUANT, 64 * W>(qr, xr, ur, wn, K, red_d, red_f);
+                break;
+            default:
+                sc = rb_quant_row<MBQ_PRO_QUANT, 64 * W>(qr, xr, ur, wn, K, red_d, red_f);
+                break;
+        }
+        if (threadIdx.x == 0) s_lds[m] = sc;
+    }
+    __syncthreads();
+}
+
 // QF false: q and s come quantised from global memory.  QF true: the
 // workgroup runs prologue `pro` (an MBQ_PRO_* value) and the quantisation on
 // the bf16 rows x (and u, wn) itself, into dynamic LDS (M x K codes), first.
@@ -298,31 +332,7 @@ __global__ __launch_bounds__(64 * W) void linear_rb_kernel(
     __shared__ float red[W][M][64];
     __shared__ float s_lds[M];
     extern __shared__ __align__(16) int8_t q_lds[];
-    if constexpr (QF) {
-        __shared__ double red_d[W];
-        __shared__ float red_f[W];
-        for (int m = 0; m < M; ++m) {
-            int8_t *qr = q_lds + (int64_t)m * K;
-            const uint16_t *xr = x + (int64_t)m * K, *ur = u ? u + (int64_t)m * K : nullptr;
-            float sc;
-            switch (pro) {
-                case MBQ_PRO_RMSNORM_QUANT:
-                    sc = rb_quant_row<MBQ_PRO_RMSNORM_QUANT, 64 * W>(qr, xr, ur, wn, K, red_d, red_f);
-                    break;
-                case MBQ_PRO_WRMSNORM_QUANT:
-                    sc = rb_quant_row<MBQ_PRO_WRMSNORM_QUANT, 64 * W>(qr, xr, ur, wn, K, red_d, red_f);
-                    break;
-                case MBQ_PRO_SWIGLU_QUANT:
-                    sc = rb_quant_row<MBQ_PRO_SWIGLU_QUANT, 64 * W>(qr, xr, ur, wn, K, red_d, red_f);
-                    break;
-                default:
-                    sc = rb_quant_row<MBQ_PRO_QUANT, 64 * W>(qr, xr, ur, wn, K, red_d, red_f);
-                    break;
-            }
-            if (threadIdx.x == 0) s_lds[m] = sc;
-        }
-        __syncthreads();
-    }
+    if constexpr (QF) rb_prologue<M, W>(q_lds, s_lds, K, pro, x, u, wn);
     const int lane = threadIdx.x & 63;
     const int w = uniform(threadIdx.x >> 6);
     const int rb = blockIdx.x;
@@ -383,6 +393,141 @@ __global__ __launch_bounds__(64 * W) void linear_rb_kernel(
     }
 }
 
+// Row-set form: one workgroup per (row block, row set).  A 64-row tile holds
+// its rows in four sets of 16 (rows 4n + i, n = 0..15: W4 slab i, W6 dwords
+// 6i .. 6i + 5 of each lane, a slab and a half), and the products of set i
+// need only those bytes, so four workgroups share a row block without any
+// combine: each loads a quarter of every tile (plus the tile's scales of its
+// rows) and issues a quarter of the products.  A matrix of few row blocks so
+// spreads over four times the CUs.  Waves split the k groups as in the
+// row-block form and their sums are added in wave order; each output row sums
+// its groups in the same order as the row-block form with the same W.
+template <int BITS, int TB>
+struct RsBatch {
+    v4i w[TB];           // W4: the row set's slab; W6: its 16-byte part
+    v2u w2[TB];          // W6: its 8-byte part (unused for W4)
+    uint32_t sc[TB];     // fp16 bits of the lane's row scale
+    v4i a0[TB], a1[TB];
+};
+
+template <int BITS, int TB, bool QLDS>
+__device__ __forceinline__ void rs_load(RsBatch<BITS, TB> &b, const uint8_t *tiles, int off16, int off8, int offsc,
+                                        const v4i *qrow, const __attribute__((address_space(3))) v4i *qlds, int gb,
+                                        int g_last) {
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+        const int g = min(gb + u, g_last);
+        const uint8_t *t = tiles + (int64_t)g * Layout<BITS>::kTileBytes;
+        b.w[u] = load_stream(reinterpret_cast<const v4i *>(t + off16));
+        if constexpr (BITS == 6) b.w2[u] = __builtin_nontemporal_load(gptr(reinterpret_cast<const v2u *>(t + off8)));
+        b.sc[u] = __builtin_nontemporal_load(gptr(reinterpret_cast<const uint16_t *>(t + offsc)));
+        if constexpr (QLDS) {
+            b.a0[u] = qlds[g * 8];
+            b.a1[u] = qlds[g * 8 + 1];
+        } else {
+            b.a0[u] = *gptr(qrow + g * 8);
+            b.a1[u] = *gptr(qrow + g * 8 + 1);
+        }
+    }
+}
+
+template <int BITS, int TB, int AR>
+__device__ __forceinline__ void rs_sum(const RsBatch<BITS, TB> &b, bool odd, int gb, int g1, float (&facc)[AR]) {
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+        if (gb + u < g1) {
+            v4i h0, h1;
+            if constexpr (BITS == 4) {
+                h0 = unpack_row_w4(b.w[u], 0);
+                h1 = unpack_row_w4(b.w[u], 1);
+            } else {
+                // the set's six dwords: 16-byte part first for even sets, 8-byte part first for odd
+                const v4i w = b.w[u];
+                const v2u v = b.w2[u];
+                const uint32_t d0 = odd ? v.x : w.x, d1 = odd ? v.y : w.y, d2 = odd ? w.x : w.z;
+                const uint32_t d3 = odd ? w.y : w.w, d4 = odd ? w.z : v.x, d5 = odd ? w.w : v.y;
+                h0 = unpack_row_w6(d0, d1, d2);
+                h1 = unpack_row_w6(d3, d4, d5);
+            }
+            const v4i z = {0, 0, 0, 0};
+            v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(b.a0[u], h0, z, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(b.a1[u], h1, acc, 0, 0, 0);
+            const float S = f16_bits_to_f32(b.sc[u] & 0xFFFFu);
+#pragma unroll
+            for (int j = 0; j < AR; ++j) facc[j] = fmaf((float)acc[j], S, facc[j]);
+        }
+    }
+}
+
+template <int BITS, int M, int W, int SHOT, bool QF>
+__global__ __launch_bounds__(64 * W) void linear_rs_kernel(
+    const uint8_t *__restrict__ packed, const int8_t *__restrict__ q, const float *__restrict__ s,
+    uint16_t *__restrict__ y, int64_t y_stride, int N, int K, int pro, const uint16_t *__restrict__ x,
+    const uint16_t *__restrict__ u, const uint16_t *__restrict__ wn) {
+    using L = Layout<BITS>;
+    constexpr int TB = rb_batch<BITS>();
+    constexpr int AR = M > 4 ? 4 : M;
+    __shared__ float red[W][M][16];
+    __shared__ float s_lds[M];
+    extern __shared__ __align__(16) int8_t q_lds[];
+    if constexpr (QF) rb_prologue<M, W>(q_lds, s_lds, K, pro, x, u, wn);
+    const int lane = threadIdx.x & 63;
+    const int w = uniform(threadIdx.x >> 6);
+    const int rb = blockIdx.x >> 2, set = blockIdx.x & 3;
+    const int G = K >> 7;
+    const int g0 = (int)((int64_t)G * w / W), g1 = (int)((int64_t)G * (w + 1) / W);
+    const uint8_t *tiles = packed + (int64_t)rb * G * L::kTileBytes;
+    // the set's bytes in a lane: W4 slab `set`; W6 a 16-byte part (slab 0, 2,
+    // 3 or 5) and an 8-byte part (half of slab 1 or 4)
+    const int off16 = (BITS == 4 ? set : (set == 0 ? 0 : set == 1 ? 2 : set == 2 ? 3 : 5)) * kSlab + lane * 16;
+    const int off8 = (set < 2 ? 1 : 4) * kSlab + lane * 16 + (set & 1) * 8;
+    const int offsc = L::kWeightBytes + 2 * (4 * (lane & 15) + set);
+    const bool odd = set & 1;
+    // lane l sums weight row 4 (l & 15) + set for activation rows 4 (l >> 4) + j
+    const int am = (lane & 15) < M ? (lane & 15) : 0;
+    const v4i *qrow = QF ? nullptr : reinterpret_cast<const v4i *>(q + (int64_t)am * K + (lane >> 4) * 32);
+    const __attribute__((address_space(3))) v4i *qlds =
+        reinterpret_cast<const __attribute__((address_space(3))) v4i *>(
+            (const __attribute__((address_space(3))) int8_t *)q_lds + (int64_t)am * K + (lane >> 4) * 32);
+    float facc[AR];
+#pragma unroll
+    for (int j = 0; j < AR; ++j) facc[j] = 0.0f;
+    if (g1 - g0 > 0 && g1 - g0 <= SHOT) {
+        RsBatch<BITS, SHOT> A;
+        rs_load<BITS, SHOT, QF>(A, tiles, off16, off8, offsc, qrow, qlds, g0, g1 - 1);
+        rs_sum<BITS, SHOT, AR>(A, odd, g0, g1, facc);
+    } else if (g1 - g0 > SHOT) {
+        RsBatch<BITS, TB> A, B;
+        rs_load<BITS, TB, QF>(A, tiles, off16, off8, offsc, qrow, qlds, g0, g1 - 1);
+        for (int gb = g0;;) {
+            rs_load<BITS, TB, QF>(B, tiles, off16, off8, offsc, qrow, qlds, gb + TB, g1 - 1);
+            rs_sum<BITS, TB, AR>(A, odd, gb, g1, facc);
+            gb += TB;
+            if (gb >= g1) break;
+            rs_load<BITS, TB, QF>(A, tiles, off16, off8, offsc, qrow, qlds, gb + TB, g1 - 1);
+            rs_sum<BITS, TB, AR>(B, odd, gb, g1, facc);
+            gb += TB;
+            if (gb >= g1) break;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < AR; ++j) {
+        const int m = 4 * (lane >> 4) + j;
+        if (m < M) red[w][m][lane & 15] = facc[j];
+    }
+    __syncthreads();
+    const float unscale = 1.0f / (float)(1 << L::kAccShift);   // exact power of two
+    for (int t = threadIdx.x; t < M * 16; t += 64 * W) {
+        const int m = t >> 4, r = t & 15;
+        float tot = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < W; ++ww) tot += red[ww][m][r];
+        const int n = rb * 64 + 4 * r + set;
+        const float sm = QF ? s_lds[m] : s[m];
+        if (n < N) y[m * y_stride + n] = (uint16_t)f32_to_bf16_bits(sm * (tot * unscale));
+    }
+}
+
 // Exact int32 group sums for the tests: one wave per tile, through the same
 // tile functions the product runs.  MFMA = true: mfma_tile_regs, the form of
 // the per-op linear (every M) and of the fused walk from two rows on, with
@@ -436,13 +581,40 @@ void launch_rb(const uint8_t *pk, const int8_t *q, const float *s, uint16_t *y, 
     if (groups > 32) {
         linear_rb_kernel<BITS, M, 4, 8, QF><<<grid, dim3(64 * 4), lds, st>>>(pk, q, s, y, y_stride, (int)N, (int)K,
                                                                              pro, x, u, wn);
-    } else if constexpr (BITS == 4 && M <= 3) {
+    } else if constexpr (BITS == 4) {
         linear_rb_kernel<BITS, M, 16, 2, QF><<<grid, dim3(64 * 16), lds, st>>>(pk, q, s, y, y_stride, (int)N,
                                                                                (int)K, pro, x, u, wn);
     } else {
         linear_rb_kernel<BITS, M, 8, 4, QF><<<grid, dim3(64 * 8), lds, st>>>(pk, q, s, y, y_stride, (int)N, (int)K,
                                                                              pro, x, u, wn);
     }
+}
+
+// Row-set form: W = 16 waves whatever M is, so a row's sum order never
+// depends on the row count; up to 2 or 4 tiles per wave at once, longer
+// ranges in two-deep batches.
+template <int BITS, int M, bool QF>
+void launch_rs(const uint8_t *pk, const int8_t *q, const float *s, uint16_t *y, int64_t y_stride, int64_t N,
+               int64_t K, int64_t n_rb, int64_t groups, int pro, const uint16_t *x, const uint16_t *u,
+               const uint16_t *wn, hipStream_t st) {
+    const dim3 grid((unsigned)(n_rb * 4));
+    const size_t lds = QF ? (size_t)(M * K) : 0;
+    if (groups <= 32)
+        linear_rs_kernel<BITS, M, 16, 2, QF><<<grid, dim3(64 * 16), lds, st>>>(pk, q, s, y, y_stride, (int)N, (int)K,
+                                                                               pro, x, u, wn);
+    else
+        linear_rs_kernel<BITS, M, 16, 4, QF><<<grid, dim3(64 * 16), lds, st>>>(pk, q, s, y, y_stride, (int)N, (int)K,
+                                                                               pro, x, u, wn);
+}
+
+template <int BITS, int M, bool QF>
+void launch_rows(const LinearPlan &plan, const uint8_t *pk, const int8_t *q, const float *s, uint16_t *y,
+                 int64_t y_stride, int64_t N, int64_t K, int pro, const uint16_t *x, const uint16_t *u,
+                 const uint16_t *wn, hipStream_t st) {
+    if (plan.rs_form)
+        launch_rs<BITS, M, QF>(pk, q, s, y, y_stride, N, K, plan.n_rb, plan.groups, pro, x, u, wn, st);
+    else
+        launch_rb<BITS, M, QF>(pk, q, s, y, y_stride, N, K, plan.n_rb, plan.groups, pro, x, u, wn, st);
 }
 
 template <int BITS>
@@ -452,7 +624,7 @@ hipError_t launch_linear_bits(int64_t M, int64_t N, int64_t K, const int8_t *q, 
     const uint8_t *pk = (const uint8_t *)packed;
     uint16_t *yv = (uint16_t *)y;
     if (plan.rb_form) {
-#define MBQ_RB(MM) launch_rb<BITS, MM, false>(pk, q, s, yv, y_stride, N, K, plan.n_rb, plan.groups, 0, nullptr, nullptr, nullptr, st)
+#define MBQ_RB(MM) launch_rows<BITS, MM, false>(plan, pk, q, s, yv, y_stride, N, K, 0, nullptr, nullptr, nullptr, st)
         switch (M) {
             case 1: MBQ_RB(1); break;
             case 2: MBQ_RB(2); break;
@@ -541,6 +713,11 @@ LinearPlan plan_linear(int bits, int64_t M, int64_t N, int64_t K) {
     // alone) stay split.
     p.rb_form = p.n_rb <= kRbMaxBlocks &&
                 (p.groups <= kRbAnyBlocksGroups || (p.n_rb >= kRbMinBlocks && p.groups <= kRbMaxGroups));
+    // Four workgroups per row block (the row-set form) while they fit the
+    // chip in one round: 4096 x 4096 4.4 / 4.6 against 5.2 / 6.3 us at M = 1
+    // / 4, 1024 x 5120 5.3 / 5.6 against 5.7 / 6.3 us; at 80 and more row
+    // blocks it was 13-90 % slower.
+    p.rs_form = p.rb_form && p.n_rb <= kRsMaxBlocks;
     return p;
 }
 
@@ -562,8 +739,7 @@ hipError_t launch_linear_prologue(int bits, int pro, int64_t M, int64_t N, int64
         const uint8_t *pk = (const uint8_t *)packed;
         uint16_t *yv = (uint16_t *)y;
         const uint16_t *xs = (const uint16_t *)x, *us = (const uint16_t *)u, *wn = (const uint16_t *)w;
-#define MBQ_RBF(B, MM) \
-    launch_rb<B, MM, true>(pk, nullptr, nullptr, yv, N, N, K, plan.n_rb, plan.groups, pro, xs, us, wn, st)
+#define MBQ_RBF(B, MM) launch_rows<B, MM, true>(plan, pk, nullptr, nullptr, yv, N, N, K, pro, xs, us, wn, st)
 #define MBQ_RBF_M(B)                   \
     switch (M) {                       \
         case 1: MBQ_RBF(B, 1); break;  \

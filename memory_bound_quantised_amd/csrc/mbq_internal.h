@@ -220,15 +220,25 @@ __device__ __forceinline__ void dot_tile_w6(const v4i (&w)[6], Act act, int (&ac
 // activation rows j = 0..3 of weight row 4 * l + i.  Rows past M cost nothing
 // extra: a 16-row product is one instruction whatever M is.
 
-// The lane's unpacked weights (2^kAccShift * w) of row i, k half h (k = 32s +
-// 16h + 0..15, in order) as four int8x4 dwords.
+// The lane's unpacked weights (2^kAccShift * w) of one row set, k half h
+// (k = 32s + 16h + 0..15, in order) as four int8x4 dwords.  A row set's bytes
+// in a lane: W4 the four dwords of one slab; W6 six consecutive dwords of the
+// lane's 24 (row set i: dwords 6i .. 6i + 5, a slab and a half).
+__device__ __forceinline__ v4i unpack_row_w4(v4i slab, int h) {
+    const uint32_t d0 = (uint32_t)(h ? slab.z : slab.x), d1 = (uint32_t)(h ? slab.w : slab.y);
+    return v4i{(int)((d0 << 4) & 0xF0F0F0F0u), (int)(d0 & 0xF0F0F0F0u), (int)((d1 << 4) & 0xF0F0F0F0u),
+               (int)(d1 & 0xF0F0F0F0u)};
+}
+__device__ __forceinline__ v4i unpack_row_w6(uint32_t x0, uint32_t x1, uint32_t x2) {
+    const uint32_t m6 = 0xFCFCFCFCu;
+    return v4i{(int)(x0 & m6), (int)(x1 & m6), (int)(x2 & m6),
+               (int)(((x0 << 6) & 0xC0C0C0C0u) | ((x1 << 4) & 0x30303030u) | ((x2 << 2) & 0x0C0C0C0Cu))};
+}
+// The same for row i of a whole tile held in registers.
 template <int BITS>
 __device__ __forceinline__ v4i unpack_half(const v4i (&w)[Layout<BITS>::kSlabs], int i, int h) {
     if constexpr (BITS == 4) {
-        const uint32_t wd[4] = {(uint32_t)w[i].x, (uint32_t)w[i].y, (uint32_t)w[i].z, (uint32_t)w[i].w};
-        const uint32_t d0 = wd[2 * h], d1 = wd[2 * h + 1];
-        return v4i{(int)((d0 << 4) & 0xF0F0F0F0u), (int)(d0 & 0xF0F0F0F0u), (int)((d1 << 4) & 0xF0F0F0F0u),
-                   (int)(d1 & 0xF0F0F0F0u)};
+        return unpack_row_w4(w[i], h);
     } else {
         uint32_t wd[24];
 #pragma unroll
@@ -238,10 +248,7 @@ __device__ __forceinline__ v4i unpack_half(const v4i (&w)[Layout<BITS>::kSlabs],
             wd[4 * j + 2] = (uint32_t)w[j].z;
             wd[4 * j + 3] = (uint32_t)w[j].w;
         }
-        const uint32_t x0 = wd[6 * i + 3 * h], x1 = wd[6 * i + 3 * h + 1], x2 = wd[6 * i + 3 * h + 2];
-        const uint32_t m6 = 0xFCFCFCFCu;
-        return v4i{(int)(x0 & m6), (int)(x1 & m6), (int)(x2 & m6),
-                   (int)(((x0 << 6) & 0xC0C0C0C0u) | ((x1 << 4) & 0x30303030u) | ((x2 << 2) & 0x0C0C0C0Cu))};
+        return unpack_row_w6(wd[6 * i + 3 * h], wd[6 * i + 3 * h + 1], wd[6 * i + 3 * h + 2]);
     }
 }
 

@@ -85,6 +85,7 @@ struct LinearPlan {
     int64_t splits;    // waves per row block (k ranges)
     int64_t ws_bytes;  // counters + fp32 partials
     bool rb_form;      // one workgroup per row block, no partials (splits unused)
+    bool rs_form;      // with rb_form: four workgroups per row block, one per row set
 };
 LinearPlan plan_linear(int bits, int64_t M, int64_t N, int64_t K);
 hipError_t launch_linear(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,

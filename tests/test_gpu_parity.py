@@ -222,14 +222,16 @@ def test_linear_vs_oracle(bits, M, N, K):
     assert_close_bf16(host(y), oracle.linear(bits, q, s, canon, S), f"W{bits} M={M} {N}x{K}")
 
 
-# The row-block form of the linear (one workgroup per 64-row block, no
-# partials): its edges.  3070 x 4224: 48 blocks, the last one
-# 62 rows, 33 groups over 16 or 8 waves (uneven ranges, some past the
-# all-at-once count, so through the batched loop); 16384 x 128: 256 blocks of
-# one group (most waves idle); 3100 x 8192: 64 groups over 4 waves (batched).
+# The forms without partials: their edges.  Row-set form (four workgroups per
+# row block, at most 64 blocks): 3070 x 4224, 48 blocks, the last one 62 rows,
+# 33 groups over 16 waves (uneven ranges); 3100 x 8192, 64 groups (ranges past
+# the all-at-once count, so through the batched loop).  Row-block form:
+# 16384 x 128, 256 blocks of one group (most waves idle); 8190 x 4096, 128
+# blocks, the last one 62 rows, 32 groups over 16 (W4) or 8 (W6) waves;
+# 4200 x 8320, 66 blocks, 65 groups over 4 waves (batched, uneven).
 @pytest.mark.parametrize("bits", [4, 6])
 @pytest.mark.parametrize("M", [1, 3, 4, 8])
-@pytest.mark.parametrize("N,K", [(3070, 4224), (16384, 128), (3100, 8192)])
+@pytest.mark.parametrize("N,K", [(3070, 4224), (3100, 8192), (16384, 128), (8190, 4096), (4200, 8320)])
 def test_linear_row_block_form_vs_oracle(bits, M, N, K):
     canon, S = synth.weights(bits, N, K, seed=N ^ K)
     x = synth.activations(M, K)
@@ -239,9 +241,10 @@ def test_linear_row_block_form_vs_oracle(bits, M, N, K):
 
 
 # The linear with its prologue and quantisation inside it: bitwise the
-# quantisation call followed by the linear (every prologue; 4096 x 4096 and
-# 3070 x 4224 take the row-block form with 16 or 8 waves, 5120 x 8192,
-# 1024 x 5120 and 5120 x 17408 the one with 4 waves and batched ranges).
+# quantisation call followed by the linear (every prologue; 4096 x 4096,
+# 3070 x 4224 and 1024 x 5120 take the row-set form, 5120 x 8192,
+# 5120 x 17408 and 4096 x 20480 the row-block form with 4 waves and batched
+# ranges).
 @pytest.mark.parametrize("bits", [4, 6])
 @pytest.mark.parametrize("prologue", [0, 1, 2, 3])
 @pytest.mark.parametrize("M", [1, 3, 8])
@@ -288,19 +291,25 @@ def test_linear_full_size_sampled(bits, M, N, K):
     assert_close_bf16(y[:, rows], ref, f"W{bits} M={M} {N}x{K}")
 
 
+# Row m of an M-row call is bitwise the one-row call, in every form: the
+# row-set form (3000 x 5120: 47 row blocks), the row-block form with 16 (W4)
+# or 8 (W6) waves (8192 x 1024) and with 4 (8192 x 8192), and the split form
+# (1000 x 8192).
 @pytest.mark.parametrize("bits", [4, 6])
-def test_linear_rows_independent_and_deterministic(bits):
-    N, K = 3000, 5120
+@pytest.mark.parametrize("M", [3, 4, 8])
+@pytest.mark.parametrize("N,K", [(3000, 5120), (8192, 1024), (8192, 8192), (1000, 8192)])
+def test_linear_rows_independent_and_deterministic(bits, M, N, K):
     canon, S = synth.weights(bits, N, K, seed=9)
     packed = packed_on_device(bits, canon, S, N, K)
-    x = synth.activations(3, K)
+    x = synth.activations(M, K)
     q, s = oracle.quantize_act(x)
-    y3 = host(mbq.linear(bits, dev(q), dev(s), packed, N))
-    y3b = host(mbq.linear(bits, dev(q), dev(s), packed, N))
-    assert np.array_equal(y3, y3b)
-    for m in range(3):
+    y = host(mbq.linear(bits, dev(q), dev(s), packed, N))
+    yb = host(mbq.linear(bits, dev(q), dev(s), packed, N))
+    assert np.array_equal(y, yb)
+    for m in range(M):
         ym = host(mbq.linear(bits, dev(q[m:m + 1]), dev(s[m:m + 1]), packed, N))
-        assert np.array_equal(ym, y3[m:m + 1])
+        assert np.array_equal(ym, y[m:m + 1]), f"W{bits} {N}x{K} row {m} of {M}"
+
 
 
 def test_linear_zero_row():
