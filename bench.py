@@ -455,7 +455,12 @@ def main():
                "unit": "GB/s", "n_gpus": 1, "steps": 8, "warmup": 1, "ms_per_step": r["linear_us"] / 1e3,
                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
                "data": "synthetic", "config": {"workload": r["workload"]}, "linear": r,
-               "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+               "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+               "roofline": {"bound": "hbm", "kernel": "linear_rs_kernel (row-set form: four workgroups per "
+                                                     "64-row block, one launch per call)",
+                            "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                            "bytes_per_launch": r["weight_bytes_per_call"], "launch_us": r["linear_us"]}}
         if ceiling:
             out["ceiling"] = ceiling
             out["pct_of_ceiling"] = round(100 * gbs / ceiling["GB/s_best"], 2)
