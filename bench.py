@@ -77,6 +77,36 @@ def build_set(mbq, set_name, bits, n_layers, dataflow="plain"):
     return ops, widths, dev_ops
 
 
+def time_sequence_graph(mbq, dev_ops, widths, M, reps):
+    """Milliseconds per step of the one-launch-per-op walk captured once in a HIP
+    graph and replayed (event-timed): the per-op launches without host gaps."""
+    import torch
+    bufs = [torch.zeros((M, w), dtype=torch.bfloat16, device="cuda") for w in widths]
+    bufs[0].copy_(to_dev(synth.activations(M, widths[0])))
+    seq = mbq.LayerSequence(dev_ops, bufs, M, fused=False)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        seq.run()                       # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        seq.run()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        g.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    for b in bufs:
+        assert torch.isfinite(b.float()).all(), "non-finite output in the captured unfused walk"
+    return float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+
+
 def time_sequence(mbq, dev_ops, widths, M, steps, warmup, fused=True):
     import torch
     bufs = [torch.zeros((M, w), dtype=torch.bfloat16, device="cuda") for w in widths]
@@ -493,6 +523,10 @@ def main():
     if args.unfused:
         log(f"timing the unfused walk at M={args.m}")
         unfused = time_sequence(mbq, dev_ops, widths, args.m, max(3, args.steps // 4), 1, fused=False)
+        try:
+            unfused["graph_ms"] = time_sequence_graph(mbq, dev_ops, widths, args.m, max(3, args.steps // 4))
+        except Exception as e:   # pragma: no cover - depends on the runtime
+            log(f"capturing the unfused walk failed: {e}")
     main_r = results[args.m]
     t_s = main_r["event_ms_median"] / 1e3
     gbs = wbytes / t_s / 1e9
@@ -528,6 +562,9 @@ def main():
     if unfused is not None:
         out["unfused_walk"] = {"event_ms_median": round(unfused["event_ms_median"], 4),
                                "GB/s": round(wbytes / (unfused["event_ms_median"] / 1e3) / 1e9, 2)}
+        if "graph_ms" in unfused:
+            out["unfused_walk"]["graph_ms"] = round(unfused["graph_ms"], 4)
+            out["unfused_walk"]["graph_GB/s"] = round(wbytes / (unfused["graph_ms"] / 1e3) / 1e9, 2)
     # One step is one launch of the persistent walk kernel, timed with HIP events
     # recorded on the stream it is launched on.
     out["roofline"] = {"bound": "hbm", "kernel": "seq_kernel (fused decode-step walk, 1 launch per step)",
