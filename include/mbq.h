@@ -227,14 +227,17 @@ int mbq_linear_noalloc(int bits, int64_t M, int64_t N, int64_t K, const int8_t *
 
 /* The exact int32 group sums acc[m][n][g] (device int32 [M][N][K/128]) that the
  * linears rescale, for tests.  `form` picks the tile code that produces them,
- * each being the very function the product runs:
- *   MBQ_FORM_MFMA  the matrix-core tile (v_mfma_i32_16x16x64_i8, activation rows
- *                  padded to 16): mbq_w4a8_linear / mbq_w6a8_linear at every M,
- *                  and the fused walk from M = 2 on;
- *   MBQ_FORM_DOT4  the v_dot4 tile with its four 32-k slice sums added in int32:
- *                  the fused walk at M = 1.
+ * each being the very functions the product runs:
+ *   MBQ_FORM_MFMA    the whole-tile matrix-core code (v_mfma_i32_16x16x64_i8,
+ *                    activation rows padded to 16): the linear's split and
+ *                    row-block forms and the fused walk, at every M;
+ *   MBQ_FORM_ROWSET  the row-set code of the linear's row-set form (the tile's
+ *                    four sets of 16 rows loaded, unpacked and multiplied one
+ *                    set at a time);
+ *   MBQ_FORM_DOT4    the v_dot4 tile with its four 32-k slice sums added in
+ *                    int32 (a second form, not on the product's path).
  * Returns MBQ_ERR_SHAPE for any other form. */
-enum { MBQ_FORM_DOT4 = 0, MBQ_FORM_MFMA = 1 };
+enum { MBQ_FORM_DOT4 = 0, MBQ_FORM_MFMA = 1, MBQ_FORM_ROWSET = 2 };
 int mbq_linear_group_acc(int bits, int form, int64_t M, int64_t N, int64_t K, const int8_t *q,
                          const void *packed, int32_t *acc, void *stream);
 

@@ -301,12 +301,13 @@ def w6a8_linear(q, s, packed, N, ws=None, out=None):
     return linear(6, q, s, packed, N, ws, out)
 
 
-FORM_DOT4, FORM_MFMA = 0, 1
+FORM_DOT4, FORM_MFMA, FORM_ROWSET = 0, 1, 2
 
 
 def linear_group_acc(bits: int, q, packed, N: int, form: int = FORM_MFMA):
     """Exact int32 group sums [M][N][K/128] through the product's tile code:
-    form=FORM_MFMA (the linears, the walk from M=2) or FORM_DOT4 (the walk at M=1)."""
+    form=FORM_MFMA (the whole-tile code of the linears and the walk), FORM_ROWSET (the
+    linear's row-set form) or FORM_DOT4 (the v_dot4 tile, off the product's path)."""
     import torch
     M, K = q.shape
     acc = torch.empty((M, N, K // 128), dtype=torch.int32, device=q.device)

@@ -264,13 +264,13 @@ int mbq_linear_noalloc(int bits, int64_t M, int64_t N, int64_t K, const int8_t *
 int mbq_linear_group_acc(int bits, int form, int64_t M, int64_t N, int64_t K, const int8_t *q,
                          const void *packed, int32_t *acc, void *stream) {
     if (!bits_ok(bits)) return MBQ_ERR_BITS;
-    if (form != MBQ_FORM_DOT4 && form != MBQ_FORM_MFMA) return MBQ_ERR_SHAPE;
+    if (form != MBQ_FORM_DOT4 && form != MBQ_FORM_MFMA && form != MBQ_FORM_ROWSET) return MBQ_ERR_SHAPE;
     if (!q || !packed || !acc) return MBQ_ERR_NULL;
     if (!m_ok(M) || !n_ok(N) || !k_ok(K)) return MBQ_ERR_SHAPE;
     if (!aligned(packed, 256) || !aligned(q, 16) || !aligned(acc, 4)) return MBQ_ERR_ALIGN;
     int st = check_device();
     if (st) return st;
-    hipError_t e = launch_group_acc(bits, form == MBQ_FORM_MFMA, M, N, K, q, packed, acc, (hipStream_t)stream);
+    hipError_t e = launch_group_acc(bits, form, M, N, K, q, packed, acc, (hipStream_t)stream);
     return e == hipSuccess ? MBQ_OK : hip_fail(e);
 }
 

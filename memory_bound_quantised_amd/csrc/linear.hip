@@ -402,6 +402,37 @@ __global__ __launch_bounds__(64 * W) void linear_rb_kernel(
 // spreads over four times the CUs.  Waves split the k groups as in the
 // row-block form and their sums are added in wave order; each output row sums
 // its groups in the same order as the row-block form with the same W.
+// Where row set `set` lies in a lane's share of a tile: W4 the 16 bytes of
+// slab `set`; W6 a 16-byte part (slab 0, 2, 3 or 5) and an 8-byte part (a half
+// of slab 1 or 4) that hold its six dwords, the 8-byte part first for odd
+// sets; offsc: the byte of the fp16 scale of the lane's row 4 (lane & 15) + set.
+struct RowsetAt {
+    int off16, off8, offsc;
+    bool odd;
+};
+template <int BITS>
+__device__ __forceinline__ RowsetAt rowset_at(int set, int lane) {
+    RowsetAt r;
+    r.off16 = (BITS == 4 ? set : (set == 0 ? 0 : set == 1 ? 2 : set == 2 ? 3 : 5)) * kSlab + lane * 16;
+    r.off8 = (set < 2 ? 1 : 4) * kSlab + lane * 16 + (set & 1) * 8;
+    r.offsc = Layout<BITS>::kWeightBytes + 2 * (4 * (lane & 15) + set);
+    r.odd = set & 1;
+    return r;
+}
+// The set's two unpacked k halves from its bytes (v unused for W4).
+template <int BITS>
+__device__ __forceinline__ void rowset_unpack(v4i w, v2u v, bool odd, v4i &h0, v4i &h1) {
+    if constexpr (BITS == 4) {
+        h0 = unpack_row_w4(w, 0);
+        h1 = unpack_row_w4(w, 1);
+    } else {
+        const uint32_t d0 = odd ? v.x : w.x, d1 = odd ? v.y : w.y, d2 = odd ? w.x : w.z;
+        const uint32_t d3 = odd ? w.y : w.w, d4 = odd ? w.z : v.x, d5 = odd ? w.w : v.y;
+        h0 = unpack_row_w6(d0, d1, d2);
+        h1 = unpack_row_w6(d3, d4, d5);
+    }
+}
+
 template <int BITS, int TB>
 struct RsBatch {
     v4i w[TB];           // W4: the row set's slab; W6: its 16-byte part
@@ -411,16 +442,17 @@ struct RsBatch {
 };
 
 template <int BITS, int TB, bool QLDS>
-__device__ __forceinline__ void rs_load(RsBatch<BITS, TB> &b, const uint8_t *tiles, int off16, int off8, int offsc,
+__device__ __forceinline__ void rs_load(RsBatch<BITS, TB> &b, const uint8_t *tiles, const RowsetAt &at,
                                         const v4i *qrow, const __attribute__((address_space(3))) v4i *qlds, int gb,
                                         int g_last) {
 #pragma unroll
     for (int u = 0; u < TB; ++u) {
         const int g = min(gb + u, g_last);
         const uint8_t *t = tiles + (int64_t)g * Layout<BITS>::kTileBytes;
-        b.w[u] = load_stream(reinterpret_cast<const v4i *>(t + off16));
-        if constexpr (BITS == 6) b.w2[u] = __builtin_nontemporal_load(gptr(reinterpret_cast<const v2u *>(t + off8)));
-        b.sc[u] = __builtin_nontemporal_load(gptr(reinterpret_cast<const uint16_t *>(t + offsc)));
+        b.w[u] = load_stream(reinterpret_cast<const v4i *>(t + at.off16));
+        if constexpr (BITS == 6)
+            b.w2[u] = __builtin_nontemporal_load(gptr(reinterpret_cast<const v2u *>(t + at.off8)));
+        b.sc[u] = __builtin_nontemporal_load(gptr(reinterpret_cast<const uint16_t *>(t + at.offsc)));
         if constexpr (QLDS) {
             b.a0[u] = qlds[g * 8];
             b.a1[u] = qlds[g * 8 + 1];
@@ -437,21 +469,8 @@ __device__ __forceinline__ void rs_sum(const RsBatch<BITS, TB> &b, bool odd, int
     for (int u = 0; u < TB; ++u) {
         if (gb + u < g1) {
             v4i h0, h1;
-            if constexpr (BITS == 4) {
-                h0 = unpack_row_w4(b.w[u], 0);
-                h1 = unpack_row_w4(b.w[u], 1);
-            } else {
-                // the set's six dwords: 16-byte part first for even sets, 8-byte part first for odd
-                const v4i w = b.w[u];
-                const v2u v = b.w2[u];
-                const uint32_t d0 = odd ? v.x : w.x, d1 = odd ? v.y : w.y, d2 = odd ? w.x : w.z;
-                const uint32_t d3 = odd ? w.y : w.w, d4 = odd ? w.z : v.x, d5 = odd ? w.w : v.y;
-                h0 = unpack_row_w6(d0, d1, d2);
-                h1 = unpack_row_w6(d3, d4, d5);
-            }
-            const v4i z = {0, 0, 0, 0};
-            v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(b.a0[u], h0, z, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(b.a1[u], h1, acc, 0, 0, 0);
+            rowset_unpack<BITS>(b.w[u], b.w2[u], odd, h0, h1);
+            const v4i acc = mfma_rowset(b.a0[u], b.a1[u], h0, h1);
             const float S = f16_bits_to_f32(b.sc[u] & 0xFFFFu);
 #pragma unroll
             for (int j = 0; j < AR; ++j) facc[j] = fmaf((float)acc[j], S, facc[j]);
@@ -477,12 +496,7 @@ __global__ __launch_bounds__(64 * W) void linear_rs_kernel(
     const int G = K >> 7;
     const int g0 = (int)((int64_t)G * w / W), g1 = (int)((int64_t)G * (w + 1) / W);
     const uint8_t *tiles = packed + (int64_t)rb * G * L::kTileBytes;
-    // the set's bytes in a lane: W4 slab `set`; W6 a 16-byte part (slab 0, 2,
-    // 3 or 5) and an 8-byte part (half of slab 1 or 4)
-    const int off16 = (BITS == 4 ? set : (set == 0 ? 0 : set == 1 ? 2 : set == 2 ? 3 : 5)) * kSlab + lane * 16;
-    const int off8 = (set < 2 ? 1 : 4) * kSlab + lane * 16 + (set & 1) * 8;
-    const int offsc = L::kWeightBytes + 2 * (4 * (lane & 15) + set);
-    const bool odd = set & 1;
+    const RowsetAt at = rowset_at<BITS>(set, lane);
     // lane l sums weight row 4 (l & 15) + set for activation rows 4 (l >> 4) + j
     const int am = (lane & 15) < M ? (lane & 15) : 0;
     const v4i *qrow = QF ? nullptr : reinterpret_cast<const v4i *>(q + (int64_t)am * K + (lane >> 4) * 32);
@@ -494,18 +508,18 @@ __global__ __launch_bounds__(64 * W) void linear_rs_kernel(
     for (int j = 0; j < AR; ++j) facc[j] = 0.0f;
     if (g1 - g0 > 0 && g1 - g0 <= SHOT) {
         RsBatch<BITS, SHOT> A;
-        rs_load<BITS, SHOT, QF>(A, tiles, off16, off8, offsc, qrow, qlds, g0, g1 - 1);
-        rs_sum<BITS, SHOT, AR>(A, odd, g0, g1, facc);
+        rs_load<BITS, SHOT, QF>(A, tiles, at, qrow, qlds, g0, g1 - 1);
+        rs_sum<BITS, SHOT, AR>(A, at.odd, g0, g1, facc);
     } else if (g1 - g0 > SHOT) {
         RsBatch<BITS, TB> A, B;
-        rs_load<BITS, TB, QF>(A, tiles, off16, off8, offsc, qrow, qlds, g0, g1 - 1);
+        rs_load<BITS, TB, QF>(A, tiles, at, qrow, qlds, g0, g1 - 1);
         for (int gb = g0;;) {
-            rs_load<BITS, TB, QF>(B, tiles, off16, off8, offsc, qrow, qlds, gb + TB, g1 - 1);
-            rs_sum<BITS, TB, AR>(A, odd, gb, g1, facc);
+            rs_load<BITS, TB, QF>(B, tiles, at, qrow, qlds, gb + TB, g1 - 1);
+            rs_sum<BITS, TB, AR>(A, at.odd, gb, g1, facc);
             gb += TB;
             if (gb >= g1) break;
-            rs_load<BITS, TB, QF>(A, tiles, off16, off8, offsc, qrow, qlds, gb + TB, g1 - 1);
-            rs_sum<BITS, TB, AR>(B, odd, gb, g1, facc);
+            rs_load<BITS, TB, QF>(A, tiles, at, qrow, qlds, gb + TB, g1 - 1);
+            rs_sum<BITS, TB, AR>(B, at.odd, gb, g1, facc);
             gb += TB;
             if (gb >= g1) break;
         }
@@ -529,11 +543,13 @@ __global__ __launch_bounds__(64 * W) void linear_rs_kernel(
 }
 
 // Exact int32 group sums for the tests: one wave per tile, through the same
-// tile functions the product runs.  MFMA = true: mfma_tile_regs, the form of
-// the per-op linear (every M) and of the fused walk from two rows on, with
-// the activation halves loaded exactly as the linear loads them; false:
-// group_sums_dot, the v_dot4 form of the fused walk at one row.
-template <int BITS, int M, bool MFMA>
+// tile functions the product runs.  FORM 1: mfma_tile_regs, the whole-tile
+// form of the per-op linear's split and row-block forms and of the fused
+// walk, with the activation halves loaded exactly as the linear loads them;
+// FORM 2: the row-set form's loads (rowset_at), unpack (rowset_unpack) and
+// products (mfma_rowset), one row set after another; FORM 0: group_sums_dot,
+// the v_dot4 form the walk is built with when MBQ_MFMA_MIN_M is raised.
+template <int BITS, int M, int FORM>
 __global__ __launch_bounds__(64) void group_acc_kernel(const uint8_t *__restrict__ packed,
                                                        const int8_t *__restrict__ q,
                                                        int32_t *__restrict__ acc_out, int N, int K) {
@@ -542,10 +558,32 @@ __global__ __launch_bounds__(64) void group_acc_kernel(const uint8_t *__restrict
     const int tile = blockIdx.x;
     const int rb = tile / G, g = tile % G;
     const int lane = threadIdx.x;
+    if constexpr (FORM == 2) {
+        const int am = (lane & 15) < M ? (lane & 15) : 0;
+        const v4i *qrow = reinterpret_cast<const v4i *>(q + (int64_t)am * K + (lane >> 4) * 32);
+        const v4i a0 = *gptr(qrow + g * 8), a1 = *gptr(qrow + g * 8 + 1);
+        const uint8_t *t = packed + (int64_t)tile * L::kTileBytes;
+#pragma unroll
+        for (int set = 0; set < 4; ++set) {
+            const RowsetAt at = rowset_at<BITS>(set, lane);
+            const v4i wq = *gptr(reinterpret_cast<const v4i *>(t + at.off16));
+            const v2u wv = BITS == 6 ? *gptr(reinterpret_cast<const v2u *>(t + at.off8)) : v2u{0u, 0u};
+            v4i h0, h1;
+            rowset_unpack<BITS>(wq, wv, at.odd, h0, h1);
+            const v4i acc = mfma_rowset(a0, a1, h0, h1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = 4 * (lane >> 4) + j;
+                const int n = rb * 64 + 4 * (lane & 15) + set;
+                if (m < M && n < N) acc_out[((int64_t)m * N + n) * G + g] = acc[j] >> L::kAccShift;
+            }
+        }
+        return;
+    }
     v4i w[L::kSlabs];
     v2u sb;
     load_tile<BITS>(packed + (int64_t)tile * L::kTileBytes, lane, w, sb);
-    if constexpr (MFMA) {
+    if constexpr (FORM == 1) {
         const int am = (lane & 15) < M ? (lane & 15) : 0;
         const v4i *qrow = reinterpret_cast<const v4i *>(q + (int64_t)am * K + (lane >> 4) * 32);
         v4i acc[4];
@@ -662,12 +700,12 @@ hipError_t launch_linear_bits(int64_t M, int64_t N, int64_t K, const int8_t *q, 
     return hipGetLastError();
 }
 
-template <int BITS, bool MFMA>
+template <int BITS, int FORM>
 hipError_t launch_group_acc_form(int64_t M, int64_t N, int64_t K, const int8_t *q, const void *packed,
                                  int32_t *acc, hipStream_t st) {
     const dim3 grid((unsigned)(row_blocks(N) * (K / kGroup)));
     const uint8_t *p = (const uint8_t *)packed;
-#define MBQ_GA(MM) group_acc_kernel<BITS, MM, MFMA><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K)
+#define MBQ_GA(MM) group_acc_kernel<BITS, MM, FORM><<<grid, 64, 0, st>>>(p, q, acc, (int)N, (int)K)
     switch (M) {
         case 1: MBQ_GA(1); break;
         case 2: MBQ_GA(2); break;
@@ -769,13 +807,15 @@ hipError_t launch_linear_prologue(int bits, int pro, int64_t M, int64_t N, int64
     return launch_linear(bits, M, N, K, q, s, packed, y, N, lin_ws, plan, st);
 }
 
-hipError_t launch_group_acc(int bits, bool mfma, int64_t M, int64_t N, int64_t K, const int8_t *q,
+hipError_t launch_group_acc(int bits, int form, int64_t M, int64_t N, int64_t K, const int8_t *q,
                             const void *packed, int32_t *acc, hipStream_t st) {
     if (bits == 4)
-        return mfma ? launch_group_acc_form<4, true>(M, N, K, q, packed, acc, st)
-                    : launch_group_acc_form<4, false>(M, N, K, q, packed, acc, st);
-    return mfma ? launch_group_acc_form<6, true>(M, N, K, q, packed, acc, st)
-                : launch_group_acc_form<6, false>(M, N, K, q, packed, acc, st);
+        return form == 2 ? launch_group_acc_form<4, 2>(M, N, K, q, packed, acc, st)
+               : form == 1 ? launch_group_acc_form<4, 1>(M, N, K, q, packed, acc, st)
+                           : launch_group_acc_form<4, 0>(M, N, K, q, packed, acc, st);
+    return form == 2 ? launch_group_acc_form<6, 2>(M, N, K, q, packed, acc, st)
+           : form == 1 ? launch_group_acc_form<6, 1>(M, N, K, q, packed, acc, st)
+                       : launch_group_acc_form<6, 0>(M, N, K, q, packed, acc, st);
 }
 
 }  // namespace mbq

@@ -258,15 +258,17 @@ __device__ __forceinline__ v4i unpack_half(const v4i (&w)[Layout<BITS>::kSlabs],
 // (row lane & 15 of the group's k slice lane >> 4).  This is the one
 // matrix-core implementation: the per-op linear, the fused walk and the
 // group-sum test entry point all call it.
+// The two products of one row set (its unpacked k halves h0, h1).
+__device__ __forceinline__ v4i mfma_rowset(v4i a0, v4i a1, v4i h0, v4i h1) {
+    const v4i z = {0, 0, 0, 0};
+    const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, h0, z, 0, 0, 0);
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, h1, acc, 0, 0, 0);
+}
 template <int BITS>
 __device__ __forceinline__ void mfma_tile_regs(const v4i (&w)[Layout<BITS>::kSlabs], v4i a0, v4i a1,
                                                v4i (&acc)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const v4i z = {0, 0, 0, 0};
-        acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, unpack_half<BITS>(w, i, 0), z, 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, unpack_half<BITS>(w, i, 1), acc[i], 0, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i) acc[i] = mfma_rowset(a0, a1, unpack_half<BITS>(w, i, 0), unpack_half<BITS>(w, i, 1));
 }
 // The same with the lane's activation slice read from memory at qa.
 template <int BITS>

@@ -101,7 +101,7 @@ int64_t noalloc_scratch_bytes();
 int linear_noalloc(int bits, int64_t M, int64_t N, int64_t K, const int8_t *q, const float *s,
                    const void *packed, void *y, hipStream_t st, hipError_t *hip_err);
 // Exact int32 group sums through the matrix-core (mfma) or v_dot4 tile form.
-hipError_t launch_group_acc(int bits, bool mfma, int64_t M, int64_t N, int64_t K, const int8_t *q,
+hipError_t launch_group_acc(int bits, int form, int64_t M, int64_t N, int64_t K, const int8_t *q,
                             const void *packed, int32_t *acc, hipStream_t st);
 
 // HBM stream-read ceiling (ceiling.hip): one pass over bytes (a multiple of 1 KiB).

@@ -80,7 +80,7 @@ def test_linear_argument_validation():
     assert L.mbq_linear_workspace_bytes(7, 1, 64, 128) == -3
     assert L.mbq_linear_group_acc(5, 1, 1, 64, 128, A, A, A, None) == -3
     assert L.mbq_linear_group_acc(4, 1, 1, 64, 128, None, A, A, None) == -1
-    assert L.mbq_linear_group_acc(4, 2, 1, 64, 128, A, A, A, None) == -2    # no such tile form
+    assert L.mbq_linear_group_acc(4, 3, 1, 64, 128, A, A, A, None) == -2    # no such tile form
     assert L.mbq_linear_group_acc(4, 0, 9, 64, 128, A, A, A, None) == -2
 
 

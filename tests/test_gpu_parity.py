@@ -156,11 +156,12 @@ def test_pack_pads_rows_with_zeros(bits):
 # ---------------------------------------------------------------- exact integer sums
 #
 # mbq_linear_group_acc runs the product's own tile functions: FORM_MFMA is the
-# matrix-core tile of the per-op linears (every M) and of the walk from M = 2,
-# FORM_DOT4 the v_dot4 tile of the walk at M = 1.  Both must give the exact
-# integer sums.
+# whole-tile matrix-core code of the per-op linear's split and row-block forms
+# and of the walk (every M), FORM_ROWSET the row-set form's (each set of 16
+# rows loaded, unpacked and multiplied on its own), FORM_DOT4 the v_dot4 tile.
+# Each must give the exact integer sums.
 
-FORMS = [mbq.FORM_DOT4, mbq.FORM_MFMA]
+FORMS = [mbq.FORM_DOT4, mbq.FORM_MFMA, mbq.FORM_ROWSET]
 
 
 @pytest.mark.parametrize("form", FORMS)
