@@ -289,11 +289,16 @@ __device__ __forceinline__ void attention_split(const AttnArgs &a) {
     const int64_t used = (int64_t)a.P + a.M;       // positions in the cache
     const uint16_t *kg = a.k + (int64_t)g * a.L * D, *vg = a.v + (int64_t)g * a.L * D;
 
-    // Loads: wave w covers positions 16 w .. 16 w + 15 (lane & 15), and load u
-    // chunks 4 u .. 4 u + 3 (lane >> 4): 64 contiguous bytes of 16 rows.  The
+    // Loads: wave w covers positions 16 w .. 16 w + 15.  Key load u takes
+    // chunks 4 u .. 4 u + 3 (lane >> 4) of the 16 rows (lane & 15), 64
+    // contiguous bytes of each.  Values need no operand layout, so where a
+    // thread makes an even number of loads, value load u takes whole 128-byte
+    // lines instead: rows 8 (u & 1) + lane / 8, chunks 8 (u / 2) + lane % 8
+    // (eight consecutive lanes read one line; measured faster than the key
+    // layout, where consecutive lanes read 16 different rows).  The
     // transposed value tile keeps a column's positions contiguous, rotated by
-    // 8 (d / 8 mod 8) positions, so the four lane groups of a write land on
-    // different banks while every 8-position operand run stays contiguous.
+    // 8 (d / 8 mod 8) positions, so the lanes of a write land on different
+    // banks while every 8-position operand run stays contiguous.
     // With one position tile per wave (WPR = 4) the keys are not staged:
     // load u of a wave is exactly its score operand for k step u (position
     // 16 w + lr, k 32 u + 8 lq .. +7), kept in registers until the block's
@@ -303,17 +308,17 @@ __device__ __forceinline__ void attention_split(const AttnArgs &a) {
     v4i kbuf[kLoads], vbuf[kLoads];
     const int pp = 16 * (wave % kPt) + lr;
     const int cbase = (wave / kPt) * (kChunks * kPt / 4);
+    constexpr bool kVLines = kLoads % 2 == 0;
+    auto vpos = [&](int u) { return kVLines ? 16 * (wave % kPt) + 8 * (u & 1) + (lane >> 3) : pp; };
+    auto vchunk = [&](int u) { return kVLines ? cbase + 8 * (u >> 1) + (lane & 7) : cbase + 4 * u + lq; };
     auto fetch = [&](int b) {
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) {
-            const int c = cbase + 4 * u + lq;
-            const int64_t pos = (int64_t)b * BLK + pp;
+            const int64_t pos = (int64_t)b * BLK + pp, vp = (int64_t)b * BLK + vpos(u);
             kbuf[u] = v4i{0, 0, 0, 0};
             vbuf[u] = v4i{0, 0, 0, 0};
-            if (pos < used) {
-                kbuf[u] = *gptr(reinterpret_cast<const v4i *>(kg + pos * D) + c);
-                vbuf[u] = *gptr(reinterpret_cast<const v4i *>(vg + pos * D) + c);
-            }
+            if (pos < used) kbuf[u] = *gptr(reinterpret_cast<const v4i *>(kg + pos * D) + cbase + 4 * u + lq);
+            if (vp < used) vbuf[u] = *gptr(reinterpret_cast<const v4i *>(vg + vp * D) + vchunk(u));
         }
     };
     static_assert(WPR != 4 || (BLK == 64 && kLoads == kKs), "one key load per k step");
@@ -325,10 +330,11 @@ __device__ __forceinline__ void attention_split(const AttnArgs &a) {
             if constexpr (WPR == 4) kop[u] = kbuf[u];
             else *reinterpret_cast<v4i *>(k_lds + pp * kKStride + c * 16) = kbuf[u];
             const uint32_t w[4] = {(uint32_t)vbuf[u].x, (uint32_t)vbuf[u].y, (uint32_t)vbuf[u].z, (uint32_t)vbuf[u].w};
-            const int col = (pp + 8 * (c & 7)) & (BLK - 1);   // rows 8c .. 8c+7: d / 8 = c
+            const int vc = vchunk(u);
+            const int col = (vpos(u) + 8 * (vc & 7)) & (BLK - 1);   // rows 8 vc .. 8 vc + 7: d / 8 = vc
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<uint16_t *>(vt_lds + (8 * c + e) * kVtStride + col * 2) =
+                *reinterpret_cast<uint16_t *>(vt_lds + (8 * vc + e) * kVtStride + col * 2) =
                     (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
         }
     };
