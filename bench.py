@@ -18,7 +18,9 @@ quantisation), and the CPU oracle on all host cores and on one.
 --workload linear prints the single-linear measurement as the headline instead;
 --workload attention times the split-prefix decode attention of one
 27B-shaped attention layer (32 query heads, 4 key/value heads of 256) over a
---ctx-token bf16 KV cache and reports the cache-read rate.
+--ctx-token bf16 KV cache and reports the cache-read rate; successive calls
+read distinct caches, about 1 GiB in all, so that none is served from the
+last-level cache.
 """
 from __future__ import annotations
 
@@ -165,31 +167,41 @@ def measured_traffic(key):
 ATTN_SHAPE = dict(n_q=32, n_kv=4, D=256)
 
 
+# Distinct KV caches the attention calls rotate over: at least four, and at
+# least this many bytes in all (four times the GPU's 256 MiB last-level
+# "Infinity" cache), so that no call finds its cache there -- a decode step
+# reads each layer's cache once.
+ATTN_ROTATE_BYTES = 1 << 30
+
+
 def run_attention(args):
     """One JSON line for the decode attention: KV-cache bytes per launch over the
-    event-timed launch, for M = args.m (and args.extra_m as extra fields)."""
+    event-timed launch, for M = args.m (and args.extra_m as extra fields).
+    Successive calls read distinct caches (ATTN_ROTATE_BYTES in all)."""
     import torch
     import memory_bound_quantised_amd as mbq
     n_q, n_kv, D, P = ATTN_SHAPE["n_q"], ATTN_SHAPE["n_kv"], ATTN_SHAPE["D"], args.ctx
     Ms = [args.m] + [m for m in args.extra_m if m != args.m]
     L = P + max(Ms)
+    layer_bytes = 2 * n_kv * L * D * 2
+    copies = max(4, -(-ATTN_ROTATE_BYTES // layer_bytes))
     g = torch.Generator(device="cuda").manual_seed(1234)
-    k = torch.randn((n_kv, L, D), device="cuda", generator=g).to(torch.bfloat16)
-    v = torch.randn((n_kv, L, D), device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.randn((copies, n_kv, L, D), device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn((copies, n_kv, L, D), device="cuda", generator=g).to(torch.bfloat16)
     res = {}
     for M in Ms:
         q = torch.randn((M, n_q, D), device="cuda", generator=g).to(torch.bfloat16)
         ws = torch.zeros(mbq.attention_workspace_bytes(M, n_q, n_kv, D, P), dtype=torch.uint8, device="cuda")
         out = torch.empty((M, n_q, D), dtype=torch.bfloat16, device="cuda")
-        for _ in range(args.warmup):
-            mbq.decode_attention(q, k, v, P, out=out, ws=ws)
+        for i in range(max(args.warmup, copies)):
+            mbq.decode_attention(q, k[i % copies], v[i % copies], P, out=out, ws=ws)
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         t0 = time.perf_counter()
         ev[0].record(stream)
         for i in range(args.steps):
-            mbq.decode_attention(q, k, v, P, out=out, ws=ws)
+            mbq.decode_attention(q, k[i % copies], v[i % copies], P, out=out, ws=ws)
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -206,8 +218,8 @@ def run_attention(args):
         "ms_per_step": round(r["wall_ms"], 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"split-prefix decode attention, 32 query / 4 key-value heads of 256, "
-                               f"{P}-token bf16 cache, M={args.m}", "ctx": P, "M": args.m,
-                   "combine": args.attn_combine, **ATTN_SHAPE},
+                               f"{P}-token bf16 cache, M={args.m}, {copies} rotated caches", "ctx": P, "M": args.m,
+                   "combine": args.attn_combine, "rotated_caches": copies, **ATTN_SHAPE},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "kernel": ("decode_attention_kernel, then attn_merge_kernel when the prefix has "
                                                  "several splits (timed together per call)")

@@ -295,7 +295,9 @@ __device__ __forceinline__ void attention_split(const AttnArgs &a) {
     // thread makes an even number of loads, value load u takes whole 128-byte
     // lines instead: rows 8 (u & 1) + lane / 8, chunks 8 (u / 2) + lane % 8
     // (eight consecutive lanes read one line; measured faster than the key
-    // layout, where consecutive lanes read 16 different rows).  The
+    // layout, where consecutive lanes read 16 different rows).  Value loads
+    // carry the non-temporal hint; key loads do not (measured: the hint
+    // speeds the values and slows the keys).  The
     // transposed value tile keeps a column's positions contiguous, rotated by
     // 8 (d / 8 mod 8) positions, so the lanes of a write land on different
     // banks while every 8-position operand run stays contiguous.
@@ -318,7 +320,7 @@ __device__ __forceinline__ void attention_split(const AttnArgs &a) {
             kbuf[u] = v4i{0, 0, 0, 0};
             vbuf[u] = v4i{0, 0, 0, 0};
             if (pos < used) kbuf[u] = *gptr(reinterpret_cast<const v4i *>(kg + pos * D) + cbase + 4 * u + lq);
-            if (vp < used) vbuf[u] = *gptr(reinterpret_cast<const v4i *>(vg + vp * D) + vchunk(u));
+            if (vp < used) vbuf[u] = load_stream(reinterpret_cast<const v4i *>(vg + vp * D) + vchunk(u));
         }
     };
     static_assert(WPR != 4 || (BLK == 64 && kLoads == kKs), "one key load per k step");
