@@ -44,6 +44,19 @@ constexpr int64_t kRsMaxBlocks = 64;         // the row-set form up to this many
 // The form with the prologue inside keeps the M x K activation codes in LDS,
 // next to at most 16 KiB of the kernel's own.
 constexpr int64_t kRbPrologueMaxCodes = 140 * 1024;
+// Static LDS of the row-block and row-set kernels with the prologue inside:
+// the wave partials, the row scales and the prologue's two reductions.
+constexpr int64_t rb_static_lds(int W, int M) { return (int64_t)W * M * 64 * 4 + M * 4 + W * 12; }
+constexpr int64_t rs_static_lds(int W, int M) { return (int64_t)W * M * 16 * 4 + M * 4 + W * 12; }
+// Codes plus static LDS within the CU's 160 KiB, less 1 KiB of alignment
+// slack, for every (waves, k groups) pair launch_rb and launch_rs pick: 16
+// waves only up to 32 groups (K <= 4096) in the row-block form.
+constexpr int64_t kCuLds = 160 * 1024 - 1024;
+static_assert(kRbPrologueMaxCodes + rb_static_lds(4, kMaxM) <= kCuLds &&
+                  (int64_t)kMaxM * 32 * 128 + rb_static_lds(16, kMaxM) <= kCuLds &&
+                  kRbPrologueMaxCodes + rb_static_lds(8, kMaxM) <= kCuLds &&
+                  kRbPrologueMaxCodes + rs_static_lds(16, kMaxM) <= kCuLds,
+              "prologue codes and the kernels' own LDS fit a CU");
 #ifndef MBQ_LIN_MFMA_MIN_M
 #define MBQ_LIN_MFMA_MIN_M 1
 #endif
