@@ -351,10 +351,17 @@ __device__ void external_stats(const SeqPlan *P, int w, int waves, int lane, uin
 // The product t * rinv is within two ulps of the correctly rounded quotient,
 // so it rounds to the same integer unless it lies next to a half-integer;
 // only there (and when 1 / s overflows) is the quotient computed exactly.
-__device__ __forceinline__ float quant_code(float t, float s, float rinv, bool rinv_ok) {
+// thr is 2^-14, or infinity where 1 / s overflows (always the exact quotient:
+// t * rinv may then be 0 * inf); a zero scale comes with rinv = 0, which
+// gives code 0 without the quotient.  A NaN distance (t * rinv not finite)
+// takes the quotient too, which yields the same code as the product.
+// The quotient sits under a wave-wide branch: it is rarely needed, and
+// computed for every code it costs more than the rest of the code together.
+__device__ __forceinline__ float quant_code(float t, float s, float rinv, float thr) {
     float x = t * rinv;
     const float fx = fabsf(x);
-    if (!rinv_ok || fabsf(fx - floorf(fx) - 0.5f) < 0x1p-14f) x = t / s;
+    const bool exact = !(fabsf(fx - floorf(fx) - 0.5f) >= thr);
+    if (__builtin_amdgcn_ballot_w64(exact) != 0) x = exact ? t / s : x;
     return fminf(fmaxf(rintf(x), -127.0f), 127.0f);
 }
 
@@ -422,6 +429,13 @@ __device__ __forceinline__ void quant_cols(const SeqPlan *P, const Lay &L, const
                                            uint32_t want, int words, bool norm, const float (&s)[M],
                                            const float (&r)[M], const float (&rinv)[M], const bool (&rinv_ok)[M],
                                            const Words<M, XB> &first, bool use_first) {
+    // the row's uniform cases as constants, so that no code branches on them
+    float rq[M], thr[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        rq[m] = s[m] != 0.0f ? rinv[m] : 0.0f;
+        thr[m] = s[m] != 0.0f && !rinv_ok[m] ? INFINITY : 0x1p-14f;
+    }
     for (int j0 = 0; j0 < words; j0 += XB * kSeqThreads) {
         Words<M, XB> xw;
         if (PRE && j0 == 0 && use_first) xw = first;
@@ -448,8 +462,9 @@ __device__ __forceinline__ void quant_cols(const SeqPlan *P, const Lay &L, const
                 for (int e = 0; e < 2; ++e) {
                     float t = bf16_bits_to_f32((pair >> (16 * e)) & 0xFFFFu);
                     if (WEIGHTED) t *= bf16_bits_to_f32((ww[WEIGHTED ? u : 0] >> (16 * e)) & 0xFFFFu);
-                    if (norm) t = bf16_bits_to_f32(f32_to_bf16_bits(t * r[m]));
-                    const float qv = s[m] != 0.0f ? quant_code(t, s[m], rinv[m], rinv_ok[m]) : 0.0f;
+                    const float tn = bf16_bits_to_f32(f32_to_bf16_bits(t * r[m]));
+                    t = norm ? tn : t;
+                    const float qv = quant_code(t, s[m], rq[m], thr[m]);
                     packed |= ((uint32_t)(int)qv & 0xFFu) << (8 * e);
                 }
                 *reinterpret_cast<uint16_t *>(g_lds + m * L.qs + 2 * j) = (uint16_t)packed;

@@ -39,6 +39,11 @@ def special_rows(K):
     rows.append(one)
     big = np.random.default_rng(K).standard_normal(K).astype(np.float32) * 1e4
     rows.append(big)
+    # scale below 127 / FLT_MAX: 1 / s overflows, so codes need the exact
+    # quotient (half the columns zero, whose codes must stay 0)
+    tiny = np.random.default_rng(K + 1).uniform(-3e-37, 3e-37, K).astype(np.float32)
+    tiny[::2] = 0.0
+    rows.append(tiny)
     return synth.f32_to_bf16_bits(np.stack(rows))
 
 
@@ -93,7 +98,7 @@ def test_swiglu_quantize(M, K):
 @pytest.mark.parametrize("K", [128, 4096])
 def test_quantize_special_rows(K, rmsnorm):
     x = special_rows(K)
-    for start in range(0, 4, 4):
+    for start in range(0, len(x), 4):
         xb = x[start:start + 4]
         q, s = mbq.quantize_act(dev(xb), rmsnorm=rmsnorm)
         qo, so = oracle.prologue_quant(xb, oracle.PRO_RMSNORM_QUANT if rmsnorm else oracle.PRO_QUANT)
@@ -433,6 +438,46 @@ def _oracle_op_rows(bits, bufs, o, mats, rows=None):
         assert d.max() <= 1, f"{o['name']}: gated input {int(d.max())} bf16 steps from the fp64 definition"
         return oracle.op(bits, h, oracle.PRO_QUANT, canon, S)
     return oracle.op(bits, x, o["prologue"], canon, S, o.get("norm_w"), None)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("bits", [4, 6])
+def test_sequence_quantises_corner_rows(bits, fused):
+    """The walk's input quantisation on the corner-case rows (all zero, exact
+    ties, a lone value at the tail, large values, a scale whose reciprocal
+    overflows), then an op on its output.  Outputs are compared row by row
+    relative to the row's largest output, since the tiny row's outputs sit far
+    below the absolute tolerance."""
+    import torch
+    K, N = 384, 256
+    x = special_rows(K)
+    M = len(x)
+    ops = [dict(name="a", K=K, N=N, in_buf=0, out_buf=1, prologue=oracle.PRO_QUANT),
+           dict(name="b", K=N, N=128, in_buf=1, out_buf=2, prologue=oracle.PRO_QUANT)]
+    mats, dev_ops = {}, []
+    for i, o in enumerate(ops):
+        o["matrix"] = i
+        mats[i] = synth.weights(bits, o["N"], o["K"], seed=700 + i)
+        dev_ops.append(dict(bits=bits, prologue=o["prologue"], N=o["N"], K=o["K"], in_buf=o["in_buf"],
+                            out_buf=o["out_buf"], packed=packed_on_device(bits, *mats[i], o["N"], o["K"])))
+    bufs = [torch.zeros((M, w), dtype=torch.bfloat16, device="cuda") for w in (K, N, 128)]
+    bufs[0].copy_(dev(x))
+    seq = mbq.LayerSequence(dev_ops, bufs, M, fused=fused)
+    seq.run()
+    if fused:
+        seq.check()
+    torch.cuda.synchronize()
+    hb = [host(b) for b in bufs]
+    for o in ops:
+        y = synth.bf16_bits_to_f32(hb[o["out_buf"]]).astype(np.float64)
+        ref = synth.bf16_bits_to_f32(_oracle_op_rows(bits, hb, o, mats)).astype(np.float64)
+        for m in range(M):
+            top = np.abs(ref[m]).max()
+            if top == 0.0:
+                assert np.all(y[m] == 0.0), f"{o['name']} row {m}"
+                continue
+            err = np.abs(y[m] - ref[m]) / top
+            assert np.all(err <= 1e-3 + 1e-2 * np.abs(ref[m]) / top), f"{o['name']} row {m}: max {err.max()}"
 
 
 @pytest.mark.parametrize("fused", [True, False])
