@@ -166,6 +166,19 @@ def measured_traffic(key):
 
 ATTN_SHAPE = dict(n_q=32, n_kv=4, D=256)
 
+# The only performance figures the source pages give for this path: whole-model
+# decode rates on NVIDIA consumer GPUs, before and after the kernel work
+# ("Doubling LLM token rates in ComfyUI", introduction).  They include
+# attention, speculative decoding and everything else on other hardware, so
+# they are context for tokens_per_s, not a baseline for this metric.
+PAGES_CONTEXT = {
+    "source": "Doubling LLM token rates in ComfyUI, introduction (whole-model decode, other GPUs)",
+    "9b_tokens_per_s_rtx5090_before_after": [106, 219],
+    "9b_tokens_per_s_rtx5080_before_after": [91, 129],
+    "27b_tokens_per_s_rtx5090_before_after": [55, 122],
+    "27b_w4a8_tokens_per_s_rtx5090_with_mtp": 137,
+}
+
 
 # Distinct KV caches the attention calls rotate over: at least four, and at
 # least this many bytes in all (four times the GPU's 256 MiB last-level
@@ -595,6 +608,7 @@ def main():
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample (all host cores, then one thread)")
         out["cpu_baseline"] = cpu_baseline(args.set, args.bits, n_layers, args.dataflow)
+    out["pages_context"] = PAGES_CONTEXT
     print(json.dumps(out), flush=True)
 
 
