@@ -52,6 +52,7 @@ int relayout_inplace(int bits, int64_t N, int64_t K, void *buf, int n_cu, hipStr
 
 // Split-prefix decode attention (attn.hip).
 struct AttnPlan {
+    // blocks_per_split: blocks of each split; the last (n_blocks mod n_split) splits take one more
     int64_t n_blocks = 0, blocks_per_split = 0, n_split = 0, rows = 0;
     int64_t block = 64;      // positions per block
     int64_t merge_tpq = 1;   // merge lanes per four outputs
