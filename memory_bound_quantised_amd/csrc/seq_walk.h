@@ -473,6 +473,68 @@ __device__ __forceinline__ void quant_cols(const SeqPlan *P, const Lay &L, const
     }
 }
 
+// Wave 0's poll of the statistics records [0, nrec) of the phase input: lane
+// l takes records l, l + 64, ... and accumulates each row's maximum (am) and,
+// with NORM, its sum of squares (ss).  A batch holds kStatBatch x 3M words:
+// with NORM, kStatBatch whole records (maximum, sum-of-squares low and high
+// words per row); without, only the maxima are read, M words per record, so a
+// batch covers three times the records.
+template <int M, bool NORM>
+__device__ __forceinline__ void poll_stats(const SeqPlan *P, const uint64_t *stats, int64_t stride, int nrec,
+                                           uint32_t want, int lane, double (&ss)[M], float (&am)[M]) {
+    constexpr int kStatBatch = stat_batch<M>();
+    constexpr int kRecs = NORM ? kStatBatch : 3 * kStatBatch;   // records per lane per batch
+    // record (within the batch) and word (within the record) of slot (u, c)
+    constexpr auto slot_rec = [](int u, int c) { return NORM ? u : 3 * u + c / M; };
+    constexpr auto slot_word = [](int u, int c) { return NORM ? c : 3 * (c % M); };
+    for (int base = 0; base < nrec; base += 64 * kRecs) {
+        vm_room<kStatBatch * 3 * M>();
+        uint64_t v[kStatBatch][3 * M];
+#pragma unroll
+        for (int u = 0; u < kStatBatch; ++u)
+#pragma unroll
+            for (int c = 0; c < 3 * M; ++c) {
+                const int i = base + lane + 64 * slot_rec(u, c);
+                v[u][c] = i < nrec ? load_shared(stats + slot_word(u, c) * stride + i) : 0;
+            }
+        int64_t spins = 0;
+        for (;;) {
+            bool stale = false;
+#pragma unroll
+            for (int u = 0; u < kStatBatch; ++u)
+#pragma unroll
+                for (int c = 0; c < 3 * M; ++c)
+                    stale |= base + lane + 64 * slot_rec(u, c) < nrec && tag_of(v[u][c]) != want;
+            if (!wave_any(stale) || gave_up(P, spins)) break;
+#pragma unroll
+            for (int u = 0; u < kStatBatch; ++u)
+#pragma unroll
+                for (int c = 0; c < 3 * M; ++c) {
+                    const int i = base + lane + 64 * slot_rec(u, c);
+                    if (i < nrec && tag_of(v[u][c]) != want) v[u][c] = load_shared(stats + slot_word(u, c) * stride + i);
+                }
+        }
+#pragma unroll
+        for (int u = 0; u < kStatBatch; ++u) {
+            if constexpr (NORM) {
+                if (base + lane + 64 * u < nrec) {
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        const uint64_t lo = v[u][3 * m + 1], hi = v[u][3 * m + 2];
+                        am[m] = fmaxf(am[m], __uint_as_float((uint32_t)v[u][3 * m]));
+                        ss[m] += __longlong_as_double((long long)(((hi & 0xFFFFFFFFull) << 32) | (lo & 0xFFFFFFFFull)));
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 3 * M; ++c)
+                    if (base + lane + 64 * slot_rec(u, c) < nrec)
+                        am[c % M] = fmaxf(am[c % M], __uint_as_float((uint32_t)v[u][c]));
+            }
+        }
+    }
+}
+
 // Quantise columns [k_lo, k_hi) of the phase input into LDS (int8, row stride
 // q_stride), after the phase's RMSNorm with or without weights (a SwiGLU
 // input arrives gated, in the tagged copy).  Row statistics come from
@@ -529,46 +591,10 @@ __device__ __forceinline__ void enter_phase(const SeqPlan *P, const Lay &L, int 
             }
             const int64_t stride = L.stat_stride;
             const uint64_t *stats = L.stats + (wg % kStatReplicas) * L.stat_rep + ph.in_rec;
-            constexpr int kStatBatch = stat_batch<M>();
-            for (int base = 0; base < ph.in_nrec; base += 64 * kStatBatch) {
-                vm_room<kStatBatch * 3 * M>();
-                uint64_t v[kStatBatch][3 * M];
-#pragma unroll
-                for (int u = 0; u < kStatBatch; ++u) {
-                    const int i = base + lane + 64 * u;
-#pragma unroll
-                    for (int c = 0; c < 3 * M; ++c) v[u][c] = i < ph.in_nrec ? load_shared(stats + c * stride + i) : 0;
-                }
-                int64_t spins = 0;
-                for (;;) {
-                    bool stale = false;
-#pragma unroll
-                    for (int u = 0; u < kStatBatch; ++u)
-#pragma unroll
-                        for (int c = 0; c < 3 * M; ++c)
-                            stale |= base + lane + 64 * u < ph.in_nrec && tag_of(v[u][c]) != want;
-                    if (!wave_any(stale) || gave_up(P, spins)) break;
-#pragma unroll
-                    for (int u = 0; u < kStatBatch; ++u) {
-                        const int i = base + lane + 64 * u;
-#pragma unroll
-                        for (int c = 0; c < 3 * M; ++c)
-                            if (i < ph.in_nrec && tag_of(v[u][c]) != want) v[u][c] = load_shared(stats + c * stride + i);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < kStatBatch; ++u) {
-                    if (base + lane + 64 * u < ph.in_nrec) {
-#pragma unroll
-                        for (int m = 0; m < M; ++m) {
-                            const uint64_t lo = v[u][3 * m + 1], hi = v[u][3 * m + 2];
-                            am[m] = fmaxf(am[m], __uint_as_float((uint32_t)v[u][3 * m]));
-                            ss[m] += __longlong_as_double(
-                                (long long)(((hi & 0xFFFFFFFFull) << 32) | (lo & 0xFFFFFFFFull)));
-                        }
-                    }
-                }
-            }
+            if (uniform(norm ? 1 : 0))
+                poll_stats<M, true>(P, stats, stride, ph.in_nrec, want, lane, ss, am);
+            else
+                poll_stats<M, false>(P, stats, stride, ph.in_nrec, want, lane, ss, am);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const double tot = wave_sum63(ss[m]);
