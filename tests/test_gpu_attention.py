@@ -96,6 +96,18 @@ def test_decode_attention_27b_shape(M, combine):
     assert_close_bf16(_run(q, k, v, P), oracle.decode_attention(q, k, v, P), f"27B M={M}")
 
 
+@pytest.mark.parametrize("P", [32767, 40895, 40960])
+def test_decode_attention_split_remainders(P, combine):
+    """Cache lengths whose blocks do not divide evenly over the splits: the
+    last (blocks mod splits) splits take one more block.  On the 27B layer
+    shape with 128 splits, 32767 + 1 positions are 512 blocks (none left
+    over), 40895 + 1 are 639 (all splits but one take one more) and 40960 + 1
+    are 641 (only the last takes one more: the one-row tail)."""
+    n_q, n_kv, D, M = 32, 4, 256, 1
+    q, k, v = _inputs(M, n_q, n_kv, D, P + M, seed=P)
+    assert_close_bf16(_run(q, k, v, P), oracle.decode_attention(q, k, v, P), f"27B P={P}")
+
+
 def test_decode_attention_graph_replays(combine):
     """The attention captured in a HIP graph (two launches, or one cooperative
     launch with the merge inside): replays on queries written between them
