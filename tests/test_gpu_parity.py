@@ -541,7 +541,7 @@ def test_sequence_gate_and_norm_inputs_from_before_the_walk(bits, M, fused):
 
 
 @pytest.mark.parametrize("bits", [4, 6])
-@pytest.mark.parametrize("M", [1, 3])
+@pytest.mark.parametrize("M", [1, 3, 8])
 def test_layer_sequence_9b_layers_teacher_forced(bits, M):
     ops, mats, bufs, _ = _run_sequence(bits, synth.layer_shapes_9b, 2, M, distinct=True)
     rng = np.random.default_rng(4)
@@ -553,10 +553,11 @@ def test_layer_sequence_9b_layers_teacher_forced(bits, M):
         assert_close_bf16(bufs[o["out_buf"]][:, rows], ref, o["name"])
 
 
-@pytest.mark.parametrize("bits,M", [(4, 1), (4, 2), (4, 3), (4, 4), (4, 8), (6, 1), (6, 3), (6, 4)])
+@pytest.mark.parametrize("bits,M", [(4, 1), (4, 2), (4, 3), (4, 4), (4, 5), (4, 6), (4, 7), (4, 8),
+                                    (6, 1), (6, 2), (6, 3), (6, 4), (6, 5), (6, 6), (6, 7), (6, 8)])
 def test_layer_sequence_27b_layer_teacher_forced(bits, M):
-    """One 27B-shaped layer (W4 over the M = 1..4 sweep and M = 8; W6 at M = 1, 3
-    and 4): q is 16384 wide and o reads its first 8192 columns."""
+    """One 27B-shaped layer at every row count, both bit widths: q is 16384
+    wide and o reads its first 8192 columns."""
     ops, mats, bufs, _ = _run_sequence(bits, synth.layer_shapes_27b, 1, M, distinct=True)
     rng = np.random.default_rng(5)
     for o in ops:
@@ -567,7 +568,7 @@ def test_layer_sequence_27b_layer_teacher_forced(bits, M):
         assert_close_bf16(bufs[o["out_buf"]][:, rows], ref, o["name"])
 
 
-@pytest.mark.parametrize("bits,M", [(4, 1), (4, 2), (4, 3), (4, 4), (4, 8), (6, 3), (6, 4)])
+@pytest.mark.parametrize("bits,M", [(4, 1), (4, 2), (4, 3), (4, 4), (4, 6), (4, 8), (6, 1), (6, 3), (6, 4), (6, 8)])
 def test_layer_sequence_27b_layer_swiglu_dataflow(bits, M):
     """The same layer through the walk's other kernel form: weighted RMSNorms in
     front of q/k/v and gate/up, the SwiGLU gate in front of down.  From M = 3 on
