@@ -108,6 +108,18 @@ def test_decode_attention_split_remainders(P, combine):
     assert_close_bf16(_run(q, k, v, P), oracle.decode_attention(q, k, v, P), f"27B P={P}")
 
 
+@pytest.mark.parametrize("M,n_q,n_kv,D", [(1, 16, 4, 128), (8, 16, 4, 128), (1, 8, 2, 64), (8, 8, 2, 64),
+                                          (5, 8, 8, 256)])
+def test_decode_attention_long_prefix_other_shapes(M, n_q, n_kv, D, combine):
+    """A long prefix that is not a whole number of blocks, over other head
+    sizes, group sizes and row counts: every form (one, two or four row tiles;
+    64- or 32-position blocks) deals its blocks over many splits with some
+    left over."""
+    P = 20011
+    q, k, v = _inputs(M, n_q, n_kv, D, P + M, seed=M * 1000 + D)
+    assert_close_bf16(_run(q, k, v, P), oracle.decode_attention(q, k, v, P), f"M={M} D={D} n_kv={n_kv}")
+
+
 def test_decode_attention_graph_replays(combine):
     """The attention captured in a HIP graph (two launches, or one cooperative
     launch with the merge inside): replays on queries written between them
