@@ -136,30 +136,37 @@ def time_sequence(mbq, dev_ops, widths, M, steps, warmup, fused=True):
                 event_ms_best=float(per.min()), event_ms_mean=float(per.mean()))
 
 
+# Counter records of each workload's dominant kernel, valid while the sources
+# they were taken from are unchanged: (file, kernel sources).
 KERNEL_SOURCES = ["seq_walk.h", "seq_plain.hip", "seq_full.hip", "seqplan.hip", "mbq_seq.h", "mbq_internal.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "seq_kernel_traffic.json")
+ATTN_TRAFFIC = (os.path.join(ROOT, "profiles", "decode_attention_traffic.json"),
+                ["attn.hip", "mbq_internal.h", "mbq_kernels.h"])
+LINEAR_TRAFFIC = (os.path.join(ROOT, "profiles", "linear_traffic.json"),
+                  ["linear.hip", "quant_rows.h", "mbq_internal.h", "mbq_kernels.h"])
 
 
-def kernel_sources_sha256():
+def kernel_sources_sha256(sources=KERNEL_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "memory_bound_quantised_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(key):
+def measured_traffic(key, record=(TRAFFIC_FILE, KERNEL_SOURCES)):
     """HBM bytes per launch from the committed counter runs (FETCH_SIZE + WRITE_SIZE, each
     scaled by what the counter reads for a copy kernel of known size), or None when there
     is none for this workload or the kernel sources changed since it was taken."""
+    path, sources = record
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
     e = rec.get("workloads", {}).get(key)
-    if not e or rec.get("kernel_sources_sha256") != kernel_sources_sha256():
+    if not e or rec.get("kernel_sources_sha256") != kernel_sources_sha256(sources):
         return None
     return e["fetch_bytes_per_launch"] + e["write_bytes_per_launch"]
 
@@ -239,7 +246,9 @@ def run_attention(args):
                      if args.attn_combine == "kernel" else
                      "decode_attention_kernel, combining its splits in the same cooperative launch",
                      "achieved": round(gbs, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(f"27b/ctx{P}/m{args.m}/{args.attn_combine}", ATTN_TRAFFIC),
+                     "traffic_kernel": "decode_attention_kernel (the split kernel alone)",
                      "bytes_per_launch": r["kv_bytes"], "launch_ms": round(r["ms"], 4)},
     }
     for M, rm in res.items():
@@ -489,6 +498,15 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
+    if args.calib_copy > 0:
+        src = torch.ones(args.calib_copy << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calib_copy} MiB x 3")
+        del src, dst
+
     if args.workload == "attention":
         if args.attn_combine == "inline":
             os.environ["MBQ_ATTN_COMBINE"] = "inline"
@@ -514,22 +532,14 @@ def main():
                "roofline": {"bound": "hbm", "kernel": "linear_rs_kernel (row-set form: four workgroups per "
                                                      "64-row block, one launch per call)",
                             "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                            "frac": round(gbs / HBM_PEAK_GBS, 4),
+                            "traffic": measured_traffic("4096x4096/w4/m1", LINEAR_TRAFFIC),
                             "bytes_per_launch": r["weight_bytes_per_call"], "launch_us": r["linear_us"]}}
         if ceiling:
             out["ceiling"] = ceiling
             out["pct_of_ceiling"] = round(100 * gbs / ceiling["GB/s_best"], 2)
         print(json.dumps(out), flush=True)
         return
-
-    if args.calib_copy > 0:
-        src = torch.ones(args.calib_copy << 18, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration copy: {args.calib_copy} MiB x 3")
-        del src, dst
 
     n_layers = args.layers or synth.WEIGHT_SETS[args.set][1]
     shapes = synth.weight_set(args.set, n_layers)
