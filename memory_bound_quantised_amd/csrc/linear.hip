@@ -505,7 +505,22 @@ __global__ __launch_bounds__(64 * W) void linear_rs_kernel(
     if constexpr (QF) rb_prologue<M, W>(q_lds, s_lds, K, pro, x, u, wn);
     const int lane = threadIdx.x & 63;
     const int w = uniform(threadIdx.x >> 6);
-    const int rb = blockIdx.x >> 2, set = blockIdx.x & 3;
+    // The four workgroups of a row block on one XCD, which share its scale
+    // lines in that XCD's L2 (workgroups go to the XCDs in turn): in each run
+    // of 32 workgroups, workgroup 32 g + 8 s + j is set s of row block 8 g + j;
+    // a last, partial run of r row blocks is dealt as 4 sets of r.
+    int rb, set;
+    {
+        const int b = blockIdx.x, n_rb = (N + 63) >> 6, full = n_rb >> 3;
+        if ((b >> 5) < full) {
+            rb = 8 * (b >> 5) + (b & 7);
+            set = (b >> 3) & 3;
+        } else {
+            const int r = n_rb - 8 * full, o = b - 32 * full;
+            rb = 8 * full + o % r;
+            set = o / r;
+        }
+    }
     const int G = K >> 7;
     const int g0 = (int)((int64_t)G * w / W), g1 = (int)((int64_t)G * (w + 1) / W);
     const uint8_t *tiles = packed + (int64_t)rb * G * L::kTileBytes;
