@@ -293,13 +293,14 @@ __device__ __forceinline__ void attention_split(const AttnArgs &a) {
     const int64_t used = (int64_t)a.P + a.M;       // positions in the cache
     const uint16_t *kg = a.k + (int64_t)g * a.L * D, *vg = a.v + (int64_t)g * a.L * D;
 
-    // Loads: wave w covers positions 16 w .. 16 w + 15.  Key load u takes
-    // chunks 4 u .. 4 u + 3 (lane >> 4) of the 16 rows (lane & 15), 64
-    // contiguous bytes of each.  Values need no operand layout, so where a
-    // thread makes an even number of loads, value load u takes whole 128-byte
-    // lines instead: rows 8 (u & 1) + lane / 8, chunks 8 (u / 2) + lane % 8
-    // (eight consecutive lanes read one line; measured faster than the key
-    // layout, where consecutive lanes read 16 different rows).  Value loads
+    // Loads: wave w covers positions 16 w .. 16 w + 15.  Keys held as score
+    // operands (WPR = 4) take, in load u, chunks 4 u .. 4 u + 3 (lane >> 4)
+    // of the 16 rows (lane & 15), 64 contiguous bytes of each.  Values, and
+    // keys staged in LDS, need no operand layout, so where a thread makes an
+    // even number of loads, load u takes whole 128-byte lines instead: rows
+    // 8 (u & 1) + lane / 8, chunks 8 (u / 2) + lane % 8 (eight consecutive
+    // lanes read one line; measured faster than the operand layout, where
+    // consecutive lanes read 16 different rows).  Value loads
     // carry the non-temporal hint; key loads do not (measured: the hint
     // speeds the values and slows the keys).  The
     // transposed value tile keeps a column's positions contiguous, rotated by
@@ -317,13 +318,16 @@ __device__ __forceinline__ void attention_split(const AttnArgs &a) {
     constexpr bool kVLines = kLoads % 2 == 0;
     auto vpos = [&](int u) { return kVLines ? 16 * (wave % kPt) + 8 * (u & 1) + (lane >> 3) : pp; };
     auto vchunk = [&](int u) { return kVLines ? cbase + 8 * (u >> 1) + (lane & 7) : cbase + 4 * u + lq; };
+    // keys staged in LDS take the values' layout; keys held as operands (WPR = 4) their own
+    auto kpos = [&](int u) { return WPR == 4 ? pp : vpos(u); };
+    auto kchunk = [&](int u) { return WPR == 4 ? cbase + 4 * u + lq : vchunk(u); };
     auto fetch = [&](int b) {
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) {
-            const int64_t pos = (int64_t)b * BLK + pp, vp = (int64_t)b * BLK + vpos(u);
+            const int64_t pos = (int64_t)b * BLK + kpos(u), vp = (int64_t)b * BLK + vpos(u);
             kbuf[u] = v4i{0, 0, 0, 0};
             vbuf[u] = v4i{0, 0, 0, 0};
-            if (pos < used) kbuf[u] = *gptr(reinterpret_cast<const v4i *>(kg + pos * D) + cbase + 4 * u + lq);
+            if (pos < used) kbuf[u] = *gptr(reinterpret_cast<const v4i *>(kg + pos * D) + kchunk(u));
             if (vp < used) vbuf[u] = load_stream(reinterpret_cast<const v4i *>(vg + vp * D) + vchunk(u));
         }
     };
@@ -334,7 +338,7 @@ __device__ __forceinline__ void attention_split(const AttnArgs &a) {
         for (int u = 0; u < kLoads; ++u) {
             const int c = cbase + 4 * u + lq;
             if constexpr (WPR == 4) kop[u] = kbuf[u];
-            else *reinterpret_cast<v4i *>(k_lds + pp * kKStride + c * 16) = kbuf[u];
+            else *reinterpret_cast<v4i *>(k_lds + kpos(u) * kKStride + kchunk(u) * 16) = kbuf[u];
             const uint32_t w[4] = {(uint32_t)vbuf[u].x, (uint32_t)vbuf[u].y, (uint32_t)vbuf[u].z, (uint32_t)vbuf[u].w};
             const int vc = vchunk(u);
             const int col = (vpos(u) + 8 * (vc & 7)) & (BLK - 1);   // rows 8 vc .. 8 vc + 7: d / 8 = vc
