@@ -135,9 +135,13 @@ __device__ __forceinline__ void merge_chunk(const MergeArgs &a, int g, int64_t e
     const int r_hi = min(rows, (int)((e_lo + groups * 4 - 1) / D) + 1);
     const int nr = r_hi - r_lo;
     // the lane's partials (at most 8 splits: tpq * 8 >= n) go out first, so
-    // that their round trip overlaps the weights' one
-    const int64_t e0 = e_lo + (int64_t)(tid / tpq) * 4;   // the group's first output
-    const int t = tid % tpq;
+    // that their round trip overlaps the weights' one.  A wave holds 64 / tpq
+    // groups, lane gw + (64 / tpq) t being lane t of group gw: consecutive
+    // lanes read consecutive outputs of one split (whole lines), not one
+    // output of consecutive splits.
+    const int gpw = 64 / tpq;                              // groups per wave
+    const int t = (tid & 63) / gpw;
+    const int64_t e0 = e_lo + (int64_t)((tid >> 6) * gpw + (tid & 63) % gpw) * 4;   // the group's first output
     const int r = (int)(e0 / D), d = (int)(e0 % D);
     const bool real = r < rows;
     f4 v[8];
@@ -189,7 +193,7 @@ __device__ __forceinline__ void merge_chunk(const MergeArgs &a, int g, int64_t e
             if (s < n) acc += w_s[s * kMaxRowsWg + r - r_lo] * v[u];
         }
     }
-    for (int off = 1; off < tpq; off <<= 1)   // the group's lanes are consecutive
+    for (int off = gpw; off < 64; off <<= 1)   // the group's lanes are gpw apart: the same tree over t
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
     if (real && t == 0) {
