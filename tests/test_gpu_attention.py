@@ -120,6 +120,19 @@ def test_decode_attention_long_prefix_other_shapes(M, n_q, n_kv, D, combine):
     assert_close_bf16(_run(q, k, v, P), oracle.decode_attention(q, k, v, P), f"M={M} D={D} n_kv={n_kv}")
 
 
+@pytest.mark.parametrize("P", [1100, 2048, 4000])
+@pytest.mark.parametrize("M,n_q,n_kv,D", [(1, 32, 4, 256), (8, 32, 4, 256), (3, 8, 2, 128), (5, 8, 1, 64)])
+def test_decode_attention_merge_group_widths(M, n_q, n_kv, D, P, combine):
+    """Split counts for every width of the merge's lane groups.  A group of
+    tpq lanes sums a run of four outputs, at most 8 splits per lane, and a
+    wave's groups are interleaved over its lanes, so each tpq is its own lane
+    mapping.  These cache lengths give 9 splits (tpq 2), 17 (tpq 4, most
+    splits one block longer) and 32 (tpq 4, the most it covers); the other
+    tests cover up to 8 splits (tpq 1), 40 to 64 (tpq 8) and 128 (tpq 16)."""
+    q, k, v = _inputs(M, n_q, n_kv, D, P + M, seed=P + 10 * M + D)
+    assert_close_bf16(_run(q, k, v, P), oracle.decode_attention(q, k, v, P), f"M={M} D={D} P={P}")
+
+
 def test_decode_attention_graph_replays(combine):
     """The attention captured in a HIP graph (two launches, or one cooperative
     launch with the merge inside): replays on queries written between them
